@@ -1,0 +1,469 @@
+"""Benchmark: gradient GB/s through encode + decode + error feedback on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c2|c3|c4]
+
+A step is one pass of the whole compressor hot path over one gradient set:
+  c5 (default): BERT-large gradient set (bf16 grads, fp32 memory):
+      PowerSGD EF rank 4 on the 144 weight matrices, top-k EF (k = 1%) encode +
+      decode on the 30522 x 1024 embedding, and every 10th step the Accordion
+      check (per-layer norms of all 145 tensors -> host switch).
+  c2: ResNet-18 PowerSGD EF (rank 2), c3: ResNet-50-sized top-k EF (k = 1%),
+  c4: VGG-19 Accordion PowerSGD (rank 4/2, norms every 10 steps).
+Inputs are seeded synthetic arrays (gen/), uploaded before timing.
+
+Prints one JSON line (rank 0).  `value` is gradient GB/s = gradient bytes in
+their stored dtype / step time.  `roofline` reports the kernel with the largest
+share of the step: its algorithmic bytes per launch over its mean launch time
+(HIP events on the launch stream), against the 8 TB/s HBM peak.
+`cpu_baseline` times the CPU oracle (one thread) on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gen  # noqa: E402
+
+METRIC = "gradient GB/s through encode+decode+EF (µs/step) at 1 GPU; % of HBM peak"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", action="store_true", help="write 1 GiB between timed steps (cold Infinity Cache)")
+    ap.add_argument("--copy-calib", action="store_true", help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ workloads
+
+class Workload:
+    name = ""
+    description = ""
+    grad_bytes = 0
+    alg_bytes = 0.0           # per step, amortised
+    kernel_bytes = {}         # kernel name -> algorithmic bytes per step
+    config = {}
+
+    def step(self, t):
+        raise NotImplementedError
+
+
+def _flat(torch, sizes, dtype, dev, align_elems):
+    offs, o = [], 0
+    for s in sizes:
+        offs.append(o)
+        o += (s + align_elems - 1) // align_elems * align_elems
+    buf = torch.zeros(max(o, 1), dtype=dtype, device=dev)
+    return buf, [buf[a:a + s] for a, s in zip(offs, sizes)]
+
+
+def _upload_bf16(torch, dst, bits):
+    dst.copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+
+
+class PowersgdPart:
+    """Device buffers + ctypes table for a list of matrices sharing one flat memory buffer."""
+
+    def __init__(self, torch, gc, shapes, ranks, grad_views_per_set, mem_views, dev, qcfg):
+        self.gc = gc
+        self.shapes = shapes
+        self.ranks = list(ranks)
+        self.q = [torch.from_numpy(gen.q_init(qcfg, l, m)).to(dev) for l, (n, m) in enumerate(shapes)]
+        self.p = [torch.zeros(4, n, device=dev) for n, m in shapes]
+        self.out_buf, outs = _flat(torch, [n * m for n, m in shapes], torch.float32, dev, 64)
+        self.out = [o.view(n, m) for o, (n, m) in zip(outs, shapes)]
+        self.mem = [mv.view(n, m) for mv, (n, m) in zip(mem_views, shapes)]
+        self.grads = [[g.view(n, m) for g, (n, m) in zip(gs, shapes)] for gs in grad_views_per_set]
+        self.tables = [self._mats(s) for s in range(len(self.grads))]
+        self.ws = torch.empty(gc.gc_powersgd_workspace_bytes(self._mats(0)), dtype=torch.uint8, device=dev)
+
+    def _mats(self, s):
+        gc = self.gc
+        return [gc.Mat(grad=self.grads[s][i], mem=self.mem[i], q=self.q[i], rank=self.ranks[i], p=self.p[i],
+                       out=self.out[i]) for i in range(len(self.shapes))]
+
+    def set_ranks(self, ranks):
+        self.ranks = list(ranks)
+        self.tables = [self._mats(s) for s in range(len(self.grads))]
+
+    def step(self, s, eta=1.0):
+        self.gc.gc_powersgd_ef_step(self.tables[s], eta, self.ws)
+
+
+def psgd_bytes(shapes, ranks, sg):
+    return sum((sg + 12) * n * m + 4 * r * (n + 2 * m) for (n, m), r in zip(shapes, ranks))
+
+
+class C5(Workload):
+    name = "c5"
+
+    def __init__(self, torch, gc, dev):
+        self.torch, self.gc = torch, gc
+        shapes = gen.BERT_MATS
+        emb_d = gen.BERT_EMB[0] * gen.BERT_EMB[1]
+        self.k = gen.C5_EMB_K
+        sizes = [n * m for n, m in shapes] + [emb_d]
+        self.sizes = sizes
+        self.sets = []
+        for s in range(2):
+            buf, views = _flat(torch, sizes, torch.bfloat16, dev, 64)
+            for l in range(len(shapes)):
+                _upload_bf16(torch, views[l], gen.c5_matrix_bf16(s, l).ravel())
+            _upload_bf16(torch, views[-1], gen.c5_embedding_bf16(s))
+            self.sets.append((buf, views))
+        self.mem_buf, mem_views = _flat(torch, sizes, torch.float32, dev, 64)
+        self.ps = PowersgdPart(torch, gc, shapes, [4] * len(shapes), [v[:-1] for _, v in self.sets],
+                               mem_views[:-1], dev, gen.CFG_C5)
+        self.emb_mem = mem_views[-1]
+        self.emb_out = torch.zeros(emb_d, device=dev)
+        self.idx = torch.empty(self.k, dtype=torch.int32, device=dev)
+        self.val = torch.empty(self.k, dtype=torch.float32, device=dev)
+        self.tws = torch.empty(gc.gc_topk_workspace_bytes(emb_d, self.k), dtype=torch.uint8, device=dev)
+        self.norms = torch.empty(len(sizes), device=dev)
+        self.nws = torch.empty(gc.gc_grad_norm_workspace_bytes(self.sets[0][1]), dtype=torch.uint8, device=dev)
+        self.prev = np.zeros(len(sizes), np.float32)
+        self.checks = 0
+        self.levels = None
+        total = sum(sizes)
+        self.grad_bytes = 2 * total
+        mat_elems = sum(n * m for n, m in shapes)
+        self.kernel_bytes = {
+            "psgd_out": psgd_bytes(shapes, self.ps.ranks, 2),
+            "psgd_p": 6 * mat_elems, "psgd_q": 6 * mat_elems,
+            "topk_accum_hist": 10 * emb_d, "topk_capture": 4 * emb_d,
+            "topk_decode_set": 4 * emb_d + 8 * self.k,
+            "norm_partial": 2 * total / 10.0,
+        }
+        self.alg_bytes = psgd_bytes(shapes, self.ps.ranks, 2) + 14 * emb_d + 16 * self.k + 2 * total / 10.0
+        self.description = gen.WORKLOADS["c5"].description + "; Accordion check (145 layer norms) every 10 steps"
+        self.config = {"workload": "bert-large gradient set", "params": total, "matrices": len(shapes),
+                       "powersgd_rank": 4, "embedding": list(gen.BERT_EMB), "topk_k": self.k,
+                       "grad_dtype": "bf16", "memory_dtype": "f32", "eta": 1.0, "accordion_check_every": 10}
+
+    def step(self, t):
+        gc, s = self.gc, t % 2
+        views = self.sets[s][1]
+        if t % 10 == 0:
+            gc.gc_grad_norm(views, self.norms, self.nws)
+            now = self.norms.cpu().numpy()
+            self.levels, self.prev = gc.gc_accordion_select(now, self.prev, gen.C4_THRESHOLD, self.checks > 0)
+            self.checks += 1
+        self.ps.step(s)
+        gc.gc_topk_ef_encode(views[-1], self.emb_mem, 1.0, self.k, self.idx, self.val, self.tws)
+        gc.gc_topk_decode(self.idx, self.val, self.emb_out)
+
+
+class C2(Workload):
+    name = "c2"
+
+    def __init__(self, torch, gc, dev, rank=2):
+        shapes = gen.RESNET18_MATS
+        sizes = [n * m for n, m in shapes]
+        self.sets = []
+        for s in range(2):
+            buf, views = _flat(torch, sizes, torch.float32, dev, 64)
+            for l, g in enumerate(gen.c2_grads(s)):
+                views[l].copy_(torch.from_numpy(g.ravel()))
+            self.sets.append(views)
+        self.mem_buf, mem_views = _flat(torch, sizes, torch.float32, dev, 64)
+        self.ps = PowersgdPart(torch, gc, shapes, [rank] * len(shapes), self.sets, mem_views, dev, gen.CFG_C2)
+        self.grad_bytes = 4 * sum(sizes)
+        self.alg_bytes = psgd_bytes(shapes, self.ps.ranks, 4)
+        me = sum(sizes)
+        self.kernel_bytes = {"psgd_out": psgd_bytes(shapes, self.ps.ranks, 4), "psgd_p": 8 * me, "psgd_q": 8 * me}
+        self.description = gen.WORKLOADS["c2"].description + f" (rank {rank})"
+        self.config = {"workload": "resnet18 gradient set", "params": me, "powersgd_rank": rank,
+                       "grad_dtype": "f32", "memory_dtype": "f32"}
+
+    def step(self, t):
+        self.ps.step(t % 2)
+
+
+class C3(Workload):
+    name = "c3"
+
+    def __init__(self, torch, gc, dev, k=gen.C3_KS[1]):
+        self.gc = gc
+        d = gen.C3_D
+        self.k = k
+        self.g = [torch.from_numpy(gen.c3_grad(s)).to(dev) for s in range(2)]
+        self.mem = torch.zeros(d, device=dev)
+        self.out = torch.zeros(d, device=dev)
+        self.idx = torch.empty(k, dtype=torch.int32, device=dev)
+        self.val = torch.empty(k, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(gc.gc_topk_workspace_bytes(d, k), dtype=torch.uint8, device=dev)
+        self.grad_bytes = 4 * d
+        self.alg_bytes = 16 * d + 16 * k
+        self.kernel_bytes = {"topk_accum_hist": 12 * d, "topk_capture": 4 * d, "topk_decode_set": 4 * d + 8 * k}
+        self.description = gen.WORKLOADS["c3"].description + f" (k={k})"
+        self.config = {"workload": "resnet50-sized flat gradient", "params": d, "topk_k": k,
+                       "grad_dtype": "f32", "memory_dtype": "f32", "eta": 1.0}
+
+    def step(self, t):
+        self.gc.gc_topk_ef_encode(self.g[t % 2], self.mem, 1.0, self.k, self.idx, self.val, self.ws)
+        self.gc.gc_topk_decode(self.idx, self.val, self.out)
+
+
+class C4(Workload):
+    name = "c4"
+
+    def __init__(self, torch, gc, dev):
+        self.gc, self.torch, self.dev = gc, torch, dev
+        shapes = gen.VGG19_MATS
+        sizes = [n * m for n, m in shapes]
+        self.shapes = shapes
+        self.sets = []
+        for s in range(2):
+            buf, views = _flat(torch, sizes, torch.float32, dev, 64)
+            for l, g in enumerate(gen.c4_grads(100 + s)):
+                views[l].copy_(torch.from_numpy(g.ravel()))
+            self.sets.append(views)
+        self.mem_buf, mem_views = _flat(torch, sizes, torch.float32, dev, 64)
+        self.ps = PowersgdPart(torch, gc, shapes, [4] * len(shapes), self.sets, mem_views, dev, gen.CFG_C4)
+        self.norms = torch.empty(len(sizes), device=dev)
+        self.nws = torch.empty(gc.gc_grad_norm_workspace_bytes(self.sets[0]), dtype=torch.uint8, device=dev)
+        self.prev = np.zeros(len(sizes), np.float32)
+        self.checks = 0
+        me = sum(sizes)
+        self.grad_bytes = 4 * me
+        self.alg_bytes = psgd_bytes(shapes, [4] * len(shapes), 4) + 4 * me / 10.0
+        self.kernel_bytes = {"psgd_out": psgd_bytes(shapes, [4] * len(shapes), 4), "psgd_p": 8 * me,
+                             "psgd_q": 8 * me, "norm_partial": 4 * me / 10.0}
+        self.description = gen.WORKLOADS["c4"].description
+        self.config = {"workload": "vgg19 gradient set", "params": me, "levels": "l_low=rank4, l_high=rank2",
+                       "grad_dtype": "f32", "memory_dtype": "f32", "accordion_check_every": 10}
+
+    def step(self, t):
+        gc, s = self.gc, t % 2
+        if t % 10 == 0:
+            gc.gc_grad_norm(self.sets[s], self.norms, self.nws)
+            lv, self.prev = gc.gc_accordion_select(self.norms.cpu().numpy(), self.prev, gen.C4_THRESHOLD,
+                                                   self.checks > 0)
+            self.checks += 1
+            self.ps.set_ranks([gen.C4_RANK_LOW_COMPRESSION if v == gc.GC_LEVEL_LOW else gen.C4_RANK_HIGH_COMPRESSION
+                               for v in lv])
+        self.ps.step(s)
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def cpu_baseline(name):
+    """The oracle as it stands, one thread, on a bounded sample of the workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:   # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        if name == "c5":
+            mats = [(l, gen.c5_matrix_bf16(0, l)) for l in range(6)]          # encoder layer 0
+            q = [gen.q_init(gen.CFG_C5, l, gen.BERT_MATS[l][1]).T for l in range(6)]
+            emb = gen.c5_embedding_bf16(0)[: gen.BERT_EMB[1] * 1272]            # 1/24 of the rows
+            ek = int(0.01 * emb.size)
+            sample = "BERT encoder layer 0 (6 matrices, PowerSGD EF r4) + 1/24 of the embedding (top-k 1% EF)"
+            nbytes = 2 * (sum(g.size for _, g in mats) + emb.size)
+
+            def run():
+                for l, g in mats:
+                    n, m = gen.BERT_MATS[l]
+                    oracle.powersgd_ef_step(g.reshape(n, m), np.zeros((n, m), np.float32), q[l], 1.0, 4)
+                r = oracle.topk_ef_step(np.zeros(emb.size, np.float32), emb, 1.0, ek)
+                oracle.topk_decode(r["idx"], r["val"], emb.size)
+        elif name == "c3":
+            g = gen.c3_grad(0)[:2_560_000]
+            k = int(0.01 * g.size)
+            sample = "first 2.56M entries of the ResNet-50-sized gradient, top-k 1% EF"
+            nbytes = 4 * g.size
+
+            def run():
+                r = oracle.topk_ef_step(np.zeros(g.size, np.float32), g, 1.0, k)
+                oracle.topk_decode(r["idx"], r["val"], g.size)
+        else:
+            shapes = gen.RESNET18_MATS if name == "c2" else gen.VGG19_MATS
+            grads = gen.c2_grads(0) if name == "c2" else gen.c4_grads(0)
+            sel = list(range(len(shapes)))[-6:]
+            rank = 2 if name == "c2" else 4
+            sample = f"last 6 matrices of the gradient set, PowerSGD EF rank {rank}"
+            nbytes = 4 * sum(grads[l].size for l in sel)
+
+            def run():
+                for l in sel:
+                    n, m = shapes[l]
+                    oracle.powersgd_ef_step(grads[l], np.zeros((n, m), np.float32),
+                                            gen.q_init(0, l, m).T, 1.0, rank)
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            run()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > 10.0 or reps >= 500:
+                break
+        gbs = nbytes * reps / el / 1e9
+        return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{sample}; {reps} repetition(s), {el:.1f} s, float64 NumPy, one BLAS/OpenMP thread"}
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+
+
+# ------------------------------------------------------------------ traffic from committed counters
+
+def traffic_from_profiles(kernel, workload, src_hash):
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != src_hash:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def kernel_source_hash(kernel):
+    fname = "powersgd.hip" if kernel.startswith("psgd") else "norm.hip" if kernel.startswith("norm") else "topk.hip"
+    p = os.path.join(ROOT, "gradient_compression_error_amd", "csrc", fname)
+    h = hashlib.sha256(open(p, "rb").read())
+    h.update(open(os.path.join(ROOT, "gradient_compression_error_amd", "csrc", "gc_common.h"), "rb").read())
+    return h.hexdigest()
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU only: the compressor hot path runs on a single "
+                                   "GPU and no cross-GPU path is built; use --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    import gradient_compression_error_amd as gc
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calib:
+        n = 1 << 28   # 1 GiB of float32
+        a = torch.ones(n, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": 4 * n, "copy_calib_bytes_written": 4 * n, "launches": 3}))
+        return
+
+    print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
+    W = {"c5": C5, "c2": C2, "c3": C3, "c4": C4}[args.workload](torch, gc, dev)
+    torch.cuda.synchronize()
+    flush_buf = torch.empty(1 << 28, device=dev) if args.flush else None
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for t in range(args.warmup):
+        W.step(t)
+    torch.cuda.synchronize()
+
+    # which kernel dominates: one instrumented step per candidate (outside the timed region)
+    shares = {}
+    for kname in W.kernel_bytes:
+        gc.gc_timing_enable(kname)
+        W.step(args.warmup)
+        torch.cuda.synchronize()
+        ms, n = gc.gc_timing_read()
+        shares[kname] = ms
+    gc.gc_timing_enable(None)
+    dominant = max(shares, key=shares.get)
+
+    print(f"[bench] timing {args.steps} steps (dominant kernel {dominant})", file=sys.stderr, flush=True)
+    gc.gc_timing_enable(dominant)
+    torch.cuda.synchronize()
+    if args.flush:
+        total_ms = 0.0
+        for t in range(args.steps):
+            flush_buf.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            W.step(args.warmup + 1 + t)
+            e1.record()
+            torch.cuda.synchronize()
+            total_ms += e0.elapsed_time(e1)
+        wall_ms = total_ms
+    else:
+        t0 = time.perf_counter()
+        for t in range(args.steps):
+            W.step(args.warmup + 1 + t)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+    k_ms, k_launches = gc.gc_timing_read()
+    gc.gc_timing_enable(None)
+
+    ms_step = wall_ms / args.steps
+    gbs = W.grad_bytes / (ms_step * 1e-3) / 1e9
+    step_frac = W.alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    launches_per_step = k_launches / args.steps
+    bytes_per_launch = W.kernel_bytes[dominant] / launches_per_step
+    mean_launch_ms = k_ms / k_launches
+    achieved = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash(dominant)
+    roof = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(dominant, W.name, src_hash),
+            "bytes_per_launch": int(bytes_per_launch), "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+            "launches_per_step": launches_per_step,
+            "kernel_share_of_step": {k: round(v / ms_step, 3) for k, v in shares.items()}}
+
+    line = {"metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "us_per_step": round(ms_step * 1e3, 1),
+            "hbm_frac_step": round(step_frac, 4), "algorithmic_bytes_per_step": int(W.alg_bytes),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "cache": "flushed between steps" if args.flush else "warm (back-to-back steps)",
+            "config": W.config, "description": W.description, "device": torch.cuda.get_device_name(0),
+            "roofline": roof}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cb = cpu_baseline(W.name)
+        cb["cpu"] = _cpu_model()
+        cb["host_cpus"] = os.cpu_count()
+        line["cpu_baseline"] = cb
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(s + "\n")
+
+
+def _cpu_model():
+    try:
+        for l in open("/proc/cpuinfo"):
+            if l.startswith("model name"):
+                return l.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

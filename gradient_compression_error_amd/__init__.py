@@ -1,0 +1,216 @@
+"""MI355X-native gradient compression with error feedback.
+
+A thin ctypes binding over the C ABI of ``libgc.so`` (declared in
+``include/gc.h``).  Every function here has the name of the C entry point it
+marshals arguments for; all computation runs in the library's gfx950 kernels.
+PyTorch supplies device memory and the stream only.
+
+Importing this package loads ``libgc.so`` and raises ``ImportError`` if it has
+not been built (``python -m gradient_compression_error_amd.build``).  There is
+no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgc.so")
+
+GC_OK, GC_ERR_ARG, GC_ERR_DTYPE, GC_ERR_WORKSPACE, GC_ERR_HIP = 0, 1, 2, 3, 4
+GC_F32, GC_BF16 = 0, 1
+GC_LEVEL_LOW, GC_LEVEL_HIGH = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gradient_compression_error_amd.build` "
+                      "(or __graft_entry__.build()); there is no fallback path")
+
+lib = C.CDLL(LIB_PATH)
+
+
+class gc_mat(C.Structure):
+    _fields_ = [("grad", C.c_void_p), ("mem", C.c_void_p), ("q", C.c_void_p), ("p", C.c_void_p),
+                ("out", C.c_void_p), ("n", C.c_int32), ("m", C.c_int32), ("rank", C.c_int32)]
+
+
+class gc_span(C.Structure):
+    _fields_ = [("ptr", C.c_void_p), ("len", C.c_int64)]
+
+
+def _sig(name, res, *args):
+    f = getattr(lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_vp, _i64, _i32, _f32, _sz = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_size_t
+_sig("gc_status_str", C.c_char_p, _i32)
+_sig("gc_last_error", C.c_char_p)
+_sig("gc_topk_workspace_bytes", _sz, _i64, _i64)
+_sig("gc_topk_ef_encode", _i32, _vp, _i32, _vp, _i64, _f32, _i64, _vp, _vp, _vp, _sz, _vp)
+_sig("gc_topk_decode", _i32, _vp, _vp, _i64, _vp, _i64, _i32, _vp)
+_sig("gc_powersgd_workspace_bytes", _sz, C.POINTER(gc_mat), _i32)
+_sig("gc_powersgd_ef_step", _i32, C.POINTER(gc_mat), _i32, _i32, _f32, _vp, _sz, _vp)
+_sig("gc_grad_norm_workspace_bytes", _sz, C.POINTER(gc_span), _i32)
+_sig("gc_grad_norm", _i32, C.POINTER(gc_span), _i32, _i32, _vp, _vp, _sz, _vp)
+_sig("gc_accordion_select", _i32, C.POINTER(C.c_float), C.POINTER(C.c_float), _i32, _f32, _i32,
+     C.POINTER(C.c_int))
+_sig("gc_timing_enable", _i32, C.c_char_p)
+_sig("gc_timing_read", _i32, C.POINTER(C.c_double), C.POINTER(C.c_int64))
+_sig("gc_kernel_names", C.c_char_p)
+
+EXPORTED = ["gc_status_str", "gc_last_error", "gc_topk_workspace_bytes", "gc_topk_ef_encode",
+            "gc_topk_decode", "gc_powersgd_workspace_bytes", "gc_powersgd_ef_step",
+            "gc_grad_norm_workspace_bytes", "gc_grad_norm", "gc_accordion_select",
+            "gc_timing_enable", "gc_timing_read", "gc_kernel_names"]
+
+
+class GCError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gc_status_str(status)} ({gc_last_error()})")
+
+
+def _check(status: int, where: str):
+    if status != GC_OK:
+        raise GCError(status, where)
+
+
+def gc_status_str(status: int) -> str:
+    return lib.gc_status_str(status).decode()
+
+
+def gc_last_error() -> str:
+    return lib.gc_last_error().decode()
+
+
+def gc_kernel_names() -> list[str]:
+    return lib.gc_kernel_names().decode().split(",")
+
+
+# ------------------------------------------------------------------ tensor helpers
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return GC_F32
+    if t.dtype == torch.bfloat16:
+        return GC_BF16
+    raise TypeError(f"gradient dtype {t.dtype} not supported (float32 or bfloat16)")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+# ------------------------------------------------------------------ top-k
+
+def gc_topk_workspace_bytes(d: int, k: int) -> int:
+    return int(lib.gc_topk_workspace_bytes(d, k))
+
+
+def gc_topk_ef_encode(grad, mem, eta: float, k: int, out_idx, out_val, ws, stream=None) -> None:
+    """Mem-SGD top-k encode: mem <- acc - top_k(acc), (out_idx, out_val) <- top_k(acc)."""
+    _check(lib.gc_topk_ef_encode(_ptr(grad), _dtype_code(grad), _ptr(mem), mem.numel(), float(eta), int(k),
+                                 _ptr(out_idx), _ptr(out_val), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "gc_topk_ef_encode")
+
+
+def gc_topk_decode(idx, val, out, accumulate: bool = False, stream=None) -> None:
+    k = idx.numel()
+    _check(lib.gc_topk_decode(_ptr(idx) if k else None, _ptr(val) if k else None, k, _ptr(out), out.numel(),
+                              1 if accumulate else 0, _stream(stream)), "gc_topk_decode")
+
+
+# ------------------------------------------------------------------ PowerSGD
+
+@dataclass
+class Mat:
+    """One PowerSGD matrix: grad/mem n x m, q (rank cols, m) column-major, p (rank cols, n), out n x m."""
+    grad: object
+    mem: object
+    q: object
+    rank: int
+    p: object = None
+    out: object = None
+
+
+def _mats(mats: Sequence[Mat]):
+    arr = (gc_mat * len(mats))()
+    for i, a in enumerate(mats):
+        n, m = a.mem.shape
+        arr[i] = gc_mat(_ptr(a.grad), _ptr(a.mem), _ptr(a.q), _ptr(a.p), _ptr(a.out), n, m, int(a.rank))
+    return arr
+
+
+def gc_powersgd_workspace_bytes(mats: Sequence[Mat]) -> int:
+    return int(lib.gc_powersgd_workspace_bytes(_mats(mats), len(mats)))
+
+
+def gc_powersgd_ef_step(mats: Sequence[Mat], eta: float, ws, stream=None) -> None:
+    arr = _mats(mats)
+    _check(lib.gc_powersgd_ef_step(arr, len(mats), _dtype_code(mats[0].grad), float(eta), _ptr(ws), _nbytes(ws),
+                                   _stream(stream)), "gc_powersgd_ef_step")
+
+
+# ------------------------------------------------------------------ norms / Accordion
+
+def _spans(layers):
+    arr = (gc_span * len(layers))()
+    for i, t in enumerate(layers):
+        arr[i] = gc_span(_ptr(t), t.numel())
+    return arr
+
+
+def gc_grad_norm_workspace_bytes(layers) -> int:
+    return int(lib.gc_grad_norm_workspace_bytes(_spans(layers), len(layers)))
+
+
+def gc_grad_norm(layers, norms, ws, stream=None) -> None:
+    _check(lib.gc_grad_norm(_spans(layers), len(layers), _dtype_code(layers[0]), _ptr(norms), _ptr(ws), _nbytes(ws),
+                            _stream(stream)), "gc_grad_norm")
+
+
+def gc_accordion_select(norm_now, norm_prev, threshold: float, has_prev: bool):
+    """Host call.  Returns (levels int32[n], new norm_prev float32[n])."""
+    now = np.ascontiguousarray(norm_now, np.float32)
+    prev = np.ascontiguousarray(norm_prev, np.float32).copy()
+    lv = np.zeros(now.size, np.int32)
+    _check(lib.gc_accordion_select(now.ctypes.data_as(C.POINTER(C.c_float)), prev.ctypes.data_as(C.POINTER(C.c_float)),
+                                   now.size, float(threshold), 1 if has_prev else 0,
+                                   lv.ctypes.data_as(C.POINTER(C.c_int))), "gc_accordion_select")
+    return lv, prev
+
+
+# ------------------------------------------------------------------ timing hooks
+
+def gc_timing_enable(kernel_name: Optional[str]) -> None:
+    _check(lib.gc_timing_enable(kernel_name.encode() if kernel_name else None), "gc_timing_enable")
+
+
+def gc_timing_read():
+    ms, n = C.c_double(), C.c_int64()
+    _check(lib.gc_timing_read(C.byref(ms), C.byref(n)), "gc_timing_read")
+    return ms.value, n.value

@@ -1,0 +1,594 @@
+// Mem-SGD top-k sparsification with error-feedback memory on gfx950.
+//
+// Method ("Sparsified SGD with Memory", method section):
+//     acc = m_t + eta * grad;  g_t = comp_k(acc);  m_{t+1} = acc - g_t
+// with comp_k = top-k by magnitude (abstract: the most significant entries).
+//
+// The selection is exact.  The magnitude key of a float is its bit pattern
+// without the sign (31 bits; key order == |x| order for non-NaN x).  The
+// threshold key T is found by a three-level radix select (12 + 12 + 7 bits):
+//
+//   topk_accum_hist  acc = fl32(m + fl32(eta*g)) written over m; 4096-bin LDS
+//                    histogram of key>>19 per workgroup, merged with device
+//                    atomics; the last workgroup picks the level-1 bin b1.
+//   topk_capture     re-reads acc; every entry with key>>19 >= b1 is appended,
+//                    in index order, to its tile's slot region (wave ballots +
+//                    a cross-wave prefix); entries in bin b1 feed the level-2
+//                    histogram; the last workgroup picks b2.
+//   topk_refine      level-3 histogram over the captured entries only; the
+//                    last workgroup fixes T and how many keys == T to take.
+//   topk_count       per tile: #(key > T), #(key == T); the last workgroup
+//                    scans both over tiles (ties go to the lowest indices).
+//   topk_emit        writes the k (index, value) pairs in ascending index
+//                    order and zeroes the selected memory entries.
+//
+// Only the first two kernels touch all d entries (16 B/entry for fp32
+// gradients); the rest work on the captured entries.  No kernel waits on
+// another workgroup: the cross-workgroup steps are done by whichever
+// workgroup finishes last (device-scope ticket + fences).
+#include "gc_common.h"
+
+namespace gc {
+namespace {
+
+constexpr int TK_THREADS = 256;
+constexpr int TK_UNROLL = 4;
+constexpr int TK_TILE = TK_THREADS * 4 * TK_UNROLL;  // 4096 entries per tile
+constexpr int H1_BINS = 4096;
+constexpr int H1_SHIFT = 19;   // key bits 30..19
+constexpr int H2_BINS = 4096;
+constexpr int H2_SHIFT = 7;    // key bits 18..7
+constexpr int H3_BINS = 128;   // key bits 6..0
+constexpr int TK_SMALL_GRID = 1024;
+constexpr int DEC_TILE = 4096;
+
+struct TopkState {
+    unsigned ticket[4];
+    unsigned b1, above1;       // level-1 bin, #keys in higher level-1 bins
+    unsigned prefix2, above2;  // (b1 << 12) | b2, #keys with (key >> 7) > prefix2
+    unsigned thr, above3;      // threshold key T, #keys > T
+    unsigned need;             // #keys == T taken (lowest indices first)
+    unsigned pad[5];
+};
+static_assert(sizeof(TopkState) == 64, "TopkState layout");
+
+struct TopkLayout {
+    size_t state, hist1, hist2, hist3, tile_cnt, tile_gt, tile_eq, eq_before, out_off;
+    size_t slot_idx, slot_val, total, zero_bytes;
+    long long ntiles;
+};
+
+TopkLayout topk_layout(long long d) {
+    TopkLayout L{};
+    L.ntiles = (d + TK_TILE - 1) / TK_TILE;
+    const size_t nt = static_cast<size_t>(L.ntiles);
+    size_t o = 0;
+    L.state = o;     o += round_up(sizeof(TopkState), 256);
+    L.hist1 = o;     o += H1_BINS * 4;
+    L.hist2 = o;     o += H2_BINS * 4;
+    L.hist3 = o;     o += round_up(H3_BINS * 4, 256);
+    L.zero_bytes = o;
+    L.tile_cnt = o;  o += round_up(nt * 4, 256);
+    L.tile_gt = o;   o += round_up(nt * 4, 256);
+    L.tile_eq = o;   o += round_up(nt * 4, 256);
+    L.eq_before = o; o += round_up(nt * 4, 256);
+    L.out_off = o;   o += round_up(nt * 4, 256);
+    L.slot_idx = o;  o += round_up(nt * TK_TILE * 4, 256);
+    L.slot_val = o;  o += round_up(nt * TK_TILE * 4, 256);
+    L.total = o;
+    return L;
+}
+
+// ---------------------------------------------------------------- device helpers
+
+// Bin b of `hist` (scanned from the top) with
+//   sum(hist[b+1 ..]) < need <= sum(hist[b ..]);
+// *bin = b and *above = sum(hist[b+1 ..]).  Needs 1 <= need <= sum(hist).
+// `hist` is a device-wide histogram built with atomics: read with device-scope
+// atomic loads.  Whole block; results in shared memory after the final barrier.
+__device__ void select_bin_256(const unsigned* hist, int nbins, unsigned need, unsigned* s_tmp,
+                               unsigned* s_bin, unsigned* s_above) {
+    const int t = threadIdx.x;
+    if (t == 0) {
+        *s_bin = 0u;
+        *s_above = 0u;
+    }
+    const int per = (nbins + TK_THREADS - 1) / TK_THREADS;
+    int hi = nbins - t * per;
+    int lo = hi - per;
+    if (hi < 0) hi = 0;
+    if (lo < 0) lo = 0;
+    unsigned s = 0;
+    for (int b = lo; b < hi; ++b) s += atomic_load_u32(hist + b);
+    unsigned total;
+    const unsigned incl = block_inclusive_scan_256(s, s_tmp, &total);
+    const unsigned excl = incl - s;
+    if (s > 0 && excl < need && need <= incl) {
+        unsigned run = excl;
+        for (int b = hi - 1; b >= lo; --b) {
+            const unsigned c = atomic_load_u32(hist + b);
+            if (run + c >= need) {
+                *s_bin = static_cast<unsigned>(b);
+                *s_above = run;
+                break;
+            }
+            run += c;
+        }
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------- kernels
+
+__global__ __launch_bounds__(256) void topk_init(unsigned* __restrict__ zero, int nwords) {
+    for (int i = threadIdx.x; i < nwords; i += blockDim.x) zero[i] = 0u;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
+        const void* __restrict__ grad, float* __restrict__ mem, long long d, float eta, unsigned k,
+        unsigned* __restrict__ hist1, TopkState* __restrict__ st) {
+    __shared__ unsigned h[H1_BINS];
+    __shared__ unsigned s_tmp[4];
+    __shared__ unsigned s_bin, s_above;
+    for (int i = threadIdx.x; i < H1_BINS; i += TK_THREADS) h[i] = 0u;
+    __syncthreads();
+
+    const long long base = static_cast<long long>(blockIdx.x) * TK_TILE;
+    if (base + TK_TILE <= d) {
+        const long long b4 = base / 4;
+        float4 gv[TK_UNROLL], mv[TK_UNROLL];
+#pragma unroll
+        for (int u = 0; u < TK_UNROLL; ++u) {
+            const long long i4 = b4 + u * TK_THREADS + threadIdx.x;
+            gv[u] = load_grad4<BF16>(grad, i4);
+            mv[u] = reinterpret_cast<const float4*>(mem)[i4];
+        }
+#pragma unroll
+        for (int u = 0; u < TK_UNROLL; ++u) {
+            float4 a;
+            a.x = ef_acc(mv[u].x, eta, gv[u].x);
+            a.y = ef_acc(mv[u].y, eta, gv[u].y);
+            a.z = ef_acc(mv[u].z, eta, gv[u].z);
+            a.w = ef_acc(mv[u].w, eta, gv[u].w);
+            reinterpret_cast<float4*>(mem)[b4 + u * TK_THREADS + threadIdx.x] = a;
+            atomicAdd(&h[key_of(a.x) >> H1_SHIFT], 1u);
+            atomicAdd(&h[key_of(a.y) >> H1_SHIFT], 1u);
+            atomicAdd(&h[key_of(a.z) >> H1_SHIFT], 1u);
+            atomicAdd(&h[key_of(a.w) >> H1_SHIFT], 1u);
+        }
+    } else {
+        for (long long i = base + threadIdx.x; i < d; i += TK_THREADS) {
+            const float a = ef_acc(mem[i], eta, load_grad1<BF16>(grad, i));
+            mem[i] = a;
+            atomicAdd(&h[key_of(a) >> H1_SHIFT], 1u);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < H1_BINS; i += TK_THREADS) {
+        const unsigned c = h[i];
+        if (c) atomicAdd(hist1 + i, c);
+    }
+    if (last_block_done(&st->ticket[0])) {
+        select_bin_256(hist1, H1_BINS, k, s_tmp, &s_bin, &s_above);
+        if (threadIdx.x == 0) {
+            st->b1 = s_bin;
+            st->above1 = s_above;
+        }
+    }
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_capture(
+        const float* __restrict__ acc, long long d, unsigned k, TopkState* __restrict__ st,
+        unsigned* __restrict__ hist2, int* __restrict__ slot_idx, float* __restrict__ slot_val,
+        unsigned* __restrict__ tile_cnt) {
+    __shared__ unsigned h[H2_BINS];
+    __shared__ unsigned s_wave[4];
+    __shared__ unsigned s_tmp[4];
+    __shared__ unsigned s_bin, s_above;
+    for (int i = threadIdx.x; i < H2_BINS; i += TK_THREADS) h[i] = 0u;
+    __syncthreads();
+
+    const unsigned b1 = st->b1;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const unsigned long long lt = lanemask_lt();
+    const long long base = static_cast<long long>(blockIdx.x) * TK_TILE;
+    int* const sidx = slot_idx + base;
+    float* const sval = slot_val + base;
+    unsigned running = 0;
+#pragma unroll
+    for (int u = 0; u < TK_UNROLL; ++u) {
+        const long long e0 = base + u * (TK_THREADS * 4) + threadIdx.x * 4;
+        float v[4];
+        bool ok[4];
+        if (e0 + 3 < d) {
+            const float4 a = reinterpret_cast<const float4*>(acc)[e0 / 4];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            ok[0] = ok[1] = ok[2] = ok[3] = true;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                ok[j] = (e0 + j) < d;
+                v[j] = ok[j] ? acc[e0 + j] : 0.0f;
+            }
+        }
+        bool cap[4];
+        unsigned before = 0, wtot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const unsigned key = key_of(v[j]);
+            const unsigned bin = key >> H1_SHIFT;
+            cap[j] = ok[j] && bin >= b1;
+            if (ok[j] && bin == b1) atomicAdd(&h[(key >> H2_SHIFT) & (H2_BINS - 1)], 1u);
+            const unsigned long long bal = __ballot(cap[j]);
+            before += __popcll(bal & lt);
+            wtot += __popcll(bal);
+        }
+        if (lane == 0) s_wave[w] = wtot;
+        __syncthreads();
+        unsigned wbefore = 0, ctot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const unsigned t = s_wave[i];
+            wbefore += (i < w) ? t : 0u;
+            ctot += t;
+        }
+        __syncthreads();
+        unsigned pos = running + wbefore + before;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (cap[j]) {
+                sidx[pos] = static_cast<int>(e0 + j);
+                sval[pos] = v[j];
+                ++pos;
+            }
+        }
+        running += ctot;
+    }
+    if (threadIdx.x == 0) tile_cnt[blockIdx.x] = running;
+    __syncthreads();
+    for (int i = threadIdx.x; i < H2_BINS; i += TK_THREADS) {
+        const unsigned c = h[i];
+        if (c) atomicAdd(hist2 + i, c);
+    }
+    if (last_block_done(&st->ticket[1])) {
+        const unsigned above1 = st->above1;
+        select_bin_256(hist2, H2_BINS, k - above1, s_tmp, &s_bin, &s_above);
+        if (threadIdx.x == 0) {
+            st->prefix2 = (b1 << 12) | s_bin;
+            st->above2 = above1 + s_above;
+        }
+    }
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_refine(
+        unsigned k, TopkState* __restrict__ st, unsigned* __restrict__ hist3,
+        const float* __restrict__ slot_val, const unsigned* __restrict__ tile_cnt, int ntiles) {
+    __shared__ unsigned h[H3_BINS];
+    __shared__ unsigned s_tmp[4];
+    __shared__ unsigned s_bin, s_above;
+    for (int i = threadIdx.x; i < H3_BINS; i += TK_THREADS) h[i] = 0u;
+    __syncthreads();
+    const unsigned prefix2 = st->prefix2;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const unsigned cnt = tile_cnt[t];
+        const float* sv = slot_val + static_cast<long long>(t) * TK_TILE;
+        for (unsigned e = threadIdx.x; e < cnt; e += TK_THREADS) {
+            const unsigned key = key_of(sv[e]);
+            if ((key >> H2_SHIFT) == prefix2) atomicAdd(&h[key & (H3_BINS - 1)], 1u);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < H3_BINS; i += TK_THREADS) {
+        const unsigned c = h[i];
+        if (c) atomicAdd(hist3 + i, c);
+    }
+    if (last_block_done(&st->ticket[2])) {
+        const unsigned above2 = st->above2;
+        select_bin_256(hist3, H3_BINS, k - above2, s_tmp, &s_bin, &s_above);
+        if (threadIdx.x == 0) {
+            const unsigned above3 = above2 + s_above;
+            st->thr = (prefix2 << H2_SHIFT) | s_bin;
+            st->above3 = above3;
+            st->need = k - above3;
+        }
+    }
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_count(
+        TopkState* __restrict__ st, const float* __restrict__ slot_val,
+        const unsigned* __restrict__ tile_cnt, int ntiles, unsigned* __restrict__ tile_gt,
+        unsigned* __restrict__ tile_eq, unsigned* __restrict__ eq_before, unsigned* __restrict__ out_off) {
+    __shared__ unsigned s_red[8];
+    __shared__ unsigned s_tmp[4];
+    const unsigned thr = st->thr;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const unsigned cnt = tile_cnt[t];
+        const float* sv = slot_val + static_cast<long long>(t) * TK_TILE;
+        unsigned gt = 0, eq = 0;
+        for (unsigned e = threadIdx.x; e < cnt; e += TK_THREADS) {
+            const unsigned key = key_of(sv[e]);
+            gt += key > thr;
+            eq += key == thr;
+        }
+        gt = wave_sum(gt);
+        eq = wave_sum(eq);
+        if (lane == 0) {
+            s_red[w] = gt;
+            s_red[4 + w] = eq;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            tile_gt[t] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+            tile_eq[t] = s_red[4] + s_red[5] + s_red[6] + s_red[7];
+        }
+        __syncthreads();
+    }
+    if (last_block_done(&st->ticket[3])) {
+        const unsigned need = st->need;
+        const int per = (ntiles + TK_THREADS - 1) / TK_THREADS;
+        const int lo = min(ntiles, static_cast<int>(threadIdx.x) * per);
+        const int hi = min(ntiles, lo + per);
+        unsigned s_eq = 0;
+        for (int t = lo; t < hi; ++t) s_eq += atomic_load_u32(tile_eq + t);
+        unsigned total;
+        unsigned eqb = block_inclusive_scan_256(s_eq, s_tmp, &total) - s_eq;
+        unsigned s_sel = 0;
+        for (int t = lo; t < hi; ++t) {
+            const unsigned e = atomic_load_u32(tile_eq + t);
+            const unsigned g = atomic_load_u32(tile_gt + t);
+            const unsigned take = need > eqb ? min(e, need - eqb) : 0u;
+            eq_before[t] = eqb;
+            eqb += e;
+            s_sel += g + take;
+        }
+        unsigned off = block_inclusive_scan_256(s_sel, s_tmp, &total) - s_sel;
+        for (int t = lo; t < hi; ++t) {
+            const unsigned e = atomic_load_u32(tile_eq + t);
+            const unsigned g = atomic_load_u32(tile_gt + t);
+            const unsigned eb = eq_before[t];
+            const unsigned take = need > eb ? min(e, need - eb) : 0u;
+            out_off[t] = off;
+            off += g + take;
+        }
+    }
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_emit(
+        const TopkState* __restrict__ st, const int* __restrict__ slot_idx,
+        const float* __restrict__ slot_val, const unsigned* __restrict__ tile_cnt,
+        const unsigned* __restrict__ eq_before, const unsigned* __restrict__ out_off, int ntiles,
+        unsigned k, int* __restrict__ out_idx, float* __restrict__ out_val, float* __restrict__ mem) {
+    __shared__ unsigned s_eq[4], s_sel[4];
+    const unsigned thr = st->thr;
+    const unsigned need = st->need;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const unsigned long long lt = lanemask_lt();
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const unsigned cnt = tile_cnt[t];
+        const long long sbase = static_cast<long long>(t) * TK_TILE;
+        unsigned eqr = eq_before[t];
+        unsigned off = out_off[t];
+        for (unsigned c0 = 0; c0 < cnt; c0 += TK_THREADS) {
+            const unsigned e = c0 + threadIdx.x;
+            const bool valid = e < cnt;
+            float v = 0.0f;
+            int ix = 0;
+            if (valid) {
+                v = slot_val[sbase + e];
+                ix = slot_idx[sbase + e];
+            }
+            const unsigned key = key_of(v);
+            const bool is_eq = valid && key == thr;
+            const bool is_gt = valid && key > thr;
+            const unsigned long long beq = __ballot(is_eq);
+            if (lane == 0) s_eq[w] = __popcll(beq);
+            __syncthreads();
+            unsigned weq = 0, teq = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                weq += (i < w) ? s_eq[i] : 0u;
+                teq += s_eq[i];
+            }
+            const unsigned rank = eqr + weq + __popcll(beq & lt);
+            const bool sel = is_gt || (is_eq && rank < need);
+            const unsigned long long bsel = __ballot(sel);
+            if (lane == 0) s_sel[w] = __popcll(bsel);
+            __syncthreads();
+            unsigned wsel = 0, tsel = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                wsel += (i < w) ? s_sel[i] : 0u;
+                tsel += s_sel[i];
+            }
+            const unsigned pos = off + wsel + __popcll(bsel & lt);
+            if (sel && pos < k) {
+                out_idx[pos] = ix;
+                out_val[pos] = v;
+                mem[ix] = 0.0f;
+            }
+            eqr += teq;
+            off += tsel;
+            __syncthreads();
+        }
+    }
+}
+
+// First position p in idx[0..k) with idx[p] >= target (idx ascending), found
+// by one wave with 64-way probes.  All lanes of the wave get the result.
+__device__ long long wave_lower_bound(const int* __restrict__ idx, long long k, long long target) {
+    const int lane = threadIdx.x & 63;
+    long long lo = 0, hi = k;
+    while (hi - lo > 64) {
+        const long long step = (hi - lo + 63) / 64;
+        const long long pos = lo + lane * step;
+        const bool less = pos < hi && static_cast<long long>(idx[pos]) < target;
+        const int c = __popcll(__ballot(less));
+        const long long nlo = c > 0 ? lo + static_cast<long long>(c - 1) * step + 1 : lo;
+        const long long nhi = c < 64 ? min(hi, lo + static_cast<long long>(c) * step) : hi;
+        lo = nlo;
+        hi = nhi;
+    }
+    const long long pos = lo + lane;
+    const bool less = pos < hi && static_cast<long long>(idx[pos]) < target;
+    return lo + __popcll(__ballot(less));
+}
+
+__global__ __launch_bounds__(256) void topk_decode_set(
+        const int* __restrict__ idx, const float* __restrict__ val, long long k,
+        float* __restrict__ out, long long d) {
+    __shared__ float4 buf4[DEC_TILE / 4];
+    __shared__ long long s_lo, s_hi;
+    float* buf = reinterpret_cast<float*>(buf4);
+    const long long t0 = static_cast<long long>(blockIdx.x) * DEC_TILE;
+    const long long t1 = min(d, t0 + DEC_TILE);
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (w == 0) {
+        const long long r = wave_lower_bound(idx, k, t0);
+        if (lane == 0) s_lo = r;
+    } else if (w == 1) {
+        const long long r = wave_lower_bound(idx, k, t1);
+        if (lane == 0) s_hi = r;
+    }
+    for (int i = threadIdx.x; i < DEC_TILE / 4; i += 256) buf4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    for (long long p = s_lo + threadIdx.x; p < s_hi; p += 256) {
+        const long long i = idx[p];
+        if (i >= t0 && i < t1) buf[i - t0] = val[p];
+    }
+    __syncthreads();
+    if (t1 - t0 == DEC_TILE) {
+        float4* o4 = reinterpret_cast<float4*>(out + t0);
+        for (int i = threadIdx.x; i < DEC_TILE / 4; i += 256) o4[i] = buf4[i];
+    } else {
+        for (long long i = t0 + threadIdx.x; i < t1; i += 256) out[i] = buf[i - t0];
+    }
+}
+
+__global__ __launch_bounds__(256) void topk_decode_add(
+        const int* __restrict__ idx, const float* __restrict__ val, long long k,
+        float* __restrict__ out, long long d) {
+    const long long p = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+    if (p < k) {
+        const long long i = idx[p];
+        if (i >= 0 && i < d) out[i] = __fadd_rn(out[i], val[p]);
+    }
+}
+
+}  // namespace
+}  // namespace gc
+
+using namespace gc;
+
+extern "C" {
+
+size_t gc_topk_workspace_bytes(int64_t d, int64_t k) {
+    if (d < 1 || d > INT32_MAX || k < 1 || k > d) return 0;
+    return topk_layout(d).total;
+}
+
+int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, float eta,
+                      int64_t k, int32_t* out_idx, float* out_val,
+                      void* ws, size_t ws_bytes, void* stream) {
+    if (!grad || !mem || !out_idx || !out_val || !ws)
+        return fail(GC_ERR_ARG, "gc_topk_ef_encode: null pointer argument");
+    if (grad_dtype != GC_F32 && grad_dtype != GC_BF16)
+        return fail(GC_ERR_DTYPE, "gc_topk_ef_encode: grad_dtype must be GC_F32 or GC_BF16");
+    if (d < 1 || d > INT32_MAX)
+        return fail(GC_ERR_ARG, "gc_topk_ef_encode: d must be in [1, INT32_MAX]");
+    if (k < 1 || k > d) return fail(GC_ERR_ARG, "gc_topk_ef_encode: k must be in [1, d]");
+    if (!aligned16(grad) || !aligned16(mem) || !aligned16(out_idx) || !aligned16(out_val) || !aligned16(ws))
+        return fail(GC_ERR_ARG, "gc_topk_ef_encode: device pointers must be 16-byte aligned");
+    const size_t gbytes = static_cast<size_t>(d) * (grad_dtype == GC_BF16 ? 2 : 4);
+    const size_t mbytes = static_cast<size_t>(d) * 4, kbytes = static_cast<size_t>(k) * 4;
+    if (overlaps(out_idx, kbytes, mem, mbytes) || overlaps(out_val, kbytes, mem, mbytes) ||
+        overlaps(out_idx, kbytes, out_val, kbytes) || overlaps(grad, gbytes, mem, mbytes) ||
+        overlaps(out_idx, kbytes, grad, gbytes) || overlaps(out_val, kbytes, grad, gbytes))
+        return fail(GC_ERR_ARG, "gc_topk_ef_encode: output buffers overlap an input or each other");
+    const TopkLayout L = topk_layout(d);
+    if (ws_bytes < L.total)
+        return fail(GC_ERR_WORKSPACE, "gc_topk_ef_encode: workspace smaller than gc_topk_workspace_bytes");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    auto* st = reinterpret_cast<TopkState*>(w + L.state);
+    auto* hist1 = reinterpret_cast<unsigned*>(w + L.hist1);
+    auto* hist2 = reinterpret_cast<unsigned*>(w + L.hist2);
+    auto* hist3 = reinterpret_cast<unsigned*>(w + L.hist3);
+    auto* tile_cnt = reinterpret_cast<unsigned*>(w + L.tile_cnt);
+    auto* tile_gt = reinterpret_cast<unsigned*>(w + L.tile_gt);
+    auto* tile_eq = reinterpret_cast<unsigned*>(w + L.tile_eq);
+    auto* eq_before = reinterpret_cast<unsigned*>(w + L.eq_before);
+    auto* out_off = reinterpret_cast<unsigned*>(w + L.out_off);
+    auto* slot_idx = reinterpret_cast<int*>(w + L.slot_idx);
+    auto* slot_val = reinterpret_cast<float*>(w + L.slot_val);
+    const int ntiles = static_cast<int>(L.ntiles);
+    const int small_grid = ntiles < TK_SMALL_GRID ? ntiles : TK_SMALL_GRID;
+    const unsigned ku = static_cast<unsigned>(k);
+    int rc;
+
+    {
+        TimedLaunch tl("topk_init", s);
+        topk_init<<<1, 256, 0, s>>>(reinterpret_cast<unsigned*>(w), static_cast<int>(L.zero_bytes / 4));
+        if ((rc = check_launch("topk_init")) != GC_OK) return rc;
+    }
+    {
+        TimedLaunch tl("topk_accum_hist", s);
+        if (grad_dtype == GC_BF16)
+            topk_accum_hist<true><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, ku, hist1, st);
+        else
+            topk_accum_hist<false><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, ku, hist1, st);
+        if ((rc = check_launch("topk_accum_hist")) != GC_OK) return rc;
+    }
+    {
+        TimedLaunch tl("topk_capture", s);
+        topk_capture<<<ntiles, TK_THREADS, 0, s>>>(mem, d, ku, st, hist2, slot_idx, slot_val, tile_cnt);
+        if ((rc = check_launch("topk_capture")) != GC_OK) return rc;
+    }
+    {
+        TimedLaunch tl("topk_refine", s);
+        topk_refine<<<small_grid, TK_THREADS, 0, s>>>(ku, st, hist3, slot_val, tile_cnt, ntiles);
+        if ((rc = check_launch("topk_refine")) != GC_OK) return rc;
+    }
+    {
+        TimedLaunch tl("topk_count", s);
+        topk_count<<<small_grid, TK_THREADS, 0, s>>>(st, slot_val, tile_cnt, ntiles, tile_gt, tile_eq,
+                                                     eq_before, out_off);
+        if ((rc = check_launch("topk_count")) != GC_OK) return rc;
+    }
+    {
+        TimedLaunch tl("topk_emit", s);
+        topk_emit<<<small_grid, TK_THREADS, 0, s>>>(st, slot_idx, slot_val, tile_cnt, eq_before, out_off,
+                                                    ntiles, ku, out_idx, out_val, mem);
+        if ((rc = check_launch("topk_emit")) != GC_OK) return rc;
+    }
+    return GC_OK;
+}
+
+int gc_topk_decode(const int32_t* idx, const float* val, int64_t k, float* out, int64_t d,
+                   int accumulate, void* stream) {
+    if (!out) return fail(GC_ERR_ARG, "gc_topk_decode: null out");
+    if (d < 1 || d > INT32_MAX) return fail(GC_ERR_ARG, "gc_topk_decode: d must be in [1, INT32_MAX]");
+    if (k < 0 || k > d) return fail(GC_ERR_ARG, "gc_topk_decode: k must be in [0, d]");
+    if (k > 0 && (!idx || !val)) return fail(GC_ERR_ARG, "gc_topk_decode: null idx/val");
+    if (!aligned16(out) || (k > 0 && (!aligned16(idx) || !aligned16(val))))
+        return fail(GC_ERR_ARG, "gc_topk_decode: device pointers must be 16-byte aligned");
+    const size_t kb = static_cast<size_t>(k) * 4, db = static_cast<size_t>(d) * 4;
+    if (k > 0 && (overlaps(out, db, idx, kb) || overlaps(out, db, val, kb)))
+        return fail(GC_ERR_ARG, "gc_topk_decode: out overlaps idx/val");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (accumulate) {
+        if (k == 0) return GC_OK;
+        TimedLaunch tl("topk_decode_add", s);
+        const long long blocks = (k + 255) / 256;
+        topk_decode_add<<<static_cast<unsigned>(blocks), 256, 0, s>>>(idx, val, k, out, d);
+        return check_launch("topk_decode_add");
+    }
+    TimedLaunch tl("topk_decode_set", s);
+    const long long blocks = (d + DEC_TILE - 1) / DEC_TILE;
+    topk_decode_set<<<static_cast<unsigned>(blocks), 256, 0, s>>>(idx, val, k, out, d);
+    return check_launch("topk_decode_set");
+}
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+/*
+ * gc.h -- C ABI of the MI355X (gfx950) gradient-compressor library libgc.so.
+ *
+ * The library implements the per-step hot path of error-feedback gradient
+ * compression for data-parallel training on one GPU:
+ *   - Mem-SGD top-k sparsification with memory ("Sparsified SGD with Memory",
+ *     method section: g_t = comp_k(m_t + eta*grad), m_{t+1} = m_t + eta*grad - g_t),
+ *   - PowerSGD rank-r compression with the residual kept in memory (named as the
+ *     low-rank compressor in the Accordion paper's method section and in the
+ *     utility-of-compression paper's method/results sections),
+ *   - the per-layer gradient norms and the two-level switch of Accordion
+ *     (Accordion paper, method section: l_low / l_high chosen from the rate of
+ *     change of the gradient norm).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller unless marked
+ *     [host].  The library never allocates device memory and never frees
+ *     anything the caller passed.
+ *   - Scratch memory is passed as (ws, ws_bytes); query the size with the
+ *     matching *_workspace_bytes function.  Contents of ws on entry are
+ *     ignored; on return they are unspecified.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
+ *     stream) and return; nothing is synchronised.  gc_accordion_select is a
+ *     pure host function.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - Return value: GC_OK or an error code.  Arguments are validated before any
+ *     work is enqueued, so a call that fails validation changes no buffer.
+ *     gc_last_error() gives a message for the last failure on this thread.
+ *   - Gradients may be float32 (GC_F32) or bfloat16 (GC_BF16); memory, factors
+ *     and decoded outputs are always float32.
+ *   - Results are deterministic: the same inputs give the same bits on every
+ *     call (all reductions have a fixed order; no floating-point atomics).
+ *   - Calls that share a workspace must not overlap in time (use one stream).
+ */
+#ifndef GC_H
+#define GC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define GC_OK            0
+#define GC_ERR_ARG       1   /* a null/misaligned pointer, a size or rank out of range, aliasing */
+#define GC_ERR_DTYPE     2   /* unknown gradient dtype */
+#define GC_ERR_WORKSPACE 3   /* ws_bytes smaller than the query result */
+#define GC_ERR_HIP       4   /* a HIP runtime call (kernel launch, event) failed */
+
+/* gradient dtypes */
+#define GC_F32  0
+#define GC_BF16 1
+
+/* Accordion levels */
+#define GC_LEVEL_LOW  0   /* l_low: low compression, used in critical regimes */
+#define GC_LEVEL_HIGH 1   /* l_high: high compression */
+
+/* Static description of a status code; never NULL. */
+const char* gc_status_str(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* gc_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Top-k sparsification with error-feedback memory                          */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes needed by gc_topk_ef_encode for a vector of d entries.
+ * Returns 0 when (d, k) is out of range. */
+size_t gc_topk_workspace_bytes(int64_t d, int64_t k);
+
+/* One Mem-SGD encode step ("Sparsified SGD with Memory", method section):
+ *     acc_i   = fl32(mem_i + fl32(eta * grad_i))   (two float32 roundings, no FMA)
+ *     g_t     = top_k(acc)                         (k largest |acc_i|)
+ *     mem_i  <- acc_i - g_t,i                      (+0.0 where selected)
+ * The message is written as k (index, value) pairs in ascending index order:
+ * out_idx[j] = i, out_val[j] = acc_i.  Among equal |acc| (including +x / -x)
+ * the lower index is taken first; the selection is exact (no sampling).
+ *
+ *   grad      [d] float32 or bf16 (grad_dtype), read only
+ *   mem       [d] float32, in/out: m_t on entry, m_{t+1} on return
+ *   d         1 <= d <= INT32_MAX
+ *   eta       step size, used as a float32 value
+ *   k         1 <= k <= d
+ *   out_idx   [k] int32, out
+ *   out_val   [k] float32, out
+ *   ws        >= gc_topk_workspace_bytes(d, k) bytes
+ * Errors: GC_ERR_ARG (null pointer, d or k out of range, misalignment,
+ * out_idx/out_val overlapping mem or each other), GC_ERR_DTYPE,
+ * GC_ERR_WORKSPACE, GC_ERR_HIP.  NaN inputs are outside the contract. */
+int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, float eta,
+                      int64_t k, int32_t* out_idx, float* out_val,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Dense decode of a top-k message (the scatter side of the same method):
+ *   accumulate == 0:  out = 0 everywhere, then out[idx[j]] = val[j]
+ *                     (idx must be strictly ascending, as gc_topk_ef_encode writes it)
+ *   accumulate != 0:  out[idx[j]] += val[j] in float32 (idx must be unique)
+ *   idx [k] int32, val [k] float32, out [d] float32; 0 <= k <= d; 1 <= d <= INT32_MAX.
+ * Entries of idx outside [0, d) are ignored (never written).
+ * Errors: GC_ERR_ARG, GC_ERR_HIP. */
+int gc_topk_decode(const int32_t* idx, const float* val, int64_t k, float* out, int64_t d,
+                   int accumulate, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* PowerSGD rank-r with error feedback                                      */
+/* ------------------------------------------------------------------------ */
+
+/* One matrix of a PowerSGD step.  M = mem + eta*grad is n x m, row-major
+ * (a conv weight reshaped to out x (in*kh*kw)).  Q is m x rank and P is
+ * n x rank, both column-major with leading dimensions m and n, so the first
+ * columns stay in place when the rank changes. */
+typedef struct gc_mat {
+    const void* grad;  /* [n*m] float32 or bf16, read only                      */
+    float* mem;        /* [n*m] in/out: memory before / residual after          */
+    float* q;          /* [m*rank] in/out: warm-start Q in, new Q out           */
+    float* p;          /* [n*rank] out: orthonormal P^ (may be NULL)            */
+    float* out;        /* [n*m] out: decoded rank-r gradient P^ Q^T (may be NULL) */
+    int32_t n, m;      /* 1 <= n, m; n*m <= INT32_MAX                            */
+    int32_t rank;      /* 1 <= rank <= min(4, n, m)                             */
+} gc_mat;
+
+/* Workspace bytes for gc_powersgd_ef_step on these matrices ([host] array).
+ * Returns 0 when an entry is out of range. */
+size_t gc_powersgd_workspace_bytes(const gc_mat* mats, int nmats);
+
+/* One PowerSGD step with error feedback on every matrix of mats ([host], nmats >= 1):
+ *     M   = mem + eta*grad
+ *     P   = M Q;  P^ = Gram-Schmidt(P)  (a zero column stays zero)
+ *     Q   = M^T P^                      (written back to q: warm start)
+ *     out = P^ Q^T;  mem = M - out
+ * float32 storage; the Gram matrix and the orthonormalisation are in float64.
+ * Buffers of different matrices must not overlap.
+ * Errors: GC_ERR_ARG, GC_ERR_DTYPE, GC_ERR_WORKSPACE, GC_ERR_HIP. */
+int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Accordion: per-layer norms and the l_low / l_high switch                 */
+/* ------------------------------------------------------------------------ */
+
+typedef struct gc_span {
+    const void* ptr;   /* device pointer to one layer's gradient */
+    int64_t len;       /* elements, >= 1 */
+} gc_span;
+
+/* Workspace bytes for gc_grad_norm on these layers ([host] array). */
+size_t gc_grad_norm_workspace_bytes(const gc_span* layers, int nlayers);
+
+/* norms[l] = ||layer l||_2 for every layer in one pass (the quantity whose
+ * rate of change Accordion's method section monitors).  Squares are summed in
+ * float64; norms [nlayers] float32 device output.
+ * Errors: GC_ERR_ARG, GC_ERR_DTYPE, GC_ERR_WORKSPACE, GC_ERR_HIP. */
+int gc_grad_norm(const gc_span* layers, int nlayers, int grad_dtype, float* norms,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Host-only level choice for one check (Accordion, method section), per layer l:
+ *   has_prev == 0            -> GC_LEVEL_LOW
+ *   rho = |prev - now| / prev (prev == 0: rho = +inf if now > 0, else 0)
+ *   rho >= threshold         -> GC_LEVEL_LOW (critical regime), else GC_LEVEL_HIGH
+ * then norm_prev[l] = norm_now[l].  rho is computed in double.
+ *   norm_now [host, nlayers], norm_prev [host, nlayers] in/out, level [host, nlayers] out.
+ * Errors: GC_ERR_ARG (null pointer, nlayers < 1, negative or NaN threshold). */
+int gc_accordion_select(const float* norm_now, float* norm_prev, int nlayers, float threshold,
+                        int has_prev, int* level);
+
+/* ------------------------------------------------------------------------ */
+/* Measurement hooks                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Bracket every launch of the kernel named `kernel_name` (as listed by
+ * gc_kernel_names) with a pair of HIP events recorded on the launch stream;
+ * NULL or "" switches timing off and drops recorded events.  Process-wide. */
+int gc_timing_enable(const char* kernel_name);
+
+/* Synchronise on the recorded events and return the summed duration (ms) and
+ * the number of launches timed since gc_timing_enable; clears the record. */
+int gc_timing_read(double* total_ms, int64_t* launches);
+
+/* Comma-separated names of the library's kernels (static string). */
+const char* gc_kernel_names(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GC_H */

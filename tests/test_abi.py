@@ -1,0 +1,192 @@
+"""C-ABI checks that need no GPU: symbols, argument validation, host logic.
+
+Validation tests pass made-up (aligned, never dereferenced) device addresses:
+every call here fails validation, which the library does before any HIP call,
+so no kernel is ever launched.  They are skipped where a GPU is visible so that
+a validation bug can never turn into a launch on made-up pointers.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import gen
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gc.h")
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+no_gpu = pytest.mark.skipif(_gpu_visible(), reason="made-up device pointers are only passed where no GPU exists")
+
+
+@pytest.fixture(scope="module")
+def gcl():
+    import gradient_compression_error_amd as g
+    return g
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(gcl):
+    names = header_functions()
+    assert len(names) >= 13
+    out = subprocess.run(["nm", "-D", "--defined-only", gcl.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared in gc.h but not exported: {missing}"
+    for n in names:
+        assert hasattr(gcl.lib, n)
+    assert sorted(gcl.EXPORTED) == names
+
+
+def test_status_strings(gcl):
+    for s in range(5):
+        assert gcl.gc_status_str(s).startswith("GC_")
+    assert gcl.gc_status_str(99) == "unknown status"
+    assert "topk_accum_hist" in gcl.gc_kernel_names()
+
+
+def test_workspace_queries(gcl):
+    assert gcl.gc_topk_workspace_bytes(0, 1) == 0
+    assert gcl.gc_topk_workspace_bytes(10, 11) == 0
+    assert gcl.gc_topk_workspace_bytes(10, 0) == 0
+    assert gcl.gc_topk_workspace_bytes(2**31, 1) == 0
+    a = gcl.gc_topk_workspace_bytes(10_000, 100)
+    b = gcl.gc_topk_workspace_bytes(25_600_000, 256_000)
+    assert 0 < a < b and b >= 25_600_000 * 8
+    mats = (gcl.gc_mat * 2)(gcl.gc_mat(0x1000, 0x2000, 0x3000, None, None, 64, 27, 2),
+                            gcl.gc_mat(0x1000, 0x2000, 0x3000, None, None, 512, 4608, 4))
+    assert gcl.lib.gc_powersgd_workspace_bytes(mats, 2) > 0
+    bad = (gcl.gc_mat * 1)(gcl.gc_mat(0x1000, 0x2000, 0x3000, None, None, 0, 27, 2))
+    assert gcl.lib.gc_powersgd_workspace_bytes(bad, 1) == 0
+    spans = (gcl.gc_span * 2)(gcl.gc_span(0x1000, 5), gcl.gc_span(0x2000, 9000))
+    assert gcl.lib.gc_grad_norm_workspace_bytes(spans, 2) >= 3 * 8
+
+
+@no_gpu
+def test_topk_validation(gcl):
+    L = gcl.lib
+    A, B, I, V, W = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    ws = gcl.gc_topk_workspace_bytes(1000, 10)
+    ok = dict(grad=A, dt=gcl.GC_F32, mem=B, d=1000, eta=1.0, k=10, idx=I, val=V, ws=W, wsb=ws)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.gc_topk_ef_encode(a["grad"], a["dt"], a["mem"], a["d"], a["eta"], a["k"], a["idx"], a["val"],
+                                   a["ws"], a["wsb"], None)
+
+    assert call(grad=None) == gcl.GC_ERR_ARG
+    assert call(mem=None) == gcl.GC_ERR_ARG
+    assert call(ws=None) == gcl.GC_ERR_ARG
+    assert call(dt=7) == gcl.GC_ERR_DTYPE
+    assert call(d=0) == gcl.GC_ERR_ARG
+    assert call(d=2**31) == gcl.GC_ERR_ARG
+    assert call(k=0) == gcl.GC_ERR_ARG
+    assert call(k=1001) == gcl.GC_ERR_ARG
+    assert call(mem=B + 4) == gcl.GC_ERR_ARG                  # misaligned
+    assert call(idx=B + 16) == gcl.GC_ERR_ARG                 # aliases memory
+    assert call(val=I) == gcl.GC_ERR_ARG                      # idx/val alias
+    assert call(wsb=ws - 1) == gcl.GC_ERR_WORKSPACE
+    assert "workspace" in gcl.gc_last_error()
+    # decode
+    assert L.gc_topk_decode(I, V, 10, None, 1000, 0, None) == gcl.GC_ERR_ARG
+    assert L.gc_topk_decode(I, V, 1001, B, 1000, 0, None) == gcl.GC_ERR_ARG
+    assert L.gc_topk_decode(None, V, 5, B, 1000, 0, None) == gcl.GC_ERR_ARG
+    assert L.gc_topk_decode(I, V, 10, B, 0, 0, None) == gcl.GC_ERR_ARG
+    assert L.gc_topk_decode(I, V, 10, I, 1000, 0, None) == gcl.GC_ERR_ARG   # out overlaps idx
+
+
+@no_gpu
+def test_powersgd_validation(gcl):
+    L = gcl.lib
+
+    def mats(**kw):
+        base = dict(grad=0x100000, mem=0x200000, q=0x300000, p=0x400000, out=None, n=64, m=27, rank=2)
+        base.update(kw)
+        return (gcl.gc_mat * 1)(gcl.gc_mat(base["grad"], base["mem"], base["q"], base["p"], base["out"],
+                                           base["n"], base["m"], base["rank"]))
+
+    big = 1 << 30
+    def step(arr, dt=gcl.GC_F32, ws=0x900000, wsb=big):
+        return L.gc_powersgd_ef_step(arr, 1, dt, 1.0, ws, wsb, None)
+
+    assert step(mats(grad=None)) == gcl.GC_ERR_ARG
+    assert step(mats(q=None)) == gcl.GC_ERR_ARG
+    assert step(mats(n=0)) == gcl.GC_ERR_ARG
+    assert step(mats(rank=0)) == gcl.GC_ERR_ARG
+    assert step(mats(rank=5)) == gcl.GC_ERR_ARG
+    assert step(mats(n=3, rank=4)) == gcl.GC_ERR_ARG          # rank > min(n, m)
+    assert step(mats(m=2, rank=3)) == gcl.GC_ERR_ARG
+    assert step(mats(n=100000, m=100000)) == gcl.GC_ERR_ARG   # n*m > INT32_MAX
+    assert step(mats(q=0x300008)) == gcl.GC_ERR_ARG           # misaligned
+    assert step(mats(p=0x200000 + 64)) == gcl.GC_ERR_ARG      # p inside mem
+    assert step(mats(out=0x100000)) == gcl.GC_ERR_ARG         # out aliases grad
+    assert step(mats(), dt=3) == gcl.GC_ERR_DTYPE
+    assert step(mats(), ws=None) == gcl.GC_ERR_ARG
+    need = L.gc_powersgd_workspace_bytes(mats(), 1)
+    assert step(mats(), wsb=need - 1) == gcl.GC_ERR_WORKSPACE
+    assert L.gc_powersgd_ef_step(mats(), 0, 0, 1.0, 0x900000, big, None) == gcl.GC_ERR_ARG
+
+
+@no_gpu
+def test_norm_validation(gcl):
+    L = gcl.lib
+    spans = (gcl.gc_span * 2)(gcl.gc_span(0x100000, 5), gcl.gc_span(0x200000, 9000))
+    need = L.gc_grad_norm_workspace_bytes(spans, 2)
+    assert L.gc_grad_norm(spans, 0, 0, 0x300000, 0x400000, need, None) == gcl.GC_ERR_ARG
+    assert L.gc_grad_norm(spans, 2, 5, 0x300000, 0x400000, need, None) == gcl.GC_ERR_DTYPE
+    assert L.gc_grad_norm(spans, 2, 0, None, 0x400000, need, None) == gcl.GC_ERR_ARG
+    assert L.gc_grad_norm(spans, 2, 0, 0x300000, 0x400000, need - 1, None) == gcl.GC_ERR_WORKSPACE
+    bad = (gcl.gc_span * 1)(gcl.gc_span(0x100004, 5))
+    assert L.gc_grad_norm(bad, 1, 0, 0x300000, 0x400000, 1 << 20, None) == gcl.GC_ERR_ARG
+    empty = (gcl.gc_span * 1)(gcl.gc_span(0x100000, 0))
+    assert L.gc_grad_norm(empty, 1, 0, 0x300000, 0x400000, 1 << 20, None) == gcl.GC_ERR_ARG
+
+
+def test_accordion_host_matches_oracle(gcl):
+    r = gen.rng(0, gen.KIND_MISC, 200)
+    for trial in range(50):
+        n = int(r.integers(1, 40))
+        prev = (r.uniform(0, 2, n) * (r.uniform(size=n) > 0.1)).astype(np.float32)
+        now = (prev * r.uniform(0.2, 2.0, n) * (r.uniform(size=n) > 0.1)).astype(np.float32)
+        thr = float(r.choice([0.0, 0.25, 0.5, 1.0]))
+        for has_prev in (False, True):
+            lv, newp = gcl.gc_accordion_select(now, prev, thr, has_prev)
+            olv, onewp = oracle.accordion_select(now, prev, has_prev, thr)
+            assert np.array_equal(lv, olv)
+            assert np.array_equal(newp, onewp)
+    # exact ties and zero previous norm
+    lv, _ = gcl.gc_accordion_select([1.0, 3.0, 3.0, 0.5, 0.0], [2.0, 2.0, 4.0, 0.0, 0.0], 0.5, True)
+    assert lv.tolist() == [0, 0, 1, 0, 1]
+    with pytest.raises(gcl.GCError):
+        gcl.gc_accordion_select([1.0], [1.0], -0.5, True)
+    with pytest.raises(gcl.GCError):
+        gcl.gc_accordion_select([1.0], [1.0], float("nan"), True)
+
+
+def test_accordion_host_c4_schedule(gcl):
+    import json
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "c4_accordion_schedule.json")))
+    prev = np.zeros(1, np.float32)
+    lows = []
+    for i, t in enumerate(range(0, gold["steps"], gold["check_every"])):
+        lv, prev = gcl.gc_accordion_select(np.array([gen.c4_scale(t)], np.float32), prev, gold["threshold"], i > 0)
+        if lv[0] == gcl.GC_LEVEL_LOW:
+            lows.append(t)
+    assert lows == gold["low_checks"]

@@ -1,0 +1,164 @@
+"""GPU parity: PowerSGD EF steps vs the float64 oracle.
+
+Tolerance (from the float32 arithmetic): relative Frobenius error <= 1e-4 for
+P^, Q, the decoded matrix and the new memory, per matrix and per step.  Each
+GPU step is compared with an oracle step from the same input state (the GPU's
+memory and Q before the step), so float32-vs-float64 drift through the warm
+start cannot fail a correct kernel.  When a reference is ~0 (full-rank
+residual) the error is measured against ||M|| instead.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gpu_util import DEV, lib, rel_err, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+class PsgdSet:
+    """Device buffers for a list of (n, m) matrices with Q capacity 4 columns."""
+
+    def __init__(self, shapes, ranks, q_cfg=0, with_p=True, with_out=True):
+        self.shapes = list(shapes)
+        self.ranks = list(ranks)
+        self.mem = [torch.zeros(n, m, device=DEV) for n, m in self.shapes]
+        self.q = [to_dev(gen.q_init(q_cfg, l, m)) for l, (n, m) in enumerate(self.shapes)]
+        self.p = [torch.zeros(4, n, device=DEV) if with_p else None for n, m in self.shapes]
+        self.out = [torch.zeros(n, m, device=DEV) if with_out else None for n, m in self.shapes]
+        self.ws = None
+
+    def mats(self, grads):
+        gc = lib()
+        return [gc.Mat(grad=g, mem=self.mem[i], q=self.q[i], rank=self.ranks[i], p=self.p[i], out=self.out[i])
+                for i, g in enumerate(grads)]
+
+    def step(self, grads_dev, eta):
+        gc = lib()
+        mats = self.mats(grads_dev)
+        need = gc.gc_powersgd_workspace_bytes(mats)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        gc.gc_powersgd_ef_step(mats, eta, self.ws)
+
+
+def check_step(ps, grads_h, eta, label=""):
+    """One GPU step compared with the oracle from the same state; returns max error."""
+    mem_before = [t.cpu().numpy() for t in ps.mem]
+    q_before = [t.cpu().numpy() for t in ps.q]
+    ps.step([to_dev(g) for g in grads_h], eta)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i, (n, m) in enumerate(ps.shapes):
+        r = ps.ranks[i]
+        ref = oracle.powersgd_ef_step(grads_h[i], mem_before[i], q_before[i].T, eta, r)
+        Mn = np.linalg.norm(ref["M"])
+        checks = [("mem", ps.mem[i].cpu().numpy(), ref["mem"]), ("Q", ps.q[i].cpu().numpy()[:r].T, ref["Q"])]
+        if ps.out[i] is not None:
+            checks.append(("out", ps.out[i].cpu().numpy(), ref["out"]))
+        if ps.p[i] is not None:
+            checks.append(("P", ps.p[i].cpu().numpy()[:r].T, ref["P"]))
+        for name, got, want in checks:
+            wn = np.linalg.norm(want)
+            if name in ("mem", "out") and wn < 1e-6 * Mn:
+                err = np.linalg.norm(got.astype(np.float64) - want) / Mn
+            else:
+                err = rel_err(got, want)
+            worst = max(worst, err)
+            assert err <= TOL, f"{label} matrix {i} ({n}x{m}, r={r}) {name}: rel err {err:.3e}"
+        # columns of Q beyond the rank are untouched
+        if r < 4:
+            assert np.array_equal(ps.q[i].cpu().numpy()[r:], q_before[i][r:])
+    return worst
+
+
+SHAPES = [(64, 27, 1), (64, 27, 4), (7, 2, 2), (2, 9, 2), (1, 1, 1), (100, 512, 4), (128, 576, 2),
+          (33, 1030, 3), (1000, 3, 3), (4, 4608, 4), (513, 4608, 4), (17, 64, 4), (300, 2304, 1)]
+
+
+@pytest.mark.parametrize("n,m,r", SHAPES)
+def test_shapes_fp32(n, m, r):
+    print(f"case: psgd {n}x{m} r={r} fp32", flush=True)
+    ps = PsgdSet([(n, m)], [r])
+    for t in range(3):
+        g = gen.gaussian_mat(n, m, 100 + t, 1e-2)
+        check_step(ps, [g], 0.8, f"step {t}")
+
+
+@pytest.mark.parametrize("n,m,r", [(64, 27, 2), (513, 4608, 4), (1024, 1024, 4), (33, 1030, 3)])
+def test_shapes_bf16(n, m, r):
+    print(f"case: psgd {n}x{m} r={r} bf16", flush=True)
+    ps = PsgdSet([(n, m)], [r])
+    for t in range(2):
+        g = gen.f32_to_bf16_bits(gen.gaussian_mat(n, m, 200 + t, 1e-3))
+        check_step(ps, [g], 1.0, f"step {t}")
+
+
+@pytest.mark.parametrize("rank", [1, 2])
+def test_c2_resnet18(rank):
+    print(f"case: C2 ResNet-18 r={rank}", flush=True)
+    ps = PsgdSet(gen.RESNET18_MATS, [rank] * len(gen.RESNET18_MATS), q_cfg=gen.CFG_C2)
+    for t in range(3):
+        check_step(ps, gen.c2_grads(t), 1.0, f"C2 step {t}")
+
+
+def test_many_matrices_multi_batch():
+    """More matrices than one launch table holds, with mixed ranks and widths."""
+    print("case: 70 mixed matrices", flush=True)
+    r = gen.rng(0, gen.KIND_MISC, 400)
+    shapes = [(int(r.integers(1, 300)), int(r.choice([5, 64, 100, 576, 1030]))) for _ in range(70)]
+    ranks = [int(min(4, n, m, r.integers(1, 5))) for n, m in shapes]
+    ps = PsgdSet(shapes, ranks)
+    for t in range(2):
+        grads = [gen.gaussian_mat(n, m, 500 + 100 * t + i, 1e-2) for i, (n, m) in enumerate(shapes)]
+        check_step(ps, grads, 1.0, f"step {t}")
+
+
+def test_null_p_and_out():
+    print("case: p=NULL out=NULL", flush=True)
+    ps = PsgdSet([(128, 1152), (64, 27)], [2, 3], with_p=False, with_out=False)
+    check_step(ps, [gen.gaussian_mat(128, 1152, 600), gen.gaussian_mat(64, 27, 601)], 1.0)
+
+
+def test_rank_switch_in_place():
+    """Accordion-style 4 -> 2 -> 4 on the same Q buffer; grown columns refilled from the host."""
+    print("case: rank switch", flush=True)
+    n, m = 256, 2304
+    ps = PsgdSet([(n, m)], [4], q_cfg=gen.CFG_C4)
+    for t, r in enumerate([4, 4, 2, 2, 4, 4]):
+        if r > ps.ranks[0]:
+            fresh = gen.q_refill(gen.CFG_C4, 0, t, m, 4)
+            ps.q[0][ps.ranks[0]:r] = to_dev(fresh[ps.ranks[0]:r])
+        ps.ranks[0] = r
+        check_step(ps, [gen.gaussian_mat(n, m, 700 + t, 1e-2)], 1.0, f"step {t} r={r}")
+
+
+def test_determinism():
+    print("case: determinism", flush=True)
+    shapes = [(512, 4608), (64, 27), (1024, 1024)]
+    grads = [to_dev(gen.gaussian_mat(n, m, 800 + i)) for i, (n, m) in enumerate(shapes)]
+    res = []
+    for _ in range(2):
+        ps = PsgdSet(shapes, [4, 2, 4])
+        ps.step(grads, 1.0)
+        torch.cuda.synchronize()
+        res.append([t.cpu().numpy().copy() for t in ps.mem + ps.q + ps.out + ps.p])
+    for a, b in zip(*res):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_c5_bert_full():
+    """All 144 BERT-large matrices, bf16 gradients, fp32 memory, rank 4, at the benchmark's launch shape."""
+    print("case: C5 BERT-large 144 matrices r=4 bf16", flush=True)
+    ps = PsgdSet(gen.BERT_MATS, [4] * len(gen.BERT_MATS), q_cfg=gen.CFG_C5)
+    grads = [gen.c5_matrix_bf16(0, l) for l in range(len(gen.BERT_MATS))]
+    worst = check_step(ps, grads, 1.0, "C5")
+    print(f"C5 worst relative error {worst:.2e}")

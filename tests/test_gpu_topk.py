@@ -1,0 +1,170 @@
+"""GPU parity: top-k error-feedback encode/decode vs the CPU oracle, bit for bit.
+
+Indices, values, the memory after the step and the decoded vector must match
+the oracle exactly (selection order: |acc| descending, index ascending).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gpu_util import DEV, TopkRunner, f32_bits, lib, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def one_step(runner, grad_h, mem_h, eta, check_decode=True):
+    """Run one encode (+decode) on the GPU and compare with the oracle from the same state."""
+    mem_t = to_dev(mem_h.copy())
+    runner.encode(to_dev(grad_h), mem_t, eta)
+    if check_decode:
+        runner.decode()
+    ref = oracle.topk_ef_step(mem_h, grad_h, eta, runner.k)
+    torch.cuda.synchronize()
+    idx = runner.idx.cpu().numpy()
+    assert np.array_equal(idx, ref["idx"]), f"indices differ at {np.flatnonzero(idx != ref['idx'])[:10]}"
+    assert np.array_equal(f32_bits(runner.val), f32_bits(ref["val"]))
+    assert np.array_equal(f32_bits(mem_t), f32_bits(ref["mem"]))
+    if check_decode:
+        assert np.array_equal(f32_bits(runner.out), f32_bits(oracle.topk_decode(ref["idx"], ref["val"], runner.d)))
+    return ref
+
+
+def test_c1_ten_steps():
+    print("case: C1 d=10000 k=100 eta=0.1 x10", flush=True)
+    r = TopkRunner(gen.C1_D, gen.C1_K)
+    mem_h = np.zeros(gen.C1_D, np.float32)
+    mem_t = to_dev(mem_h)
+    for t in range(gen.C1_STEPS):
+        g = gen.c1_grad(t)
+        r.encode(to_dev(g), mem_t, gen.C1_ETA)
+        r.decode()
+        ref = oracle.topk_ef_step(mem_h, g, gen.C1_ETA, gen.C1_K)
+        torch.cuda.synchronize()
+        assert np.array_equal(r.idx.cpu().numpy(), ref["idx"])
+        assert np.array_equal(f32_bits(r.val), f32_bits(ref["val"]))
+        assert np.array_equal(f32_bits(mem_t), f32_bits(ref["mem"]))       # memory carried on the GPU
+        assert np.array_equal(f32_bits(r.out), f32_bits(ref["g"]))
+        mem_h = ref["mem"]
+
+
+@pytest.mark.parametrize("d,k", [(1, 1), (3, 2), (4, 4), (4095, 1), (4095, 4095), (4096, 100), (4097, 4097),
+                                 (12289, 1000), (12289, 1), (100_003, 777), (300_001, 30_000)])
+def test_edge_sizes(d, k):
+    print(f"case: edge d={d} k={k}", flush=True)
+    g = gen.gaussian_vector(d, d % 1000)
+    m = gen.gaussian_vector(d, d % 1000 + 1, 0.5)
+    one_step(TopkRunner(d, k), g, m, 0.37)
+
+
+@pytest.mark.parametrize("k", [1, 1000, 12_345, 49_999, 50_000])
+def test_tie_heavy(k):
+    print(f"case: tie-heavy d=50000 k={k}", flush=True)
+    d = 50_000
+    one_step(TopkRunner(d, k), gen.tie_heavy(d, k), np.zeros(d, np.float32), 1.0)
+    # ties across signs with memory: acc in {+-0.25 j}
+    one_step(TopkRunner(d, k), gen.tie_heavy(d, k + 1), gen.tie_heavy(d, k + 2), 1.0)
+
+
+def test_zero_and_extreme_values():
+    print("case: zeros / extremes", flush=True)
+    d = 9000
+    one_step(TopkRunner(d, 10), np.zeros(d, np.float32), np.zeros(d, np.float32), 1.0)
+    r = gen.rng(0, gen.KIND_MISC, 300)
+    g = (r.standard_normal(d) * np.exp2(r.integers(-120, 120, d))).astype(np.float32)
+    g[::7] = -0.0
+    g[::11] = 0.0
+    one_step(TopkRunner(d, 500), g, np.zeros(d, np.float32), 1.0)
+    one_step(TopkRunner(d, 8000), g, np.zeros(d, np.float32), 0.5)
+
+
+def test_bf16_gradient():
+    print("case: bf16 d=100003 k=1000", flush=True)
+    d = 100_003
+    g = gen.f32_to_bf16_bits(gen.gaussian_vector(d, 5, 1e-3))
+    one_step(TopkRunner(d, 1000), g, gen.gaussian_vector(d, 6, 1e-3), 1.0)
+
+
+def test_decode_accumulate():
+    print("case: decode accumulate", flush=True)
+    d, k = 20_000, 300
+    run = TopkRunner(d, k)
+    g = gen.gaussian_vector(d, 7)
+    ref = one_step(run, g, np.zeros(d, np.float32), 1.0, check_decode=False)
+    base = gen.gaussian_vector(d, 8)
+    run.out.copy_(to_dev(base))
+    run.decode(accumulate=True)
+    want = oracle.topk_decode(ref["idx"], ref["val"], d, out=base, accumulate=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(f32_bits(run.out), f32_bits(want))
+    # k = 0 decode: all zeros
+    gc = lib()
+    empty_i = torch.empty(0, dtype=torch.int32, device=DEV)
+    empty_v = torch.empty(0, dtype=torch.float32, device=DEV)
+    gc.gc_topk_decode(empty_i, empty_v, run.out)
+    torch.cuda.synchronize()
+    assert not run.out.any().item()
+
+
+def test_determinism_and_workspace_reuse():
+    print("case: determinism + workspace reuse", flush=True)
+    d, k = 500_000, 5000
+    g = to_dev(gen.gaussian_vector(d, 9))
+    m0 = gen.gaussian_vector(d, 10, 0.3)
+    run = TopkRunner(d, k)
+    outs = []
+    for _ in range(2):
+        mem = to_dev(m0)
+        run.encode(g, mem, 0.9)
+        torch.cuda.synchronize()
+        outs.append((run.idx.cpu().numpy().copy(), f32_bits(run.val).copy(), f32_bits(mem).copy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+    # the same workspace, reused for a smaller problem
+    gc = lib()
+    d2, k2 = 70_001, 70
+    g2, m2 = gen.gaussian_vector(d2, 11), gen.gaussian_vector(d2, 12)
+    idx2 = torch.empty(k2, dtype=torch.int32, device=DEV)
+    val2 = torch.empty(k2, dtype=torch.float32, device=DEV)
+    mem2 = to_dev(m2)
+    gc.gc_topk_ef_encode(to_dev(g2), mem2, 0.5, k2, idx2, val2, run.ws)
+    ref = oracle.topk_ef_step(m2, g2, 0.5, k2)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), ref["idx"])
+    assert np.array_equal(f32_bits(mem2), f32_bits(ref["mem"]))
+
+
+@pytest.mark.parametrize("k", gen.C3_KS)
+def test_c3_full_size(k):
+    """ResNet-50-sized flat gradient, heavy-tailed, at the benchmark's launch shape: 2 steps."""
+    print(f"case: C3 d={gen.C3_D} k={k}", flush=True)
+    d = gen.C3_D
+    run = TopkRunner(d, k)
+    mem_h = np.zeros(d, np.float32)
+    mem_t = to_dev(mem_h)
+    for t in range(2):
+        g = gen.c3_grad(t)
+        run.encode(to_dev(g), mem_t, 1.0)
+        run.decode()
+        ref = oracle.topk_ef_step(mem_h, g, 1.0, k)
+        torch.cuda.synchronize()
+        assert np.array_equal(run.idx.cpu().numpy(), ref["idx"])
+        assert np.array_equal(f32_bits(run.val), f32_bits(ref["val"]))
+        assert np.array_equal(f32_bits(mem_t), f32_bits(ref["mem"]))
+        assert np.array_equal(f32_bits(run.out), f32_bits(ref["g"]))
+        mem_h = ref["mem"]
+
+
+def test_c5_embedding_full_size():
+    """BERT-large embedding (30522 x 1024) bf16 gradient, fp32 memory, k = 1%: one step."""
+    print("case: C5 embedding bf16 k=312545", flush=True)
+    d = gen.BERT_EMB[0] * gen.BERT_EMB[1]
+    g = gen.c5_embedding_bf16(0)
+    m = gen.gaussian_vector(d, 13, 1e-3)
+    one_step(TopkRunner(d, gen.C5_EMB_K), g, m, 1.0)
