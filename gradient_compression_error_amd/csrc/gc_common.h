@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <string>
 
-#include "../../include/gc.h"
+#include "gc.h"
 
 namespace gc {
 
@@ -77,28 +77,76 @@ __device__ __forceinline__ unsigned long long lanemask_lt() {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-    return v;
+// Cross-lane moves through DPP (no LDS round trip).  All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u32(unsigned v) {
+    return static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) { return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v))); }
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const unsigned long long b = __double_as_longlong(v);
+    const unsigned lo = dpp_u32<CTRL>(static_cast<unsigned>(b));
+    const unsigned hi = dpp_u32<CTRL>(static_cast<unsigned>(b >> 32));
+    return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
 
-// Inclusive prefix sum over a 256-thread block in thread order.  `tmp` is a
-// __shared__ array of at least 4 entries; contains a barrier.
-__device__ __forceinline__ unsigned block_inclusive_scan_256(unsigned v, unsigned* tmp, unsigned* total) {
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_any(unsigned v) { return dpp_u32<CTRL>(v); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_any(float v) { return dpp_f32<CTRL>(v); }
+template <int CTRL>
+__device__ __forceinline__ double dpp_any(double v) { return dpp_f64<CTRL>(v); }
+
+__device__ __forceinline__ unsigned readlane_any(unsigned v, int l) {
+    return static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+}
+__device__ __forceinline__ float readlane_any(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_any(double v, int l) {
+    const unsigned long long b = __double_as_longlong(v);
+    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<unsigned>(b)), l));
+    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<unsigned>(b >> 32)), l));
+    return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
+// Sum over the 64 lanes of a wave, returned (bit-identical) in every lane.
+// Rows of 16 lanes are reduced with DPP, the four row sums combined in a
+// fixed order.  All lanes must be active.
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+    v += dpp_any<DPP_XOR1>(v);
+    v += dpp_any<DPP_XOR2>(v);
+    v += dpp_any<DPP_HALF_MIRROR>(v);
+    v += dpp_any<DPP_MIRROR>(v);
+    return (readlane_any(v, 0) + readlane_any(v, 16)) + (readlane_any(v, 32) + readlane_any(v, 48));
+}
+
+// Inclusive prefix sum over a block of NW waves in thread order; `tmp` is a
+// __shared__ array of at least NW entries.  Contains barriers; call from all
+// threads of the block.
+template <int NW>
+__device__ __forceinline__ unsigned block_inclusive_scan(unsigned v, unsigned* tmp, unsigned* total) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        unsigned t = __shfl_up(v, o, WAVE);
+        const unsigned t = __shfl_up(v, o, WAVE);
         if (lane >= o) v += t;
     }
     if (lane == 63) tmp[w] = v;
     __syncthreads();
     unsigned before = 0, all = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        unsigned t = tmp[i];
+    for (int i = 0; i < NW; ++i) {
+        const unsigned t = tmp[i];
         before += (i < w) ? t : 0u;
         all += t;
     }
@@ -107,29 +155,22 @@ __device__ __forceinline__ unsigned block_inclusive_scan_256(unsigned v, unsigne
     return v + before;
 }
 
-// Release this thread's prior global writes/atomics at device scope.
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
-__device__ __forceinline__ unsigned atomic_load_u32(const unsigned* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ unsigned block_inclusive_scan_256(unsigned v, unsigned* tmp, unsigned* total) {
+    return block_inclusive_scan<4>(v, tmp, total);
 }
 
-// True in every thread of the block that finished last among gridDim.x blocks.
-// All global writes made by the block before the call are visible to the last
-// block after it returns true.  Contains barriers; call from all threads.
-__device__ __forceinline__ bool last_block_done(unsigned* ticket) {
-    __shared__ unsigned s_last;
-    fence_release();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned t = atomicAdd(ticket, 1u);
-        s_last = (t == gridDim.x - 1) ? 1u : 0u;
+// Index of the segment containing block `blk`: the last i < count with
+// begin[i] <= blk (begin ascending, begin[0] = 0).  Binary search on a
+// kernel-argument array (uniform scalar loads).
+template <int N>
+__device__ __forceinline__ int find_segment(const int (&begin)[N], int count, int blk) {
+    int lo = 0, hi = count;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (begin[mid] <= blk) lo = mid;
+        else hi = mid;
     }
-    __syncthreads();
-    const bool last = s_last != 0;
-    if (last) fence_acquire();
-    return last;
+    return lo;
 }
 
 }  // namespace gc

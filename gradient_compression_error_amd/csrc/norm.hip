@@ -22,19 +22,16 @@ constexpr int NM_UNROLL = 4;
 constexpr int NM_TILE = NM_THREADS * 4 * NM_UNROLL;   // 4096
 constexpr int NM_MAXL = 160;
 
-struct NmSpan {
-    const void* ptr;
-    long long len;
-    int wg_begin;
-    int ntiles;
-};
-
+// Layer table of one launch; begin[l] = first workgroup of layer l.
 struct NmBatch {
     int count;
     int pad;
     double* partial;
     float* norms;
-    NmSpan s[NM_MAXL];
+    int begin[NM_MAXL];
+    int ntiles[NM_MAXL];
+    const void* ptr[NM_MAXL];
+    long long len[NM_MAXL];
 };
 static_assert(sizeof(NmBatch) <= 4096, "kernel argument table must fit 4 KB");
 
@@ -47,20 +44,20 @@ template <bool BF16>
 __global__ __launch_bounds__(NM_THREADS) void norm_partial(const NmBatch B) {
     __shared__ double s_w[4];
     const int blk = blockIdx.x;
-    int l = 0;
-    while (l + 1 < B.count && B.s[l + 1].wg_begin <= blk) ++l;
-    const NmSpan& S = B.s[l];
-    const long long base = static_cast<long long>(blk - S.wg_begin) * NM_TILE;
+    const int l = find_segment(B.begin, B.count, blk);
+    const void* ptr = B.ptr[l];
+    const long long len = B.len[l];
+    const long long base = static_cast<long long>(blk - B.begin[l]) * NM_TILE;
     double acc = 0.0;
-    if (base + NM_TILE <= S.len) {
+    if (base + NM_TILE <= len) {
         float4 v[NM_UNROLL];
 #pragma unroll
-        for (int u = 0; u < NM_UNROLL; ++u) v[u] = load_grad4<BF16>(S.ptr, base / 4 + u * NM_THREADS + threadIdx.x);
+        for (int u = 0; u < NM_UNROLL; ++u) v[u] = load_grad4<BF16>(ptr, base / 4 + u * NM_THREADS + threadIdx.x);
 #pragma unroll
         for (int u = 0; u < NM_UNROLL; ++u) acc += sq4(v[u]);
     } else {
-        for (long long i = base + threadIdx.x; i < S.len; i += NM_THREADS) {
-            const double x = load_grad1<BF16>(S.ptr, i);
+        for (long long i = base + threadIdx.x; i < len; i += NM_THREADS) {
+            const double x = load_grad1<BF16>(ptr, i);
             acc += x * x;
         }
     }
@@ -72,9 +69,9 @@ __global__ __launch_bounds__(NM_THREADS) void norm_partial(const NmBatch B) {
 
 __global__ __launch_bounds__(NM_THREADS) void norm_final(const NmBatch B) {
     __shared__ double s_w[4];
-    const NmSpan& S = B.s[blockIdx.x];
+    const int l = blockIdx.x;
     double acc = 0.0;
-    for (int t = threadIdx.x; t < S.ntiles; t += NM_THREADS) acc += B.partial[S.wg_begin + t];
+    for (int t = threadIdx.x; t < B.ntiles[l]; t += NM_THREADS) acc += B.partial[B.begin[l] + t];
     acc = wave_sum(acc);
     if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = acc;
     __syncthreads();
@@ -125,12 +122,12 @@ int gc_grad_norm(const gc_span* layers, int nlayers, int grad_dtype, float* norm
         B.norms = norms + l0;
         int blocks = 0;
         for (int l = l0; l < nlayers && B.count < NM_MAXL; ++l) {
-            NmSpan& S = B.s[B.count++];
-            S.ptr = layers[l].ptr;
-            S.len = layers[l].len;
-            S.wg_begin = blocks;
-            S.ntiles = static_cast<int>((layers[l].len + NM_TILE - 1) / NM_TILE);
-            blocks += S.ntiles;
+            const int i = B.count++;
+            B.ptr[i] = layers[l].ptr;
+            B.len[i] = layers[l].len;
+            B.begin[i] = blocks;
+            B.ntiles[i] = static_cast<int>((layers[l].len + NM_TILE - 1) / NM_TILE);
+            blocks += B.ntiles[i];
         }
         int rc;
         {

@@ -8,32 +8,56 @@
 //
 // Orthonormalisation is done in coefficient space: with G = P^T P (float64)
 // the Gram-Schmidt recurrence gives an upper-triangular T with P^ = P T, and
-// Q' = M^T P^ = (M^T P) T.  So the second pass over M does not wait for the
-// orthonormalisation and no n x r vector pass is needed:
+// Q' = M^T P^ = (M^T P) T.  So the pass that forms M^T P does not wait for
+// the orthonormalisation:
 //
-//   psgd_p       P = M Q_in per row (waves own rows, lanes stride columns),
-//                plus per-workgroup partial Gram matrices (float64)
-//   psgd_q       partial (M^T P) per (column strip, row chunk) workgroup
+//   psgd_pq_w/_b one pass over M: each row's P = M Q_in is finished by the
+//                team holding the row (one wave for m <= 1024, the 4-wave
+//                workgroup for m <= 4096), and the same registers add
+//                M[i,:]^T P[i,:] into per-column M^T P accumulators; one
+//                M^T P and one Gram (float64) partial per workgroup and matrix
+//   psgd_p/psgd_q the same two products as separate passes, for the other
+//                shapes (m not a multiple of 4, or m > 4096)
 //   psgd_qreduce sums the partials in a fixed order, builds T from the summed
 //                Gram matrix, writes Q' = (M^T P) T into q (warm start)
 //   psgd_out     P^ = P T per row, out = P^ Q'^T, mem = M - out, P^ into p
 //
-// M is never stored: each pass recomputes it from (mem, grad).  Matrices are
-// processed in batches whose gradient+memory bytes fit the 256 MB Infinity
-// Cache, so the second and third reads of a batch can hit it.  Every reduction
-// has a fixed order: the result bits do not depend on scheduling.
+// M is never stored: psgd_pq and psgd_out each recompute it from (mem, grad).
+// psgd_pq and psgd_out use a balanced persistent partition: the grid is about
+// what the GPU holds at once, and workgroup b takes the rows whose first entry
+// falls in the b-th equal share of the batch's entries, so no workgroup waits
+// on a second round.  Every reduction has a fixed order: the result bits do
+// not depend on scheduling.
+#include <algorithm>
+#include <vector>
+
 #include "gc_common.h"
 
 namespace gc {
 namespace {
 
 constexpr int PS_THREADS = 256;
-constexpr int PS_MAXB = 32;          // matrices per launch (kernel-argument table)
+constexpr int PS_MAXB = 28;          // matrices per launch (kernel-argument table)
 constexpr int P_ROWS_WAVE = 4;       // rows per wave in psgd_p
 constexpr int P_ROWS_WG = 16;        // rows per workgroup in psgd_p
 constexpr int Q_ROWS = 32;           // rows per chunk in psgd_q
-constexpr int O_ROWS = 32;           // rows per workgroup in psgd_out
-constexpr size_t PS_GROUP_BYTES = size_t(128) << 20;
+constexpr int ROW_GROUP = 8;         // rows whose loads are issued together in psgd_q / psgd_out
+constexpr int QR_COLS = 64;          // columns per workgroup in psgd_qreduce
+#ifndef GC_PQW_NS
+#define GC_PQW_NS 2
+#endif
+#ifndef GC_PQW_MINB
+#define GC_PQW_MINB 2
+#endif
+#ifndef GC_PQ_BLOCKS_PER_CU
+#define GC_PQ_BLOCKS_PER_CU 2
+#endif
+#ifndef GC_OUT_BLOCKS_PER_CU
+#define GC_OUT_BLOCKS_PER_CU 8
+#endif
+constexpr int CUS = 256;             // MI355X compute units
+constexpr int PQ_GRID_MAX = CUS * GC_PQ_BLOCKS_PER_CU;
+constexpr int OUT_GRID_MAX = CUS * GC_OUT_BLOCKS_PER_CU;
 
 struct PsMat {
     const void* grad;
@@ -42,37 +66,75 @@ struct PsMat {
     float* p;
     float* out;
     float* praw;     // [n][4]  P = M Q
-    double* gpart;   // [ceil(n/16)][16] partial Gram matrices
-    float* qpart;    // [ceil(n/32)][m][4] partial M^T P
+    double* gpart;   // [ng][16] partial Gram matrices
+    float* qpart;    // [nq][m][4] partial M^T P
     double* tmat;    // [16] T, row-major 4x4
+    long long off;   // first entry of the matrix in the batch (matrices back to back)
     int n, m, rank;
-    int wg_p, wg_q, wg_r, wg_o;
+    int nq, ng;      // number of M^T P / Gram partials
+    int pad;
 };
 
+// Matrix table of one launch group: wave-team shapes, workgroup-team shapes,
+// then the split-path shapes.
 struct PsBatch {
     int count;
+    int nwave;          // matrices [0, nwave): psgd_pq_w (m <= 1024)
+    int nfused;         // matrices [nwave, nfused): psgd_pq_b (m <= 4096); the rest: split path
     float eta;
-    int pad[2];
+    long long ew, eb;   // entries of the psgd_pq_w / psgd_pq_b matrices
+    long long eall;     // entries of all matrices
+    int gw, gb;         // psgd_pq_w / psgd_pq_b grids
+    int gout;           // psgd_out grid
+    int pad;
+    int begin_p[PS_MAXB];   // split path: first workgroup of each matrix in psgd_p / psgd_q
+    int begin_q[PS_MAXB];
+    int begin_r[PS_MAXB];   // psgd_qreduce
     PsMat mat[PS_MAXB];
 };
 static_assert(sizeof(PsBatch) <= 4096, "kernel argument table must fit 4 KB");
 
+// Balanced partition: workgroup b of g owns the rows whose first entry s
+// satisfies floor(s * g / e) == b, i.e. s in [ceil(b e / g), ceil((b+1) e / g)).
+__host__ __device__ __forceinline__ long long share_lo(long long e, int g, int b) {
+    return (static_cast<long long>(b) * e + g - 1) / g;
+}
+__host__ __device__ __forceinline__ int owner_of(long long s, long long e, int g) {
+    return static_cast<int>((s * g) / e);
+}
+
+// Matrix holding entry s among entries [0, cnt) of the table (last i with off <= s).
+__device__ __forceinline__ int mat_of_entry(const PsBatch& B, int cnt, long long s) {
+    int lo = 0, hi = cnt;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (B.mat[mid].off <= s) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Same, among entries [i0, i1); returns the index relative to i0.
+__device__ __forceinline__ int mat_of_entry_from(const PsBatch& B, int i0, int i1, long long s) {
+    int lo = i0, hi = i1;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (B.mat[mid].off <= s) lo = mid;
+        else hi = mid;
+    }
+    return lo - i0;
+}
+
+// Rows of matrix M whose first entry lies in [s_lo, s_hi).
+__device__ __forceinline__ void rows_in_share(const PsMat& M, long long s_lo, long long s_hi, int& r0, int& r1) {
+    const long long a = s_lo - M.off, b = s_hi - M.off;
+    r0 = a <= 0 ? 0 : static_cast<int>(min(static_cast<long long>(M.n), (a + M.m - 1) / M.m));
+    r1 = b <= 0 ? 0 : static_cast<int>(min(static_cast<long long>(M.n), (b + M.m - 1) / M.m));
+}
+
 __device__ __forceinline__ int nstrips_of(int m) {
     const int w = (m % 4 == 0) ? PS_THREADS * 4 : PS_THREADS;
     return (m + w - 1) / w;
-}
-
-template <int WHICH>
-__device__ __forceinline__ int first_block(const PsMat& M) {
-    return WHICH == 0 ? M.wg_p : WHICH == 1 ? M.wg_q : WHICH == 2 ? M.wg_r : M.wg_o;
-}
-
-template <int WHICH>
-__device__ __forceinline__ int find_mat(const PsBatch& B) {
-    const int blk = blockIdx.x;
-    int i = 0;
-    while (i + 1 < B.count && first_block<WHICH>(B.mat[i + 1]) <= blk) ++i;
-    return i;
 }
 
 // M values of 4 consecutive entries starting at flat element e (16-byte aligned)
@@ -89,14 +151,45 @@ __device__ __forceinline__ float load_M1(const PsMat& M, float eta, long long e)
     return ef_acc(M.mem[e], eta, load_grad1<BF16>(M.grad, e));
 }
 
-// ------------------------------------------------------------------ psgd_p
-
 template <bool BF16, int VEC>
-__device__ __forceinline__ void p_rows(const PsMat& M, float eta, int row0, float acc[P_ROWS_WAVE][4]) {
+__device__ __forceinline__ void load_Mv(const PsMat& M, float eta, long long e, float (&v)[VEC]) {
+    if constexpr (VEC == 4) {
+        const float4 t = load_M4<BF16>(M, eta, e);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+        v[0] = load_M1<BF16>(M, eta, e);
+    }
+}
+
+// Matrix of block `blk` among entries [i0, i1) of a launch table.
+__device__ __forceinline__ int find_in_range(const int* begin, int i0, int i1, int blk) {
+    int lo = i0, hi = i1;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (begin[mid] <= blk) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// ------------------------------------------------------------------ psgd_p / psgd_q (split path)
+
+// Each wave owns P_ROWS_WAVE rows; lanes stride over the row in VEC-wide
+// chunks.  The row loads of one chunk are issued before any use.
+template <bool BF16, int VEC>
+__device__ __forceinline__ void p_rows(const PsMat& M, float eta, int row0, float (&acc)[P_ROWS_WAVE][4]) {
     const int lane = threadIdx.x & 63;
     const int n = M.n, m = M.m, r = M.rank;
     const int nch = m / VEC;
+    int rowc[P_ROWS_WAVE];
+#pragma unroll
+    for (int rr = 0; rr < P_ROWS_WAVE; ++rr) rowc[rr] = min(row0 + rr, n - 1);
+#pragma unroll 2
     for (int c = lane; c < nch; c += 64) {
+        float mv[P_ROWS_WAVE][VEC];
+#pragma unroll
+        for (int rr = 0; rr < P_ROWS_WAVE; ++rr)
+            load_Mv<BF16, VEC>(M, eta, static_cast<long long>(rowc[rr]) * m + static_cast<long long>(c) * VEC, mv[rr]);
         float qv[VEC][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -114,30 +207,22 @@ __device__ __forceinline__ void p_rows(const PsMat& M, float eta, int row0, floa
         }
 #pragma unroll
         for (int rr = 0; rr < P_ROWS_WAVE; ++rr) {
-            const int row = row0 + rr;
-            if (row < n) {
-                const long long e = static_cast<long long>(row) * m + static_cast<long long>(c) * VEC;
-                float mv[VEC];
-                if constexpr (VEC == 4) {
-                    const float4 t = load_M4<BF16>(M, eta, e);
-                    mv[0] = t.x; mv[1] = t.y; mv[2] = t.z; mv[3] = t.w;
-                } else {
-                    mv[0] = load_M1<BF16>(M, eta, e);
-                }
+            if (row0 + rr < n) {
 #pragma unroll
                 for (int v = 0; v < VEC; ++v)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[rr][j] = fmaf(mv[v], qv[v][j], acc[rr][j]);
+                    for (int j = 0; j < 4; ++j) acc[rr][j] = fmaf(mv[rr][v], qv[v][j], acc[rr][j]);
             }
         }
     }
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(PS_THREADS) void psgd_p(const PsBatch B) {
+__global__ __launch_bounds__(PS_THREADS) void psgd_p(const PsBatch B, int i0, int i1) {
     __shared__ double s_g[4][16];
-    const PsMat& M = B.mat[find_mat<0>(B)];
-    const int lwg = blockIdx.x - M.wg_p;
+    const int mi = find_in_range(B.begin_p, i0, i1, blockIdx.x);
+    const PsMat& M = B.mat[mi];
+    const int lwg = blockIdx.x - B.begin_p[mi];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row0 = lwg * P_ROWS_WG + w * P_ROWS_WAVE;
     float acc[P_ROWS_WAVE][4];
@@ -153,29 +238,26 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_p(const PsBatch B) {
     for (int rr = 0; rr < P_ROWS_WAVE; ++rr)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[rr][j] = wave_sum(acc[rr][j]);
-    // every lane now holds the 4 finished rows of this wave
-    double g[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) g[i] = 0.0;
+    // every lane now holds the finished rows of this wave; lane i < 16 keeps
+    // Gram entry (i / 4, i % 4) summed over them (float64)
+    const int ga = (lane >> 2) & 3, gb = lane & 3;
+    double g = 0.0;
 #pragma unroll
     for (int rr = 0; rr < P_ROWS_WAVE; ++rr) {
         const int row = row0 + rr;
         if (row < M.n) {
             if (lane == rr)
                 reinterpret_cast<float4*>(M.praw)[row] = make_float4(acc[rr][0], acc[rr][1], acc[rr][2], acc[rr][3]);
+            float pa = acc[rr][0], pb = acc[rr][0];
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    g[a * 4 + b] += static_cast<double>(acc[rr][a]) * static_cast<double>(acc[rr][b]);
+            for (int j = 1; j < 4; ++j) {
+                pa = (ga == j) ? acc[rr][j] : pa;
+                pb = (gb == j) ? acc[rr][j] : pb;
+            }
+            g += static_cast<double>(pa) * static_cast<double>(pb);
         }
     }
-    if (lane < 16) {
-        double v = 0.0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v = (lane == i) ? g[i] : v;
-        s_g[w][lane] = v;
-    }
+    if (lane < 16) s_g[w][lane] = g;
     __syncthreads();
     if (threadIdx.x < 16) {
         const int i = threadIdx.x;
@@ -198,22 +280,25 @@ __device__ __forceinline__ void q_chunk(const PsMat& M, float eta, int strip, in
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[v][j] = 0.0f;
     const float4* praw4 = reinterpret_cast<const float4*>(M.praw);
-    for (int i = r0; i < r1; ++i) {
-        const float4 p = praw4[i];
-        const long long e = static_cast<long long>(i) * m + col0;
-        float mv[VEC];
-        if constexpr (VEC == 4) {
-            const float4 t = load_M4<BF16>(M, eta, e);
-            mv[0] = t.x; mv[1] = t.y; mv[2] = t.z; mv[3] = t.w;
-        } else {
-            mv[0] = load_M1<BF16>(M, eta, e);
+    for (int i0 = r0; i0 < r1; i0 += ROW_GROUP) {
+        float mv[ROW_GROUP][VEC];
+#pragma unroll
+        for (int u = 0; u < ROW_GROUP; ++u) {
+            const int row = min(i0 + u, r1 - 1);
+            load_Mv<BF16, VEC>(M, eta, static_cast<long long>(row) * m + col0, mv[u]);
         }
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            acc[v][0] = fmaf(mv[v], p.x, acc[v][0]);
-            acc[v][1] = fmaf(mv[v], p.y, acc[v][1]);
-            acc[v][2] = fmaf(mv[v], p.z, acc[v][2]);
-            acc[v][3] = fmaf(mv[v], p.w, acc[v][3]);
+        for (int u = 0; u < ROW_GROUP; ++u) {
+            if (i0 + u < r1) {
+                const float4 p = praw4[i0 + u];
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    acc[v][0] = fmaf(mv[u][v], p.x, acc[v][0]);
+                    acc[v][1] = fmaf(mv[u][v], p.y, acc[v][1]);
+                    acc[v][2] = fmaf(mv[u][v], p.z, acc[v][2]);
+                    acc[v][3] = fmaf(mv[u][v], p.w, acc[v][3]);
+                }
+            }
         }
     }
     float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(chunk) * m + col0;
@@ -222,15 +307,363 @@ __device__ __forceinline__ void q_chunk(const PsMat& M, float eta, int strip, in
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(PS_THREADS) void psgd_q(const PsBatch B) {
-    const PsMat& M = B.mat[find_mat<1>(B)];
-    const int lwg = blockIdx.x - M.wg_q;
+__global__ __launch_bounds__(PS_THREADS) void psgd_q(const PsBatch B, int i0, int i1) {
+    const int mi = find_in_range(B.begin_q, i0, i1, blockIdx.x);
+    const PsMat& M = B.mat[mi];
+    const int lwg = blockIdx.x - B.begin_q[mi];
     const int ns = nstrips_of(M.m);
     const int strip = lwg % ns, chunk = lwg / ns;
     if (M.m % 4 == 0)
         q_chunk<BF16, 4>(M, B.eta, strip, chunk);
     else
         q_chunk<BF16, 1>(M, B.eta, strip, chunk);
+}
+
+// ------------------------------------------------------------------ psgd_pq
+
+// Raw (unconverted) data of one float4 chunk of a row; converted to M at use,
+// so that loads issued rows ahead do not force a wait.
+template <bool BF16>
+struct RawChunk;
+template <>
+struct RawChunk<true> {
+    float4 m;
+    uint2 g;
+};
+template <>
+struct RawChunk<false> {
+    float4 m;
+    float4 g;
+};
+
+// Raw data of row `row`, chunks c0 + s*cstride clamped to the last chunk
+// (a clamped chunk repeats a valid one; its q is zero, so it adds nothing).
+// The row pointers are uniform, the chunk offsets 32-bit.
+// Buffer-resource view of rows [r0, r1) of a matrix's memory and gradient.
+// Loads address them with a 32-bit per-lane column offset (loop invariant)
+// and a scalar row offset; reads past r1 return zero and touch no memory.
+constexpr int BUF_WORD3 = 0x00020000;
+
+template <bool BF16>
+struct RowView {
+    __amdgpu_buffer_rsrc_t mem, grad;
+};
+
+template <bool BF16>
+__device__ __forceinline__ RowView<BF16> row_view(const PsMat& M, int r0, int r1) {
+    RowView<BF16> v;
+    const long long e0 = static_cast<long long>(r0) * M.m;
+    const int nrec = (r1 - r0) * M.m;
+    v.mem = __builtin_amdgcn_make_buffer_rsrc(M.mem + e0, 0, nrec * 4, BUF_WORD3);
+    if constexpr (BF16)
+        v.grad = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(static_cast<const unsigned short*>(M.grad)) + e0,
+                                                   0, nrec * 2, BUF_WORD3);
+    else
+        v.grad = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(static_cast<const float*>(M.grad)) + e0, 0,
+                                                   nrec * 4, BUF_WORD3);
+    return v;
+}
+
+// Raw data of row `k` of the view (k may run past its end: zeros), chunks
+// c0 + s*cstride (chunks past the row end alias the next row; their q is zero).
+template <bool BF16, int S>
+__device__ __forceinline__ void load_view_row(const RowView<BF16>& V, int k, int m, int c0, int cstride,
+                                              RawChunk<BF16> (&v)[S]) {
+    const int so_m = k * m * 4;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int c = c0 + s * cstride;
+        v[s].m = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(V.mem, c * 16, so_m, 0));
+        if constexpr (BF16) {
+            v[s].g = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(V.grad, c * 8, k * m * 2, 0));
+        } else {
+            v[s].g = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(V.grad, c * 16, so_m, 0));
+        }
+    }
+    // keep each row's loads together and in program order, so the waits for a
+    // row never cover a later row
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool BF16, int S>
+__device__ __forceinline__ void load_raw_row(const PsMat& M, int row, int c0, int cstride, int c4,
+                                             RawChunk<BF16> (&v)[S]) {
+    const long long e0 = static_cast<long long>(row) * M.m;
+    const float4* mrow = reinterpret_cast<const float4*>(M.mem + e0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int c = min(c0 + s * cstride, c4 - 1);
+        v[s].m = mrow[c];
+        if constexpr (BF16) v[s].g = reinterpret_cast<const uint2*>(static_cast<const unsigned short*>(M.grad) + e0)[c];
+        else v[s].g = reinterpret_cast<const float4*>(static_cast<const float*>(M.grad) + e0)[c];
+    }
+    // keep each row's loads together and in program order, so the waits for a
+    // row never cover a later row
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float4 raw_to_M(const RawChunk<BF16>& r, float eta) {
+    float4 g;
+    if constexpr (BF16) {
+        g = make_float4(__uint_as_float(r.g.x << 16), __uint_as_float(r.g.x & 0xFFFF0000u),
+                        __uint_as_float(r.g.y << 16), __uint_as_float(r.g.y & 0xFFFF0000u));
+    } else {
+        g = r.g;
+    }
+    return make_float4(ef_acc(r.m.x, eta, g.x), ef_acc(r.m.y, eta, g.y), ef_acc(r.m.z, eta, g.z),
+                       ef_acc(r.m.w, eta, g.w));
+}
+
+template <int S>
+__device__ __forceinline__ void load_q(const PsMat& M, int c0, int cstride, int c4, float (&q)[S][4][4]) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int c = c0 + s * cstride;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < c4 && j < M.rank) t = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * M.m)[c];
+            q[s][0][j] = t.x; q[s][1][j] = t.y; q[s][2][j] = t.z; q[s][3][j] = t.w;
+        }
+    }
+}
+
+template <int S>
+__device__ __forceinline__ void partial_p(const float4 (&v)[S], const float (&q)[S][4][4], float (&pp)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pp[j] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const float vv[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pp[j] = fmaf(vv[cc], q[s][cc][j], pp[j]);
+    }
+}
+
+template <int S>
+__device__ __forceinline__ void add_mtp(const float4 (&v)[S], const float (&p)[4], float (&qt)[S][4][4]) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const float vv[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qt[s][cc][j] = fmaf(vv[cc], p[j], qt[s][cc][j]);
+    }
+}
+
+__device__ __forceinline__ double gram_term(const float (&p)[4], int ga, int gb) {
+    float pa = p[0], pb = p[0];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) {
+        pa = (ga == j) ? p[j] : pa;
+        pb = (gb == j) ? p[j] : pb;
+    }
+    return static_cast<double>(pa) * static_cast<double>(pb);
+}
+
+constexpr int PQ_SW = 4;   // float4 chunks per lane, wave team (m <= 1024)
+constexpr int PQ_SB = 4;   // float4 chunks per thread, workgroup team (m <= 4096)
+constexpr int PQ_WAVE_MAX_M = 64 * 4 * PQ_SW;
+constexpr int PQ_BLOCK_MAX_M = PS_THREADS * 4 * PQ_SB;
+
+// Wave team: the workgroup's rows [r0, r1) are split into four contiguous
+// runs, one per wave; lane l owns float4 chunks l, l+64, ...; P of a row is a
+// DPP wave sum (no barrier).  NS raw slots form a ring: a step converts its
+// slot's row to M (waiting only for that row) and refills the slot with the
+// row NS ahead before the arithmetic.  The four waves' M^T P accumulators are
+// combined in LDS in wave order and written as partial `part`.
+template <bool BF16>
+__device__ __forceinline__ void pq_wave_team(const PsMat& M, float eta, int r0, int r1, int part, float4* s_qt,
+                                             double (*s_g)[16]) {
+    constexpr int S = PQ_SW;
+    constexpr int NS = GC_PQW_NS;
+    const int m = M.m, c4 = m / 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int R = r1 - r0;
+    const int rbeg = r0 + (w * R) / 4;
+    const int rend = r0 + ((w + 1) * R) / 4;
+    float q[S][4][4], qt[S][4][4];
+    load_q<S>(M, lane, 64, c4, q);
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qt[s][cc][j] = 0.0f;
+    const int ga = (lane >> 2) & 3, gb = lane & 3;
+    double g = 0.0;
+    if (rbeg < rend) {
+        const RowView<BF16> V = row_view<BF16>(M, rbeg, rend);
+        const int nr = rend - rbeg;
+        RawChunk<BF16> ring[NS][S];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) load_view_row<BF16, S>(V, k, m, lane, 64, ring[k]);
+        auto step = [&](RawChunk<BF16> (&slot)[S], int k) {
+            float4 v[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s) v[s] = raw_to_M<BF16>(slot[s], eta);
+            load_view_row<BF16, S>(V, k + NS, m, lane, 64, slot);
+            float pp[4], p[4];
+            partial_p<S>(v, q, pp);
+            const bool valid = k < nr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[j] = valid ? wave_sum(pp[j]) : 0.0f;
+            add_mtp<S>(v, p, qt);
+            if (valid) {
+                if (lane == 0) reinterpret_cast<float4*>(M.praw)[rbeg + k] = make_float4(p[0], p[1], p[2], p[3]);
+                g += gram_term(p, ga, gb);
+            }
+        };
+        for (int k = 0; k < nr; k += NS) {
+#pragma unroll
+            for (int t = 0; t < NS; ++t) step(ring[t], k + t);
+        }
+    }
+    for (int ww = 0; ww < 4; ++ww) {
+        if (w == ww) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const int c = lane + 64 * s;
+                if (c < c4) {
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) {
+                        float4 t = make_float4(qt[s][cc][0], qt[s][cc][1], qt[s][cc][2], qt[s][cc][3]);
+                        if (ww > 0) {
+                            const float4 o = s_qt[4 * c + cc];
+                            t = make_float4(o.x + t.x, o.y + t.y, o.z + t.z, o.w + t.w);
+                        }
+                        s_qt[4 * c + cc] = t;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(part) * m;
+    for (int e = threadIdx.x; e < m; e += PS_THREADS) dst[e] = s_qt[e];
+    if (lane < 16) s_g[w][lane] = g;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        const int t = threadIdx.x;
+        M.gpart[static_cast<long long>(part) * 16 + t] = ((s_g[0][t] + s_g[1][t]) + s_g[2][t]) + s_g[3][t];
+    }
+}
+
+// Workgroup team: all four waves share each row of [r0, r1), thread t owns
+// float4 chunks t, t+256, ...; P of a row = wave sums combined through LDS
+// (double-buffered, one barrier per row).
+template <bool BF16>
+__device__ __forceinline__ void pq_block_team(const PsMat& M, float eta, int r0, int r1, int part,
+                                              float (*s_p)[4][4]) {
+    constexpr int S = PQ_SB;
+    const int m = M.m, c4 = m / 4;
+    const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
+    const int rbeg = r0, rend = r1;
+    float q[S][4][4], qt[S][4][4];
+    load_q<S>(M, t, PS_THREADS, c4, q);
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qt[s][cc][j] = 0.0f;
+    const int ga = (lane >> 2) & 3, gb = lane & 3;
+    double g = 0.0;
+    constexpr int NS = BF16 ? 2 : 2;
+    {
+        RawChunk<BF16> ra[S], rb[S];
+        load_raw_row<BF16, S>(M, rbeg, t, PS_THREADS, c4, ra);
+        if constexpr (NS == 2) load_raw_row<BF16, S>(M, min(rbeg + 1, rend - 1), t, PS_THREADS, c4, rb);
+        auto step = [&](RawChunk<BF16> (&slot)[S], int i, int par) {
+            float4 v[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s) v[s] = raw_to_M<BF16>(slot[s], eta);
+            load_raw_row<BF16, S>(M, min(i + NS, rend - 1), t, PS_THREADS, c4, slot);
+            float pp[4], p[4];
+            partial_p<S>(v, q, pp);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pp[j] = wave_sum(pp[j]);
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s_p[par][w][j] = pp[j];
+            }
+            __syncthreads();
+            const bool valid = i < rend;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                p[j] = valid ? ((s_p[par][0][j] + s_p[par][1][j]) + s_p[par][2][j]) + s_p[par][3][j] : 0.0f;
+            add_mtp<S>(v, p, qt);
+            if (valid) {
+                if (t == 0) reinterpret_cast<float4*>(M.praw)[i] = make_float4(p[0], p[1], p[2], p[3]);
+                g += gram_term(p, ga, gb);
+            }
+        };
+        if constexpr (NS == 2) {
+            for (int i = rbeg; i < rend; i += 2) {
+                step(ra, i, 0);
+                step(rb, i + 1, 1);
+            }
+        } else {
+            for (int i = rbeg; i < rend; i += 2) {
+                step(ra, i, 0);
+                step(ra, i + 1, 1);
+            }
+        }
+    }
+    float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(part) * m;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int c = t + PS_THREADS * s;
+        if (c < c4) {
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+                dst[4 * c + cc] = make_float4(qt[s][cc][0], qt[s][cc][1], qt[s][cc][2], qt[s][cc][3]);
+        }
+    }
+    if (t < 16) M.gpart[static_cast<long long>(part) * 16 + t] = g;
+}
+
+// One pass over the wave-team matrices (m % 4 == 0, m <= 1024): workgroup b
+// takes its balanced share of their rows, matrix by matrix.
+template <bool BF16>
+__global__ __launch_bounds__(PS_THREADS, GC_PQW_MINB) void psgd_pq_w(const PsBatch B) {
+    __shared__ float4 s_qt[PQ_WAVE_MAX_M];
+    __shared__ double s_g[4][16];
+    const int b = blockIdx.x, G = B.gw;
+    const long long E = B.ew;
+    const long long s_lo = share_lo(E, G, b), s_hi = share_lo(E, G, b + 1);
+    for (int i = mat_of_entry(B, B.nwave, s_lo); i < B.nwave; ++i) {
+        const PsMat& M = B.mat[i];
+        if (M.off >= s_hi) break;
+        int r0, r1;
+        rows_in_share(M, s_lo, s_hi, r0, r1);
+        if (r0 >= r1) continue;
+        pq_wave_team<BF16>(M, B.eta, r0, r1, b - owner_of(M.off, E, G), s_qt, s_g);
+        __syncthreads();
+    }
+}
+
+// One pass over the workgroup-team matrices (m % 4 == 0, 1024 < m <= 4096),
+// whose entries start at B.ew in the table.
+template <bool BF16>
+__global__ __launch_bounds__(PS_THREADS, 2) void psgd_pq_b(const PsBatch B) {
+    __shared__ float s_p[2][4][4];
+    const int b = blockIdx.x, G = B.gb;
+    const long long E = B.eb, base = B.ew;
+    const long long s_lo = base + share_lo(E, G, b), s_hi = base + share_lo(E, G, b + 1);
+    for (int i = B.nwave + mat_of_entry_from(B, B.nwave, B.nfused, s_lo); i < B.nfused; ++i) {
+        const PsMat& M = B.mat[i];
+        if (M.off >= s_hi) break;
+        int r0, r1;
+        rows_in_share(M, s_lo, s_hi, r0, r1);
+        if (r0 >= r1) continue;
+        pq_block_team<BF16>(M, B.eta, r0, r1, b - owner_of(M.off - base, E, G), s_p);
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------------ psgd_qreduce
@@ -270,19 +703,23 @@ __device__ __forceinline__ void gram_schmidt_coeffs(const double G[16], int r, d
     }
 }
 
+// One workgroup per QR_COLS columns of one matrix: sums the M^T P partials of
+// its columns (waves split the partials, combined in a fixed order), rebuilds
+// G and T from the Gram partials, writes Q' = (M^T P) T.
 __global__ __launch_bounds__(PS_THREADS) void psgd_qreduce(const PsBatch B) {
     __shared__ double s_red[PS_THREADS / 64][16];
     __shared__ double s_T[16];
-    const PsMat& M = B.mat[find_mat<2>(B)];
-    const int lwg = blockIdx.x - M.wg_r;
-    const int n = M.n, m = M.m, r = M.rank;
+    __shared__ double s_part[PS_THREADS / 64][QR_COLS][4];
+    const int mi = find_in_range(B.begin_r, 0, B.count, blockIdx.x);
+    const PsMat& M = B.mat[mi];
+    const int lwg = blockIdx.x - B.begin_r[mi];
+    const int m = M.m, r = M.rank;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // Gram matrix: fixed-order sum of the psgd_p partials
-    const int ngp = (n + P_ROWS_WG - 1) / P_ROWS_WG;
+    // Gram matrix: fixed-order sum of the partials
     double g[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) g[i] = 0.0;
-    for (int b = threadIdx.x; b < ngp; b += PS_THREADS) {
+    for (int b = threadIdx.x; b < M.ng; b += PS_THREADS) {
         const double* src = M.gpart + static_cast<long long>(b) * 16;
 #pragma unroll
         for (int i = 0; i < 16; ++i) g[i] += src[i];
@@ -293,118 +730,152 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_qreduce(const PsBatch B) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s_red[w][i] = g[i];
     }
+    // column partials: lane = column, waves take every 4th partial
+    const int col = lwg * QR_COLS + lane;
+    const bool valid = col < m;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    if (valid) {
+        const float4* qp = reinterpret_cast<const float4*>(M.qpart) + col;
+#pragma unroll 4
+        for (int c = w; c < M.nq; c += 4) {
+            const float4 t = qp[static_cast<long long>(c) * m];
+            s0 += t.x; s1 += t.y; s2 += t.z; s3 += t.w;
+        }
+    }
+    s_part[w][lane][0] = s0;
+    s_part[w][lane][1] = s1;
+    s_part[w][lane][2] = s2;
+    s_part[w][lane][3] = s3;
     __syncthreads();
     if (threadIdx.x == 0) {
         double G[16], T[16];
+#pragma unroll
         for (int i = 0; i < 16; ++i) G[i] = ((s_red[0][i] + s_red[1][i]) + s_red[2][i]) + s_red[3][i];
         gram_schmidt_coeffs(G, r, T);
+#pragma unroll
         for (int i = 0; i < 16; ++i) s_T[i] = T[i];
-        if (lwg == 0)
+        if (lwg == 0) {
+#pragma unroll
             for (int i = 0; i < 16; ++i) M.tmat[i] = T[i];
+        }
     }
     __syncthreads();
-    const int col = lwg * PS_THREADS + threadIdx.x;
-    if (col >= m) return;
-    const int nch = (n + Q_ROWS - 1) / Q_ROWS;
-    double s[4] = {0.0, 0.0, 0.0, 0.0};
-    const float4* qp = reinterpret_cast<const float4*>(M.qpart) + col;
-    for (int c = 0; c < nch; ++c) {
-        const float4 t = qp[static_cast<long long>(c) * m];
-        s[0] += t.x; s[1] += t.y; s[2] += t.z; s[3] += t.w;
-    }
+    if (w == 0 && valid) {
+        double sv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j < r) {
-            double v = 0.0;
+        for (int a = 0; a < 4; ++a)
+            sv[a] = ((s_part[0][lane][a] + s_part[1][lane][a]) + s_part[2][lane][a]) + s_part[3][lane][a];
 #pragma unroll
-            for (int a = 0; a <= j; ++a) v += s[a] * s_T[a * 4 + j];
-            M.q[static_cast<long long>(j) * m + col] = static_cast<float>(v);
+        for (int j = 0; j < 4; ++j) {
+            if (j < r) {
+                double v = 0.0;
+#pragma unroll
+                for (int a = 0; a <= j; ++a) v += sv[a] * s_T[a * 4 + j];
+                M.q[static_cast<long long>(j) * m + col] = static_cast<float>(v);
+            }
         }
     }
 }
 
 // ------------------------------------------------------------------ psgd_out
 
+// Rows [r0, r1) of one matrix, one column strip at a time (Q of the strip in
+// registers); loads of ROW_GROUP rows are issued together.
 template <bool BF16, int VEC>
-__device__ __forceinline__ void out_rows(const PsMat& M, float eta, int strip, int chunk) {
+__device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int r1) {
     const int n = M.n, m = M.m, r = M.rank;
-    const int col0 = strip * (PS_THREADS * VEC) + threadIdx.x * VEC;
-    const bool active = col0 < m;
     float T[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) T[i] = static_cast<float>(M.tmat[i]);
-    float qv[VEC][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) qv[v][j] = 0.0f;
-        if (active && j < r) {
-            if constexpr (VEC == 4) {
-                const float4 t = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m + col0)[0];
-                qv[0][j] = t.x; qv[1][j] = t.y; qv[2][j] = t.z; qv[3][j] = t.w;
-            } else {
-                qv[0][j] = M.q[static_cast<long long>(j) * m + col0];
-            }
-        }
-    }
-    const int r0 = chunk * O_ROWS;
-    const int r1 = min(n, r0 + O_ROWS);
     const float4* praw4 = reinterpret_cast<const float4*>(M.praw);
-    const bool write_p = M.p != nullptr && strip == 0 && threadIdx.x < static_cast<unsigned>(r);
-    for (int i = r0; i < r1; ++i) {
-        const float4 pr = praw4[i];
-        const float prv[4] = {pr.x, pr.y, pr.z, pr.w};
-        float ph[4];
+    const int ns = nstrips_of(m);
+    for (int strip = 0; strip < ns; ++strip) {
+        const int col0 = strip * (PS_THREADS * VEC) + threadIdx.x * VEC;
+        const bool active = col0 < m;
+        float qv[VEC][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            float v = 0.0f;
 #pragma unroll
-            for (int a = 0; a <= j; ++a) v = fmaf(prv[a], T[a * 4 + j], v);
-            ph[j] = v;
-        }
-        if (write_p) {
-            float mine = ph[0];
-#pragma unroll
-            for (int j = 1; j < 4; ++j) mine = (threadIdx.x == static_cast<unsigned>(j)) ? ph[j] : mine;
-            M.p[static_cast<long long>(threadIdx.x) * n + i] = mine;
-        }
-        if (!active) continue;
-        const long long e = static_cast<long long>(i) * m + col0;
-        if constexpr (VEC == 4) {
-            const float4 mv = load_M4<BF16>(M, eta, e);
-            const float mva[4] = {mv.x, mv.y, mv.z, mv.w};
-            float o[4], nm[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float s = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s = fmaf(ph[j], qv[v][j], s);
-                o[v] = s;
-                nm[v] = mva[v] - s;
+            for (int v = 0; v < VEC; ++v) qv[v][j] = 0.0f;
+            if (active && j < r) {
+                if constexpr (VEC == 4) {
+                    const float4 t = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m + col0)[0];
+                    qv[0][j] = t.x; qv[1][j] = t.y; qv[2][j] = t.z; qv[3][j] = t.w;
+                } else {
+                    qv[0][j] = M.q[static_cast<long long>(j) * m + col0];
+                }
             }
-            if (M.out) reinterpret_cast<float4*>(M.out)[e / 4] = make_float4(o[0], o[1], o[2], o[3]);
-            reinterpret_cast<float4*>(M.mem)[e / 4] = make_float4(nm[0], nm[1], nm[2], nm[3]);
-        } else {
-            const float mv = load_M1<BF16>(M, eta, e);
-            float s = 0.0f;
+        }
+        const bool write_p = M.p != nullptr && strip == 0 && threadIdx.x < static_cast<unsigned>(r);
+        const int colc = active ? col0 : 0;
+        for (int i0 = r0; i0 < r1; i0 += ROW_GROUP) {
+            float mv[ROW_GROUP][VEC];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s = fmaf(ph[j], qv[0][j], s);
-            if (M.out) M.out[e] = s;
-            M.mem[e] = mv - s;
+            for (int u = 0; u < ROW_GROUP; ++u) {
+                const int row = min(i0 + u, r1 - 1);
+                load_Mv<BF16, VEC>(M, eta, static_cast<long long>(row) * m + colc, mv[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < ROW_GROUP; ++u) {
+                const int i = i0 + u;
+                if (i >= r1) break;
+                const float4 pr = praw4[i];
+                const float prv[4] = {pr.x, pr.y, pr.z, pr.w};
+                float ph[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int a = 0; a <= j; ++a) v = fmaf(prv[a], T[a * 4 + j], v);
+                    ph[j] = v;
+                }
+                if (write_p) {
+                    float mine = ph[0];
+#pragma unroll
+                    for (int j = 1; j < 4; ++j) mine = (threadIdx.x == static_cast<unsigned>(j)) ? ph[j] : mine;
+                    M.p[static_cast<long long>(threadIdx.x) * n + i] = mine;
+                }
+                if (!active) continue;
+                const long long e = static_cast<long long>(i) * m + col0;
+                float o[VEC], nm[VEC];
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    float sacc = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sacc = fmaf(ph[j], qv[v][j], sacc);
+                    o[v] = sacc;
+                    nm[v] = mv[u][v] - sacc;
+                }
+                if constexpr (VEC == 4) {
+                    if (M.out) reinterpret_cast<float4*>(M.out)[e / 4] = make_float4(o[0], o[1], o[2], o[3]);
+                    reinterpret_cast<float4*>(M.mem)[e / 4] = make_float4(nm[0], nm[1], nm[2], nm[3]);
+                } else {
+                    if (M.out) M.out[e] = o[0];
+                    M.mem[e] = nm[0];
+                }
+            }
         }
     }
 }
 
+// Decode + residual for every matrix of the table: workgroup b takes its
+// balanced share of rows.
 template <bool BF16>
 __global__ __launch_bounds__(PS_THREADS) void psgd_out(const PsBatch B) {
-    const PsMat& M = B.mat[find_mat<3>(B)];
-    const int lwg = blockIdx.x - M.wg_o;
-    const int ns = nstrips_of(M.m);
-    const int strip = lwg % ns, chunk = lwg / ns;
-    if (M.m % 4 == 0)
-        out_rows<BF16, 4>(M, B.eta, strip, chunk);
-    else
-        out_rows<BF16, 1>(M, B.eta, strip, chunk);
+    const int b = blockIdx.x, G = B.gout;
+    const long long E = B.eall;
+    const long long s_lo = share_lo(E, G, b), s_hi = share_lo(E, G, b + 1);
+    for (int i = mat_of_entry(B, B.count, s_lo); i < B.count; ++i) {
+        const PsMat& M = B.mat[i];
+        if (M.off >= s_hi) break;
+        int r0, r1;
+        rows_in_share(M, s_lo, s_hi, r0, r1);
+        if (r0 >= r1) continue;
+        if (M.m % 4 == 0)
+            out_rows<BF16, 4>(M, B.eta, r0, r1);
+        else
+            out_rows<BF16, 1>(M, B.eta, r0, r1);
+    }
 }
 
 // ------------------------------------------------------------------ host side
@@ -414,19 +885,95 @@ int nstrips_host(int m) {
     return (m + w - 1) / w;
 }
 
-struct MatWs {
-    size_t praw, gpart, qpart, tmat, bytes;
+// 0: wave-team fused pass, 1: workgroup-team fused pass, 2: split path
+int shape_class(int m) {
+    if (m % 4 != 0 || m > PQ_BLOCK_MAX_M) return 2;
+    return m <= PQ_WAVE_MAX_M ? 0 : 1;
+}
+
+// How the matrices are grouped and partitioned.  Shapes only (not ranks, not
+// the gradient dtype): the workspace query and the step make the same plan.
+struct PlanMat {
+    int idx;            // index in the caller's array
+    long long off;      // first entry within the batch
+    int nq, ng;         // partial counts
+    size_t ws_off;      // workspace offset of this matrix's scratch
+};
+struct PlanBatch {
+    int first, count, nwave, nfused;   // into Plan::mats
+    long long ew, eb, eall;
+    int gw, gb, gout;
+};
+struct Plan {
+    std::vector<PlanMat> mats;
+    std::vector<PlanBatch> batches;
+    size_t ws_bytes = 0;
 };
 
-MatWs mat_ws(int n, int m) {
-    MatWs W{};
+size_t ws_round(size_t x) { return round_up(x, 256); }
+
+// Grid of a balanced pass over e entries whose widest row has mmax entries:
+// every share is at least one such row, so a workgroup owns a row of every
+// matrix its share overlaps.
+int balanced_grid(long long e, int mmax, int gmax) {
+    return e > 0 ? static_cast<int>(std::min<long long>(gmax, std::max<long long>(1, e / mmax))) : 0;
+}
+
+Plan make_plan(const gc_mat* mats, int nmats) {
+    Plan P;
     size_t o = 0;
-    W.praw = o;  o += round_up(static_cast<size_t>(n) * 16, 256);
-    W.gpart = o; o += round_up(static_cast<size_t>((n + P_ROWS_WG - 1) / P_ROWS_WG) * 16 * 8, 256);
-    W.qpart = o; o += round_up(static_cast<size_t>((n + Q_ROWS - 1) / Q_ROWS) * m * 16, 256);
-    W.tmat = o;  o += 256;
-    W.bytes = o;
-    return W;
+    for (int i = 0; i < nmats;) {
+        const int j = std::min(nmats, i + PS_MAXB);
+        std::vector<int> idx;
+        for (int k = i; k < j; ++k) idx.push_back(k);
+        std::stable_sort(idx.begin(), idx.end(),
+                         [&](int a, int b) { return shape_class(mats[a].m) < shape_class(mats[b].m); });
+        PlanBatch pb{};
+        pb.first = static_cast<int>(P.mats.size());
+        pb.count = j - i;
+        int mw = 1, mb = 1;
+        for (int a : idx) {
+            const long long e = static_cast<long long>(mats[a].n) * mats[a].m;
+            const int c = shape_class(mats[a].m);
+            if (c == 0) { ++pb.nwave; pb.ew += e; mw = std::max(mw, mats[a].m); }
+            if (c == 1) { pb.eb += e; mb = std::max(mb, mats[a].m); }
+            if (c < 2) ++pb.nfused;
+        }
+        pb.gw = balanced_grid(pb.ew, mw, PQ_GRID_MAX);
+        pb.gb = balanced_grid(pb.eb, mb, PQ_GRID_MAX);
+        long long eall = 0;
+        for (int a : idx) {
+            PlanMat pm{};
+            pm.idx = a;
+            pm.off = eall;
+            const int n = mats[a].n, m = mats[a].m;
+            const int c = shape_class(m);
+            if (c < 2) {
+                const long long base = c == 0 ? 0 : pb.ew;
+                const long long E = c == 0 ? pb.ew : pb.eb;
+                const int G = c == 0 ? pb.gw : pb.gb;
+                const int first = owner_of(pm.off - base, E, G);
+                const int last = owner_of(pm.off - base + static_cast<long long>(n - 1) * m, E, G);
+                pm.nq = pm.ng = last - first + 1;
+            } else {
+                pm.nq = (n + Q_ROWS - 1) / Q_ROWS;
+                pm.ng = (n + P_ROWS_WG - 1) / P_ROWS_WG;
+            }
+            pm.ws_off = o;
+            o += ws_round(static_cast<size_t>(n) * 16);                       // praw
+            o += ws_round(static_cast<size_t>(pm.ng) * 16 * 8);               // gpart
+            o += ws_round(static_cast<size_t>(pm.nq) * m * 16);               // qpart
+            o += 256;                                                          // tmat
+            eall += static_cast<long long>(n) * m;
+            P.mats.push_back(pm);
+        }
+        pb.eall = eall;
+        pb.gout = static_cast<int>(std::min<long long>(OUT_GRID_MAX, std::max<long long>(1, eall / 1024)));
+        P.batches.push_back(pb);
+        i = j;
+    }
+    P.ws_bytes = o;
+    return P;
 }
 
 int validate_mat(const gc_mat& a, int i, int dtype) {
@@ -451,6 +998,56 @@ int validate_mat(const gc_mat& a, int i, int dtype) {
     return GC_OK;
 }
 
+// Launches all kernels of one batch (fused-shape entries first).
+template <bool BF16>
+int run_batch(PsBatch& B, hipStream_t s) {
+    int rc;
+    int nr = 0;
+    for (int i = 0; i < B.count; ++i) {
+        B.begin_r[i] = nr;
+        nr += (B.mat[i].m + QR_COLS - 1) / QR_COLS;
+    }
+    if (B.nwave > 0) {
+        TimedLaunch tl("psgd_pq_w", s);
+        psgd_pq_w<BF16><<<B.gw, PS_THREADS, 0, s>>>(B);
+        if ((rc = check_launch("psgd_pq_w")) != GC_OK) return rc;
+    }
+    if (B.nfused > B.nwave) {
+        TimedLaunch tl("psgd_pq_b", s);
+        psgd_pq_b<BF16><<<B.gb, PS_THREADS, 0, s>>>(B);
+        if ((rc = check_launch("psgd_pq_b")) != GC_OK) return rc;
+    }
+    if (B.nfused < B.count) {
+        int np = 0, nq = 0;
+        for (int i = B.nfused; i < B.count; ++i) {
+            const PsMat& M = B.mat[i];
+            B.begin_p[i] = np; np += (M.n + P_ROWS_WG - 1) / P_ROWS_WG;
+            B.begin_q[i] = nq; nq += nstrips_host(M.m) * ((M.n + Q_ROWS - 1) / Q_ROWS);
+        }
+        {
+            TimedLaunch tl("psgd_p", s);
+            psgd_p<BF16><<<np, PS_THREADS, 0, s>>>(B, B.nfused, B.count);
+            if ((rc = check_launch("psgd_p")) != GC_OK) return rc;
+        }
+        {
+            TimedLaunch tl("psgd_q", s);
+            psgd_q<BF16><<<nq, PS_THREADS, 0, s>>>(B, B.nfused, B.count);
+            if ((rc = check_launch("psgd_q")) != GC_OK) return rc;
+        }
+    }
+    {
+        TimedLaunch tl("psgd_qreduce", s);
+        psgd_qreduce<<<nr, PS_THREADS, 0, s>>>(B);
+        if ((rc = check_launch("psgd_qreduce")) != GC_OK) return rc;
+    }
+    {
+        TimedLaunch tl("psgd_out", s);
+        psgd_out<BF16><<<B.gout, PS_THREADS, 0, s>>>(B);
+        if ((rc = check_launch("psgd_out")) != GC_OK) return rc;
+    }
+    return GC_OK;
+}
+
 }  // namespace
 }  // namespace gc
 
@@ -460,13 +1057,11 @@ extern "C" {
 
 size_t gc_powersgd_workspace_bytes(const gc_mat* mats, int nmats) {
     if (!mats || nmats < 1) return 0;
-    size_t total = 0;
     for (int i = 0; i < nmats; ++i) {
         const gc_mat& a = mats[i];
         if (a.n < 1 || a.m < 1 || static_cast<long long>(a.n) * a.m > INT32_MAX) return 0;
-        total += mat_ws(a.n, a.m).bytes;
     }
-    return total;
+    return make_plan(mats, nmats).ws_bytes;
 }
 
 int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta,
@@ -480,71 +1075,50 @@ int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta
         const int rc = validate_mat(mats[i], i, grad_dtype);
         if (rc != GC_OK) return rc;
     }
-    const size_t need = gc_powersgd_workspace_bytes(mats, nmats);
-    if (ws_bytes < need)
+    const Plan P = make_plan(mats, nmats);
+    if (ws_bytes < P.ws_bytes)
         return fail(GC_ERR_WORKSPACE, "gc_powersgd_ef_step: workspace smaller than gc_powersgd_workspace_bytes");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool bf16 = grad_dtype == GC_BF16;
-    const size_t elem_bytes = bf16 ? 6 : 8;   // grad + memory per entry
     char* wp = static_cast<char*>(ws);
-    int i = 0;
-    while (i < nmats) {
+    for (const PlanBatch& pb : P.batches) {
         PsBatch B{};
+        B.count = pb.count;
+        B.nwave = pb.nwave;
+        B.nfused = pb.nfused;
         B.eta = eta;
-        int np = 0, nq = 0, nr = 0, no = 0;
-        size_t group = 0;
-        while (i < nmats && B.count < PS_MAXB) {
-            const gc_mat& a = mats[i];
-            const size_t bytes = static_cast<size_t>(a.n) * a.m * elem_bytes;
-            if (B.count > 0 && group + bytes > PS_GROUP_BYTES) break;
-            group += bytes;
-            const MatWs W = mat_ws(a.n, a.m);
-            PsMat& M = B.mat[B.count++];
+        B.ew = pb.ew;
+        B.eb = pb.eb;
+        B.eall = pb.eall;
+        B.gw = pb.gw;
+        B.gb = pb.gb;
+        B.gout = pb.gout;
+        for (int k = 0; k < pb.count; ++k) {
+            const PlanMat& pm = P.mats[pb.first + k];
+            const gc_mat& a = mats[pm.idx];
+            char* base = wp + pm.ws_off;
+            PsMat& M = B.mat[k];
             M.grad = a.grad;
             M.mem = a.mem;
             M.q = a.q;
             M.p = a.p;
             M.out = a.out;
-            M.praw = reinterpret_cast<float*>(wp + W.praw);
-            M.gpart = reinterpret_cast<double*>(wp + W.gpart);
-            M.qpart = reinterpret_cast<float*>(wp + W.qpart);
-            M.tmat = reinterpret_cast<double*>(wp + W.tmat);
+            M.praw = reinterpret_cast<float*>(base);
+            base += ws_round(static_cast<size_t>(a.n) * 16);
+            M.gpart = reinterpret_cast<double*>(base);
+            base += ws_round(static_cast<size_t>(pm.ng) * 16 * 8);
+            M.qpart = reinterpret_cast<float*>(base);
+            base += ws_round(static_cast<size_t>(pm.nq) * a.m * 16);
+            M.tmat = reinterpret_cast<double*>(base);
+            M.off = pm.off;
             M.n = a.n;
             M.m = a.m;
             M.rank = a.rank;
-            const int ns = nstrips_host(a.m);
-            M.wg_p = np; np += (a.n + P_ROWS_WG - 1) / P_ROWS_WG;
-            M.wg_q = nq; nq += ns * ((a.n + Q_ROWS - 1) / Q_ROWS);
-            M.wg_r = nr; nr += (a.m + PS_THREADS - 1) / PS_THREADS;
-            M.wg_o = no; no += ns * ((a.n + O_ROWS - 1) / O_ROWS);
-            wp += W.bytes;
-            ++i;
+            M.nq = pm.nq;
+            M.ng = pm.ng;
         }
-        int rc;
-        {
-            TimedLaunch tl("psgd_p", s);
-            if (bf16) psgd_p<true><<<np, PS_THREADS, 0, s>>>(B);
-            else psgd_p<false><<<np, PS_THREADS, 0, s>>>(B);
-            if ((rc = check_launch("psgd_p")) != GC_OK) return rc;
-        }
-        {
-            TimedLaunch tl("psgd_q", s);
-            if (bf16) psgd_q<true><<<nq, PS_THREADS, 0, s>>>(B);
-            else psgd_q<false><<<nq, PS_THREADS, 0, s>>>(B);
-            if ((rc = check_launch("psgd_q")) != GC_OK) return rc;
-        }
-        {
-            TimedLaunch tl("psgd_qreduce", s);
-            psgd_qreduce<<<nr, PS_THREADS, 0, s>>>(B);
-            if ((rc = check_launch("psgd_qreduce")) != GC_OK) return rc;
-        }
-        {
-            TimedLaunch tl("psgd_out", s);
-            if (bf16) psgd_out<true><<<no, PS_THREADS, 0, s>>>(B);
-            else psgd_out<false><<<no, PS_THREADS, 0, s>>>(B);
-            if ((rc = check_launch("psgd_out")) != GC_OK) return rc;
-        }
+        const int rc = grad_dtype == GC_BF16 ? run_batch<true>(B, s) : run_batch<false>(B, s);
+        if (rc != GC_OK) return rc;
     }
     return GC_OK;
 }

@@ -10,45 +10,48 @@
 //
 //   topk_accum_hist  acc = fl32(m + fl32(eta*g)) written over m; 4096-bin LDS
 //                    histogram of key>>19 per workgroup, merged with device
-//                    atomics; the last workgroup picks the level-1 bin b1.
+//                    atomics into one of 8 copies.                       topk_select1 -> bin b1
 //   topk_capture     re-reads acc; every entry with key>>19 >= b1 is appended,
 //                    in index order, to its tile's slot region (wave ballots +
 //                    a cross-wave prefix); entries in bin b1 feed the level-2
-//                    histogram; the last workgroup picks b2.
-//   topk_refine      level-3 histogram over the captured entries only; the
-//                    last workgroup fixes T and how many keys == T to take.
-//   topk_count       per tile: #(key > T), #(key == T); the last workgroup
-//                    scans both over tiles (ties go to the lowest indices).
+//                    histogram.                     topk_select2 -> bin b2
+//   topk_refine      level-3 histogram over the captured entries only.
+//                                                   topk_select3 -> T, ties to take
+//   topk_count       per tile: #(key > T), #(key == T).
+//                                                   topk_scan -> per-tile offsets
 //   topk_emit        writes the k (index, value) pairs in ascending index
 //                    order and zeroes the selected memory entries.
 //
 // Only the first two kernels touch all d entries (16 B/entry for fp32
-// gradients); the rest work on the captured entries.  No kernel waits on
-// another workgroup: the cross-workgroup steps are done by whichever
-// workgroup finishes last (device-scope ticket + fences).
+// gradients); the rest work on the captured entries.  The select/scan steps
+// are single-workgroup kernels: the kernel boundary is the only cross-
+// workgroup synchronisation (a per-workgroup device-scope release fence
+// would write back the L2 once per workgroup).
 #include "gc_common.h"
 
 namespace gc {
 namespace {
 
 constexpr int TK_THREADS = 256;
-constexpr int TK_UNROLL = 4;
-constexpr int TK_TILE = TK_THREADS * 4 * TK_UNROLL;  // 4096 entries per tile
+constexpr int TK_SUB = TK_THREADS * 4 * 4;   // 4096 entries: 4 float4 per thread
+constexpr int TK_SUBS = 4;
+constexpr int TK_TILE = TK_SUB * TK_SUBS;    // 16384 entries per workgroup / slot tile
 constexpr int H1_BINS = 4096;
 constexpr int H1_SHIFT = 19;   // key bits 30..19
 constexpr int H2_BINS = 4096;
 constexpr int H2_SHIFT = 7;    // key bits 18..7
 constexpr int H3_BINS = 128;   // key bits 6..0
+constexpr int NCOPY = 8;       // copies of the level-1/2 histograms (spreads the device atomics)
 constexpr int TK_SMALL_GRID = 1024;
 constexpr int DEC_TILE = 4096;
+constexpr int INIT_BLOCKS = 64;
 
 struct TopkState {
-    unsigned ticket[4];
     unsigned b1, above1;       // level-1 bin, #keys in higher level-1 bins
     unsigned prefix2, above2;  // (b1 << 12) | b2, #keys with (key >> 7) > prefix2
     unsigned thr, above3;      // threshold key T, #keys > T
     unsigned need;             // #keys == T taken (lowest indices first)
-    unsigned pad[5];
+    unsigned pad[9];
 };
 static_assert(sizeof(TopkState) == 64, "TopkState layout");
 
@@ -64,8 +67,8 @@ TopkLayout topk_layout(long long d) {
     const size_t nt = static_cast<size_t>(L.ntiles);
     size_t o = 0;
     L.state = o;     o += round_up(sizeof(TopkState), 256);
-    L.hist1 = o;     o += H1_BINS * 4;
-    L.hist2 = o;     o += H2_BINS * 4;
+    L.hist1 = o;     o += NCOPY * H1_BINS * 4;
+    L.hist2 = o;     o += NCOPY * H2_BINS * 4;
     L.hist3 = o;     o += round_up(H3_BINS * 4, 256);
     L.zero_bytes = o;
     L.tile_cnt = o;  o += round_up(nt * 4, 256);
@@ -81,38 +84,65 @@ TopkLayout topk_layout(long long d) {
 
 // ---------------------------------------------------------------- device helpers
 
-// Bin b of `hist` (scanned from the top) with
+// Bin b of the histogram (sum of NC copies spaced `stride` words apart,
+// scanned from the top) with
 //   sum(hist[b+1 ..]) < need <= sum(hist[b ..]);
 // *bin = b and *above = sum(hist[b+1 ..]).  Needs 1 <= need <= sum(hist).
-// `hist` is a device-wide histogram built with atomics: read with device-scope
-// atomic loads.  Whole block; results in shared memory after the final barrier.
-__device__ void select_bin_256(const unsigned* hist, int nbins, unsigned need, unsigned* s_tmp,
-                               unsigned* s_bin, unsigned* s_above) {
+// The histogram was completed by the previous kernel; its copies are summed
+// into LDS first (all loads independent).  Whole block; results in shared
+// memory after the final barrier.
+template <int NBINS, int NC>
+__device__ void select_bin_256(const unsigned* __restrict__ hist, int stride, unsigned need, unsigned* s_h,
+                               unsigned* s_tmp, unsigned* s_bin, unsigned* s_above) {
+    constexpr int PER = (NBINS + TK_THREADS - 1) / TK_THREADS;
     const int t = threadIdx.x;
     if (t == 0) {
         *s_bin = 0u;
         *s_above = 0u;
     }
-    const int per = (nbins + TK_THREADS - 1) / TK_THREADS;
-    int hi = nbins - t * per;
-    int lo = hi - per;
-    if (hi < 0) hi = 0;
-    if (lo < 0) lo = 0;
+    unsigned v[PER][NC];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int b = t + i * TK_THREADS;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) v[i][k] = (b < NBINS) ? hist[k * stride + b] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int b = t + i * TK_THREADS;
+        unsigned c = 0;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) c += v[i][k];
+        if (b < NBINS) s_h[b] = c;
+    }
+    __syncthreads();
+    // thread t scans bins [hi - PER, hi) from the top
+    const int hi = NBINS - t * PER;
+    unsigned cnt[PER];
     unsigned s = 0;
-    for (int b = lo; b < hi; ++b) s += atomic_load_u32(hist + b);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int b = hi - PER + i;
+        cnt[i] = (b >= 0 && b < NBINS) ? s_h[b] : 0u;
+        s += cnt[i];
+    }
     unsigned total;
     const unsigned incl = block_inclusive_scan_256(s, s_tmp, &total);
     const unsigned excl = incl - s;
     if (s > 0 && excl < need && need <= incl) {
         unsigned run = excl;
-        for (int b = hi - 1; b >= lo; --b) {
-            const unsigned c = atomic_load_u32(hist + b);
-            if (run + c >= need) {
-                *s_bin = static_cast<unsigned>(b);
-                *s_above = run;
-                break;
+        bool found = false;
+#pragma unroll
+        for (int i = PER - 1; i >= 0; --i) {
+            const int b = hi - PER + i;
+            if (!found && b >= 0) {
+                if (run + cnt[i] >= need) {
+                    *s_bin = static_cast<unsigned>(b);
+                    *s_above = run;
+                    found = true;
+                }
+                run += cnt[i];
             }
-            run += c;
         }
     }
     __syncthreads();
@@ -120,32 +150,42 @@ __device__ void select_bin_256(const unsigned* hist, int nbins, unsigned need, u
 
 // ---------------------------------------------------------------- kernels
 
-__global__ __launch_bounds__(256) void topk_init(unsigned* __restrict__ zero, int nwords) {
-    for (int i = threadIdx.x; i < nwords; i += blockDim.x) zero[i] = 0u;
+__global__ __launch_bounds__(256) void topk_init(uint4* __restrict__ zero, int n16) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n16; i += gridDim.x * 256) zero[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 template <bool BF16>
+__device__ __forceinline__ void load_sub(const void* __restrict__ grad, const float* __restrict__ mem, long long b4,
+                                         float4 (&gv)[4], float4 (&mv)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const long long i4 = b4 + u * TK_THREADS + threadIdx.x;
+        gv[u] = load_grad4<BF16>(grad, i4);
+        mv[u] = reinterpret_cast<const float4*>(mem)[i4];
+    }
+}
+
+// acc = fl32(m + fl32(eta*g)) over TK_TILE entries per workgroup (sub-tile s+1
+// is loaded before sub-tile s is stored), with a level-1 histogram in LDS.
+template <bool BF16>
 __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
-        const void* __restrict__ grad, float* __restrict__ mem, long long d, float eta, unsigned k,
-        unsigned* __restrict__ hist1, TopkState* __restrict__ st) {
+        const void* __restrict__ grad, float* __restrict__ mem, long long d, float eta,
+        unsigned* __restrict__ hist1) {
     __shared__ unsigned h[H1_BINS];
-    __shared__ unsigned s_tmp[4];
-    __shared__ unsigned s_bin, s_above;
     for (int i = threadIdx.x; i < H1_BINS; i += TK_THREADS) h[i] = 0u;
     __syncthreads();
 
     const long long base = static_cast<long long>(blockIdx.x) * TK_TILE;
-    if (base + TK_TILE <= d) {
-        const long long b4 = base / 4;
-        float4 gv[TK_UNROLL], mv[TK_UNROLL];
+    long long nfull = (d - base) / TK_SUB;
+    if (nfull > TK_SUBS) nfull = TK_SUBS;
+    float4 gv[4], mv[4];
+    if (nfull > 0) load_sub<BF16>(grad, mem, base / 4, gv, mv);
+    for (int sb = 0; sb < nfull; ++sb) {
+        const long long b4 = (base + static_cast<long long>(sb) * TK_SUB) / 4;
+        float4 gn[4], mn[4];
+        if (sb + 1 < nfull) load_sub<BF16>(grad, mem, b4 + TK_SUB / 4, gn, mn);
 #pragma unroll
-        for (int u = 0; u < TK_UNROLL; ++u) {
-            const long long i4 = b4 + u * TK_THREADS + threadIdx.x;
-            gv[u] = load_grad4<BF16>(grad, i4);
-            mv[u] = reinterpret_cast<const float4*>(mem)[i4];
-        }
-#pragma unroll
-        for (int u = 0; u < TK_UNROLL; ++u) {
+        for (int u = 0; u < 4; ++u) {
             float4 a;
             a.x = ef_acc(mv[u].x, eta, gv[u].x);
             a.y = ef_acc(mv[u].y, eta, gv[u].y);
@@ -157,35 +197,49 @@ __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
             atomicAdd(&h[key_of(a.z) >> H1_SHIFT], 1u);
             atomicAdd(&h[key_of(a.w) >> H1_SHIFT], 1u);
         }
-    } else {
-        for (long long i = base + threadIdx.x; i < d; i += TK_THREADS) {
-            const float a = ef_acc(mem[i], eta, load_grad1<BF16>(grad, i));
-            mem[i] = a;
-            atomicAdd(&h[key_of(a) >> H1_SHIFT], 1u);
+        if (sb + 1 < nfull) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                gv[u] = gn[u];
+                mv[u] = mn[u];
+            }
         }
+    }
+    const long long t0 = base + nfull * TK_SUB;
+    const long long t1 = min(d, base + static_cast<long long>(TK_TILE));
+    for (long long i = t0 + threadIdx.x; i < t1; i += TK_THREADS) {
+        const float a = ef_acc(mem[i], eta, load_grad1<BF16>(grad, i));
+        mem[i] = a;
+        atomicAdd(&h[key_of(a) >> H1_SHIFT], 1u);
     }
     __syncthreads();
+    unsigned* dst = hist1 + (blockIdx.x % NCOPY) * H1_BINS;
     for (int i = threadIdx.x; i < H1_BINS; i += TK_THREADS) {
         const unsigned c = h[i];
-        if (c) atomicAdd(hist1 + i, c);
-    }
-    if (last_block_done(&st->ticket[0])) {
-        select_bin_256(hist1, H1_BINS, k, s_tmp, &s_bin, &s_above);
-        if (threadIdx.x == 0) {
-            st->b1 = s_bin;
-            st->above1 = s_above;
-        }
+        if (c) atomicAdd(dst + i, c);
     }
 }
 
+__global__ __launch_bounds__(TK_THREADS) void topk_select1(const unsigned* __restrict__ hist1, unsigned k,
+                                                           TopkState* __restrict__ st) {
+    __shared__ unsigned s_h[H1_BINS];
+    __shared__ unsigned s_tmp[4];
+    __shared__ unsigned s_bin, s_above;
+    select_bin_256<H1_BINS, NCOPY>(hist1, H1_BINS, k, s_h, s_tmp, &s_bin, &s_above);
+    if (threadIdx.x == 0) {
+        st->b1 = s_bin;
+        st->above1 = s_above;
+    }
+}
+
+// Re-reads acc; appends every entry with key>>19 >= b1, in index order, to the
+// workgroup's slot tile; entries in bin b1 feed the level-2 histogram.
 __global__ __launch_bounds__(TK_THREADS) void topk_capture(
-        const float* __restrict__ acc, long long d, unsigned k, TopkState* __restrict__ st,
+        const float* __restrict__ acc, long long d, const TopkState* __restrict__ st,
         unsigned* __restrict__ hist2, int* __restrict__ slot_idx, float* __restrict__ slot_val,
         unsigned* __restrict__ tile_cnt) {
     __shared__ unsigned h[H2_BINS];
-    __shared__ unsigned s_wave[4];
-    __shared__ unsigned s_tmp[4];
-    __shared__ unsigned s_bin, s_above;
+    __shared__ unsigned s_wave[2][4];
     for (int i = threadIdx.x; i < H2_BINS; i += TK_THREADS) h[i] = 0u;
     __syncthreads();
 
@@ -196,77 +250,90 @@ __global__ __launch_bounds__(TK_THREADS) void topk_capture(
     int* const sidx = slot_idx + base;
     float* const sval = slot_val + base;
     unsigned running = 0;
+    int parity = 0;
+    for (int sb = 0; sb < TK_SUBS; ++sb) {
+        const long long sbase = base + static_cast<long long>(sb) * TK_SUB;
+        if (sbase >= d) break;
+        float v[4][4];
+        bool ok[4][4];
 #pragma unroll
-    for (int u = 0; u < TK_UNROLL; ++u) {
-        const long long e0 = base + u * (TK_THREADS * 4) + threadIdx.x * 4;
-        float v[4];
-        bool ok[4];
-        if (e0 + 3 < d) {
-            const float4 a = reinterpret_cast<const float4*>(acc)[e0 / 4];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            ok[0] = ok[1] = ok[2] = ok[3] = true;
-        } else {
+        for (int u = 0; u < 4; ++u) {
+            const long long e0 = sbase + u * (TK_THREADS * 4) + threadIdx.x * 4;
+            if (e0 + 3 < d) {
+                const float4 a = reinterpret_cast<const float4*>(acc)[e0 / 4];
+                v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+                ok[u][0] = ok[u][1] = ok[u][2] = ok[u][3] = true;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    ok[u][j] = (e0 + j) < d;
+                    v[u][j] = ok[u][j] ? acc[e0 + j] : 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const long long e0 = sbase + u * (TK_THREADS * 4) + threadIdx.x * 4;
+            bool cap[4];
+            unsigned before = 0, wtot = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                ok[j] = (e0 + j) < d;
-                v[j] = ok[j] ? acc[e0 + j] : 0.0f;
+                const unsigned key = key_of(v[u][j]);
+                const unsigned bin = key >> H1_SHIFT;
+                cap[j] = ok[u][j] && bin >= b1;
+                if (ok[u][j] && bin == b1) atomicAdd(&h[(key >> H2_SHIFT) & (H2_BINS - 1)], 1u);
+                const unsigned long long bal = __ballot(cap[j]);
+                before += __popcll(bal & lt);
+                wtot += __popcll(bal);
             }
-        }
-        bool cap[4];
-        unsigned before = 0, wtot = 0;
+            if (lane == 0) s_wave[parity][w] = wtot;
+            __syncthreads();
+            unsigned wbefore = 0, ctot = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const unsigned key = key_of(v[j]);
-            const unsigned bin = key >> H1_SHIFT;
-            cap[j] = ok[j] && bin >= b1;
-            if (ok[j] && bin == b1) atomicAdd(&h[(key >> H2_SHIFT) & (H2_BINS - 1)], 1u);
-            const unsigned long long bal = __ballot(cap[j]);
-            before += __popcll(bal & lt);
-            wtot += __popcll(bal);
-        }
-        if (lane == 0) s_wave[w] = wtot;
-        __syncthreads();
-        unsigned wbefore = 0, ctot = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const unsigned t = s_wave[i];
-            wbefore += (i < w) ? t : 0u;
-            ctot += t;
-        }
-        __syncthreads();
-        unsigned pos = running + wbefore + before;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (cap[j]) {
-                sidx[pos] = static_cast<int>(e0 + j);
-                sval[pos] = v[j];
-                ++pos;
+            for (int i = 0; i < 4; ++i) {
+                const unsigned t = s_wave[parity][i];
+                wbefore += (i < w) ? t : 0u;
+                ctot += t;
             }
+            parity ^= 1;
+            unsigned pos = running + wbefore + before;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (cap[j]) {
+                    sidx[pos] = static_cast<int>(e0 + j);
+                    sval[pos] = v[u][j];
+                    ++pos;
+                }
+            }
+            running += ctot;
         }
-        running += ctot;
     }
     if (threadIdx.x == 0) tile_cnt[blockIdx.x] = running;
     __syncthreads();
+    unsigned* dst = hist2 + (blockIdx.x % NCOPY) * H2_BINS;
     for (int i = threadIdx.x; i < H2_BINS; i += TK_THREADS) {
         const unsigned c = h[i];
-        if (c) atomicAdd(hist2 + i, c);
+        if (c) atomicAdd(dst + i, c);
     }
-    if (last_block_done(&st->ticket[1])) {
-        const unsigned above1 = st->above1;
-        select_bin_256(hist2, H2_BINS, k - above1, s_tmp, &s_bin, &s_above);
-        if (threadIdx.x == 0) {
-            st->prefix2 = (b1 << 12) | s_bin;
-            st->above2 = above1 + s_above;
-        }
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_select2(const unsigned* __restrict__ hist2, unsigned k,
+                                                           TopkState* __restrict__ st) {
+    __shared__ unsigned s_h[H2_BINS];
+    __shared__ unsigned s_tmp[4];
+    __shared__ unsigned s_bin, s_above;
+    const unsigned above1 = st->above1;
+    select_bin_256<H2_BINS, NCOPY>(hist2, H2_BINS, k - above1, s_h, s_tmp, &s_bin, &s_above);
+    if (threadIdx.x == 0) {
+        st->prefix2 = (st->b1 << 12) | s_bin;
+        st->above2 = above1 + s_above;
     }
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_refine(
-        unsigned k, TopkState* __restrict__ st, unsigned* __restrict__ hist3,
+        const TopkState* __restrict__ st, unsigned* __restrict__ hist3,
         const float* __restrict__ slot_val, const unsigned* __restrict__ tile_cnt, int ntiles) {
     __shared__ unsigned h[H3_BINS];
-    __shared__ unsigned s_tmp[4];
-    __shared__ unsigned s_bin, s_above;
     for (int i = threadIdx.x; i < H3_BINS; i += TK_THREADS) h[i] = 0u;
     __syncthreads();
     const unsigned prefix2 = st->prefix2;
@@ -283,24 +350,28 @@ __global__ __launch_bounds__(TK_THREADS) void topk_refine(
         const unsigned c = h[i];
         if (c) atomicAdd(hist3 + i, c);
     }
-    if (last_block_done(&st->ticket[2])) {
-        const unsigned above2 = st->above2;
-        select_bin_256(hist3, H3_BINS, k - above2, s_tmp, &s_bin, &s_above);
-        if (threadIdx.x == 0) {
-            const unsigned above3 = above2 + s_above;
-            st->thr = (prefix2 << H2_SHIFT) | s_bin;
-            st->above3 = above3;
-            st->need = k - above3;
-        }
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_select3(const unsigned* __restrict__ hist3, unsigned k,
+                                                           TopkState* __restrict__ st) {
+    __shared__ unsigned s_h[H3_BINS];
+    __shared__ unsigned s_tmp[4];
+    __shared__ unsigned s_bin, s_above;
+    const unsigned above2 = st->above2;
+    select_bin_256<H3_BINS, 1>(hist3, H3_BINS, k - above2, s_h, s_tmp, &s_bin, &s_above);
+    if (threadIdx.x == 0) {
+        const unsigned above3 = above2 + s_above;
+        st->thr = (st->prefix2 << H2_SHIFT) | s_bin;
+        st->above3 = above3;
+        st->need = k - above3;
     }
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_count(
-        TopkState* __restrict__ st, const float* __restrict__ slot_val,
+        const TopkState* __restrict__ st, const float* __restrict__ slot_val,
         const unsigned* __restrict__ tile_cnt, int ntiles, unsigned* __restrict__ tile_gt,
-        unsigned* __restrict__ tile_eq, unsigned* __restrict__ eq_before, unsigned* __restrict__ out_off) {
+        unsigned* __restrict__ tile_eq) {
     __shared__ unsigned s_red[8];
-    __shared__ unsigned s_tmp[4];
     const unsigned thr = st->thr;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
@@ -325,33 +396,38 @@ __global__ __launch_bounds__(TK_THREADS) void topk_count(
         }
         __syncthreads();
     }
-    if (last_block_done(&st->ticket[3])) {
-        const unsigned need = st->need;
-        const int per = (ntiles + TK_THREADS - 1) / TK_THREADS;
-        const int lo = min(ntiles, static_cast<int>(threadIdx.x) * per);
-        const int hi = min(ntiles, lo + per);
-        unsigned s_eq = 0;
-        for (int t = lo; t < hi; ++t) s_eq += atomic_load_u32(tile_eq + t);
-        unsigned total;
-        unsigned eqb = block_inclusive_scan_256(s_eq, s_tmp, &total) - s_eq;
-        unsigned s_sel = 0;
-        for (int t = lo; t < hi; ++t) {
-            const unsigned e = atomic_load_u32(tile_eq + t);
-            const unsigned g = atomic_load_u32(tile_gt + t);
-            const unsigned take = need > eqb ? min(e, need - eqb) : 0u;
-            eq_before[t] = eqb;
-            eqb += e;
-            s_sel += g + take;
-        }
-        unsigned off = block_inclusive_scan_256(s_sel, s_tmp, &total) - s_sel;
-        for (int t = lo; t < hi; ++t) {
-            const unsigned e = atomic_load_u32(tile_eq + t);
-            const unsigned g = atomic_load_u32(tile_gt + t);
-            const unsigned eb = eq_before[t];
-            const unsigned take = need > eb ? min(e, need - eb) : 0u;
-            out_off[t] = off;
-            off += g + take;
-        }
+}
+
+constexpr int SCAN_THREADS = 1024;
+
+__global__ __launch_bounds__(SCAN_THREADS) void topk_scan(
+        const TopkState* __restrict__ st, const unsigned* __restrict__ tile_gt,
+        const unsigned* __restrict__ tile_eq, int ntiles, unsigned* __restrict__ eq_before,
+        unsigned* __restrict__ out_off) {
+    __shared__ unsigned s_tmp[SCAN_THREADS / 64];
+    const unsigned need = st->need;
+    const int per = (ntiles + SCAN_THREADS - 1) / SCAN_THREADS;
+    const int lo = min(ntiles, static_cast<int>(threadIdx.x) * per);
+    const int hi = min(ntiles, lo + per);
+    unsigned s_eq = 0;
+    for (int t = lo; t < hi; ++t) s_eq += tile_eq[t];
+    unsigned total;
+    unsigned eqb = block_inclusive_scan<SCAN_THREADS / 64>(s_eq, s_tmp, &total) - s_eq;
+    unsigned s_sel = 0;
+    for (int t = lo; t < hi; ++t) {
+        const unsigned e = tile_eq[t];
+        const unsigned take = need > eqb ? min(e, need - eqb) : 0u;
+        eq_before[t] = eqb;
+        eqb += e;
+        s_sel += tile_gt[t] + take;
+    }
+    unsigned off = block_inclusive_scan<SCAN_THREADS / 64>(s_sel, s_tmp, &total) - s_sel;
+    for (int t = lo; t < hi; ++t) {
+        const unsigned e = tile_eq[t];
+        const unsigned eb = eq_before[t];
+        const unsigned take = need > eb ? min(e, need - eb) : 0u;
+        out_off[t] = off;
+        off += tile_gt[t] + take;
     }
 }
 
@@ -530,32 +606,51 @@ int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, f
 
     {
         TimedLaunch tl("topk_init", s);
-        topk_init<<<1, 256, 0, s>>>(reinterpret_cast<unsigned*>(w), static_cast<int>(L.zero_bytes / 4));
+        topk_init<<<INIT_BLOCKS, 256, 0, s>>>(reinterpret_cast<uint4*>(w), static_cast<int>(L.zero_bytes / 16));
         if ((rc = check_launch("topk_init")) != GC_OK) return rc;
     }
     {
         TimedLaunch tl("topk_accum_hist", s);
         if (grad_dtype == GC_BF16)
-            topk_accum_hist<true><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, ku, hist1, st);
+            topk_accum_hist<true><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, hist1);
         else
-            topk_accum_hist<false><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, ku, hist1, st);
+            topk_accum_hist<false><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, hist1);
         if ((rc = check_launch("topk_accum_hist")) != GC_OK) return rc;
     }
     {
+        TimedLaunch tl("topk_select1", s);
+        topk_select1<<<1, TK_THREADS, 0, s>>>(hist1, ku, st);
+        if ((rc = check_launch("topk_select1")) != GC_OK) return rc;
+    }
+    {
         TimedLaunch tl("topk_capture", s);
-        topk_capture<<<ntiles, TK_THREADS, 0, s>>>(mem, d, ku, st, hist2, slot_idx, slot_val, tile_cnt);
+        topk_capture<<<ntiles, TK_THREADS, 0, s>>>(mem, d, st, hist2, slot_idx, slot_val, tile_cnt);
         if ((rc = check_launch("topk_capture")) != GC_OK) return rc;
     }
     {
+        TimedLaunch tl("topk_select2", s);
+        topk_select2<<<1, TK_THREADS, 0, s>>>(hist2, ku, st);
+        if ((rc = check_launch("topk_select2")) != GC_OK) return rc;
+    }
+    {
         TimedLaunch tl("topk_refine", s);
-        topk_refine<<<small_grid, TK_THREADS, 0, s>>>(ku, st, hist3, slot_val, tile_cnt, ntiles);
+        topk_refine<<<small_grid, TK_THREADS, 0, s>>>(st, hist3, slot_val, tile_cnt, ntiles);
         if ((rc = check_launch("topk_refine")) != GC_OK) return rc;
     }
     {
+        TimedLaunch tl("topk_select3", s);
+        topk_select3<<<1, TK_THREADS, 0, s>>>(hist3, ku, st);
+        if ((rc = check_launch("topk_select3")) != GC_OK) return rc;
+    }
+    {
         TimedLaunch tl("topk_count", s);
-        topk_count<<<small_grid, TK_THREADS, 0, s>>>(st, slot_val, tile_cnt, ntiles, tile_gt, tile_eq,
-                                                     eq_before, out_off);
+        topk_count<<<small_grid, TK_THREADS, 0, s>>>(st, slot_val, tile_cnt, ntiles, tile_gt, tile_eq);
         if ((rc = check_launch("topk_count")) != GC_OK) return rc;
+    }
+    {
+        TimedLaunch tl("topk_scan", s);
+        topk_scan<<<1, SCAN_THREADS, 0, s>>>(st, tile_gt, tile_eq, ntiles, eq_before, out_off);
+        if ((rc = check_launch("topk_scan")) != GC_OK) return rc;
     }
     {
         TimedLaunch tl("topk_emit", s);
