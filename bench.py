@@ -113,6 +113,27 @@ def psgd_bytes(shapes, ranks, sg):
     return sum((sg + 12) * n * m + 4 * r * (n + 2 * m) for (n, m), r in zip(shapes, ranks))
 
 
+def fused_split_elems(shapes):
+    """Entries of the matrices the one-pass kernel (psgd_pq) takes: rows of a
+    multiple of 4 and at most 4096 entries; the others take psgd_p + psgd_q."""
+    fused = sum(n * m for n, m in shapes if m % 4 == 0 and m <= 4096)
+    return fused, sum(n * m for n, m in shapes) - fused
+
+
+def psgd_kernel_bytes(shapes, ranks, sg):
+    """Algorithmic bytes of each PowerSGD kernel per step: the first pass reads
+    M's inputs (grad + memory) once, psgd_out reads them again and writes
+    memory and the decoded output."""
+    fused, split = fused_split_elems(shapes)
+    kb = {"psgd_out": psgd_bytes(shapes, ranks, sg)}
+    if fused:
+        kb["psgd_pq"] = (sg + 4) * fused
+    if split:
+        kb["psgd_p"] = (sg + 4) * split
+        kb["psgd_q"] = (sg + 4) * split
+    return kb
+
+
 class C5(Workload):
     name = "c5"
 
@@ -147,8 +168,7 @@ class C5(Workload):
         self.grad_bytes = 2 * total
         mat_elems = sum(n * m for n, m in shapes)
         self.kernel_bytes = {
-            "psgd_out": psgd_bytes(shapes, self.ps.ranks, 2),
-            "psgd_p": 6 * mat_elems, "psgd_q": 6 * mat_elems,
+            **psgd_kernel_bytes(shapes, self.ps.ranks, 2),
             "topk_accum_hist": 10 * emb_d, "topk_capture": 4 * emb_d,
             "topk_decode_set": 4 * emb_d + 8 * self.k,
             "norm_partial": 2 * total / 10.0,
@@ -189,7 +209,7 @@ class C2(Workload):
         self.grad_bytes = 4 * sum(sizes)
         self.alg_bytes = psgd_bytes(shapes, self.ps.ranks, 4)
         me = sum(sizes)
-        self.kernel_bytes = {"psgd_out": psgd_bytes(shapes, self.ps.ranks, 4), "psgd_p": 8 * me, "psgd_q": 8 * me}
+        self.kernel_bytes = psgd_kernel_bytes(shapes, self.ps.ranks, 4)
         self.description = gen.WORKLOADS["c2"].description + f" (rank {rank})"
         self.config = {"workload": "resnet18 gradient set", "params": me, "powersgd_rank": rank,
                        "grad_dtype": "f32", "memory_dtype": "f32"}
@@ -246,8 +266,7 @@ class C4(Workload):
         me = sum(sizes)
         self.grad_bytes = 4 * me
         self.alg_bytes = psgd_bytes(shapes, [4] * len(shapes), 4) + 4 * me / 10.0
-        self.kernel_bytes = {"psgd_out": psgd_bytes(shapes, [4] * len(shapes), 4), "psgd_p": 8 * me,
-                             "psgd_q": 8 * me, "norm_partial": 4 * me / 10.0}
+        self.kernel_bytes = {**psgd_kernel_bytes(shapes, [4] * len(shapes), 4), "norm_partial": 4 * me / 10.0}
         self.description = gen.WORKLOADS["c4"].description
         self.config = {"workload": "vgg19 gradient set", "params": me, "levels": "l_low=rank4, l_high=rank2",
                        "grad_dtype": "f32", "memory_dtype": "f32", "accordion_check_every": 10}

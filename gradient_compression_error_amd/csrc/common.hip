@@ -108,7 +108,7 @@ int gc_timing_read(double* total_ms, int64_t* launches) {
 const char* gc_kernel_names(void) {
     return "topk_init,topk_accum_hist,topk_select1,topk_capture,topk_select2,topk_refine,topk_select3,"
            "topk_count,topk_scan,topk_emit,topk_decode_set,topk_decode_add,"
-           "psgd_pq_w,psgd_pq_b,psgd_p,psgd_q,psgd_qreduce,psgd_out,"
+           "psgd_pq,psgd_p,psgd_q,psgd_qreduce,psgd_out,"
            "norm_partial,norm_final";
 }
 

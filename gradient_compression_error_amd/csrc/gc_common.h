@@ -86,6 +86,8 @@ constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141;
 constexpr int DPP_MIRROR = 0x140;
+constexpr int DPP_ROR4 = 0x124;        // row_ror:4 (rotate within a 16-lane row)
+constexpr int DPP_ROR8 = 0x128;        // row_ror:8
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) { return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v))); }

@@ -11,11 +11,12 @@
 // Q' = M^T P^ = (M^T P) T.  So the pass that forms M^T P does not wait for
 // the orthonormalisation:
 //
-//   psgd_pq_w/_b one pass over M: each row's P = M Q_in is finished by the
-//                team holding the row (one wave for m <= 1024, the 4-wave
-//                workgroup for m <= 4096), and the same registers add
-//                M[i,:]^T P[i,:] into per-column M^T P accumulators; one
-//                M^T P and one Gram (float64) partial per workgroup and matrix
+//   psgd_pq      one pass over M: a workgroup spanning a row (thread t owns
+//                columns 4t..4t+3) takes rows in groups, finishes each row's
+//                P = M Q_in with a DPP reduce-scatter plus one LDS exchange,
+//                and adds M[i,:]^T P[i,:] into per-thread M^T P accumulators;
+//                one M^T P and one Gram (float64) partial per workgroup and
+//                matrix.  Three classes by row length (<= 1024, 2048, 4096)
 //   psgd_p/psgd_q the same two products as separate passes, for the other
 //                shapes (m not a multiple of 4, or m > 4096)
 //   psgd_qreduce sums the partials in a fixed order, builds T from the summed
@@ -43,21 +44,8 @@ constexpr int P_ROWS_WG = 16;        // rows per workgroup in psgd_p
 constexpr int Q_ROWS = 32;           // rows per chunk in psgd_q
 constexpr int ROW_GROUP = 8;         // rows whose loads are issued together in psgd_q / psgd_out
 constexpr int QR_COLS = 64;          // columns per workgroup in psgd_qreduce
-#ifndef GC_PQW_NS
-#define GC_PQW_NS 2
-#endif
-#ifndef GC_PQW_MINB
-#define GC_PQW_MINB 2
-#endif
-#ifndef GC_PQ_BLOCKS_PER_CU
-#define GC_PQ_BLOCKS_PER_CU 2
-#endif
-#ifndef GC_OUT_BLOCKS_PER_CU
-#define GC_OUT_BLOCKS_PER_CU 8
-#endif
 constexpr int CUS = 256;             // MI355X compute units
-constexpr int PQ_GRID_MAX = CUS * GC_PQ_BLOCKS_PER_CU;
-constexpr int OUT_GRID_MAX = CUS * GC_OUT_BLOCKS_PER_CU;
+constexpr int OUT_GRID_MAX = CUS * 8;
 
 struct PsMat {
     const void* grad;
@@ -75,17 +63,21 @@ struct PsMat {
     int pad;
 };
 
-// Matrix table of one launch group: wave-team shapes, workgroup-team shapes,
-// then the split-path shapes.
+// Fused-pass classes by row length: m <= 1024, m <= 2048, m <= 4096 (m % 4 == 0),
+// each with its own workgroup width; the rest take the split path.
+constexpr int PQ_CLASSES = 3;
+constexpr int SPLIT_CLASS = PQ_CLASSES;
+
+// Matrix table of one launch group, matrices sorted by class.
 struct PsBatch {
     int count;
-    int nwave;          // matrices [0, nwave): psgd_pq_w (m <= 1024)
-    int nfused;         // matrices [nwave, nfused): psgd_pq_b (m <= 4096); the rest: split path
     float eta;
-    long long ew, eb;   // entries of the psgd_pq_w / psgd_pq_b matrices
-    long long eall;     // entries of all matrices
-    int gw, gb;         // psgd_pq_w / psgd_pq_b grids
-    int gout;           // psgd_out grid
+    int cbeg[PQ_CLASSES + 2];      // matrices [cbeg[c], cbeg[c+1]) are of class c
+    int cgrid[PQ_CLASSES];         // psgd_pq grid of each fused class
+    long long cbase[PQ_CLASSES];   // first entry of each fused class
+    long long cent[PQ_CLASSES];    // entries of each fused class
+    long long eall;                // entries of all matrices
+    int gout;                      // psgd_out grid
     int pad;
     int begin_p[PS_MAXB];   // split path: first workgroup of each matrix in psgd_p / psgd_q
     int begin_q[PS_MAXB];
@@ -321,8 +313,8 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_q(const PsBatch B, int i0, in
 
 // ------------------------------------------------------------------ psgd_pq
 
-// Raw (unconverted) data of one float4 chunk of a row; converted to M at use,
-// so that loads issued rows ahead do not force a wait.
+// Raw (unconverted) data of one float4 chunk of a row; converted to M only
+// when the row is used, so that the loads of the next rows can be in flight.
 template <bool BF16>
 struct RawChunk;
 template <>
@@ -335,72 +327,6 @@ struct RawChunk<false> {
     float4 m;
     float4 g;
 };
-
-// Raw data of row `row`, chunks c0 + s*cstride clamped to the last chunk
-// (a clamped chunk repeats a valid one; its q is zero, so it adds nothing).
-// The row pointers are uniform, the chunk offsets 32-bit.
-// Buffer-resource view of rows [r0, r1) of a matrix's memory and gradient.
-// Loads address them with a 32-bit per-lane column offset (loop invariant)
-// and a scalar row offset; reads past r1 return zero and touch no memory.
-constexpr int BUF_WORD3 = 0x00020000;
-
-template <bool BF16>
-struct RowView {
-    __amdgpu_buffer_rsrc_t mem, grad;
-};
-
-template <bool BF16>
-__device__ __forceinline__ RowView<BF16> row_view(const PsMat& M, int r0, int r1) {
-    RowView<BF16> v;
-    const long long e0 = static_cast<long long>(r0) * M.m;
-    const int nrec = (r1 - r0) * M.m;
-    v.mem = __builtin_amdgcn_make_buffer_rsrc(M.mem + e0, 0, nrec * 4, BUF_WORD3);
-    if constexpr (BF16)
-        v.grad = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(static_cast<const unsigned short*>(M.grad)) + e0,
-                                                   0, nrec * 2, BUF_WORD3);
-    else
-        v.grad = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(static_cast<const float*>(M.grad)) + e0, 0,
-                                                   nrec * 4, BUF_WORD3);
-    return v;
-}
-
-// Raw data of row `k` of the view (k may run past its end: zeros), chunks
-// c0 + s*cstride (chunks past the row end alias the next row; their q is zero).
-template <bool BF16, int S>
-__device__ __forceinline__ void load_view_row(const RowView<BF16>& V, int k, int m, int c0, int cstride,
-                                              RawChunk<BF16> (&v)[S]) {
-    const int so_m = k * m * 4;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int c = c0 + s * cstride;
-        v[s].m = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(V.mem, c * 16, so_m, 0));
-        if constexpr (BF16) {
-            v[s].g = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(V.grad, c * 8, k * m * 2, 0));
-        } else {
-            v[s].g = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(V.grad, c * 16, so_m, 0));
-        }
-    }
-    // keep each row's loads together and in program order, so the waits for a
-    // row never cover a later row
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-template <bool BF16, int S>
-__device__ __forceinline__ void load_raw_row(const PsMat& M, int row, int c0, int cstride, int c4,
-                                             RawChunk<BF16> (&v)[S]) {
-    const long long e0 = static_cast<long long>(row) * M.m;
-    const float4* mrow = reinterpret_cast<const float4*>(M.mem + e0);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int c = min(c0 + s * cstride, c4 - 1);
-        v[s].m = mrow[c];
-        if constexpr (BF16) v[s].g = reinterpret_cast<const uint2*>(static_cast<const unsigned short*>(M.grad) + e0)[c];
-        else v[s].g = reinterpret_cast<const float4*>(static_cast<const float*>(M.grad) + e0)[c];
-    }
-    // keep each row's loads together and in program order, so the waits for a
-    // row never cover a later row
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 template <bool BF16>
 __device__ __forceinline__ float4 raw_to_M(const RawChunk<BF16>& r, float eta) {
@@ -415,254 +341,191 @@ __device__ __forceinline__ float4 raw_to_M(const RawChunk<BF16>& r, float eta) {
                        ef_acc(r.m.w, eta, g.w));
 }
 
-template <int S>
-__device__ __forceinline__ void load_q(const PsMat& M, int c0, int cstride, int c4, float (&q)[S][4][4]) {
+// Buffer resources over rows [r0, r1) of a matrix.  The whole byte offset of
+// a load goes into the vector operand, which the hardware checks against the
+// record count: rows past r1, and lanes given an offset of 2^31 or more, read
+// zeros without touching memory.
+constexpr int BUF_WORD3 = 0x00020000;
+constexpr unsigned OOB_OFFSET = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, long long e0, int elem_bytes,
+                                                            long long nelem) {
+    char* p = const_cast<char*>(static_cast<const char*>(base)) + e0 * elem_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, static_cast<int>(nelem * elem_bytes), BUF_WORD3);
+}
+
+// One reduce-scatter step across lane pairs: each lane reads its partner's
+// registers through the DPP control CTRL.  Lanes whose BIT is clear keep the
+// first half of x, the others the second half; a kept entry gains the
+// partner's copy of it.  Partners must hold the same entries of x.
+template <int CTRL, int BIT, int N>
+__device__ __forceinline__ void scatter_step(const float (&x)[N], float (&y)[N / 2], int lane) {
+    const bool hi = (lane & BIT) != 0;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int c = c0 + s * cstride;
+    for (int i = 0; i < N / 2; ++i) {
+        const float send = hi ? x[i] : x[i + N / 2];
+        const float keep = hi ? x[i + N / 2] : x[i];
+        y[i] = keep + dpp_f32<CTRL>(send);
+    }
+}
+
+__device__ __forceinline__ int rev4(int x) {
+    return ((x & 1) << 3) | ((x & 2) << 1) | ((x & 4) >> 1) | ((x & 8) >> 3);
+}
+
+// Rows [r0, r1) of one matrix, RG rows at a time, by a workgroup of NT
+// threads that spans a row: thread t owns float4 chunk t (columns 4t..4t+3),
+// so Q_in and the M^T P accumulators of its columns stay in registers.
+//   1. the RG rows' raw data (loaded one group ahead) become M;
+//   2. each thread forms its share of the RG x 4 dot products M[i,:] Q_in;
+//   3. a DPP reduce-scatter over each 16-lane row leaves V/16 of the V = 4 RG
+//      sums per lane; the 4 NT/64 row partials go to LDS (double-buffered,
+//      one barrier per group);
+//   4. every wave sums the partials of each value in a fixed order (its lanes
+//      split the partials, then two lane-exchange adds) and reads the V
+//      finished P entries into scalars;
+//   5. M^T P accumulators += M[i, cols] P[i, :]; wave 0 stores the P rows and
+//      accumulates the Gram matrix (float64).
+// The accumulators and Gram entries of the workgroup are partial `part`.
+template <bool BF16, int NT, int RG>
+__device__ __forceinline__ void pq_rows(const PsMat& M, float eta, int r0, int r1, int part,
+                                        float (*s_part)[NT / 16][4 * RG], int& par) {
+    constexpr int V = 4 * RG;          // P entries per row group
+    constexpr int NP = NT / 16;        // partials per entry (16-lane rows of the workgroup)
+    constexpr int L = 64 / V;          // lanes sharing the sum of one entry
+    static_assert(V == 16 || V == 32, "row group of 4 or 8 rows");
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int m = M.m, c4 = m / 4, nr = r1 - r0;
+    const bool act = t < c4;
+
+    float q[4][4], qt[4][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c < c4 && j < M.rank) t = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * M.m)[c];
-            q[s][0][j] = t.x; q[s][1][j] = t.y; q[s][2][j] = t.z; q[s][3][j] = t.w;
+    for (int j = 0; j < 4; ++j) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (act && j < M.rank) v = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m)[t];
+        q[0][j] = v.x; q[1][j] = v.y; q[2][j] = v.z; q[3][j] = v.w;
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qt[cc][j] = 0.0f;
+
+    const long long e0 = static_cast<long long>(r0) * m, ne = static_cast<long long>(nr) * m;
+    const __amdgpu_buffer_rsrc_t rm = rows_rsrc(M.mem, e0, 4, ne);
+    const __amdgpu_buffer_rsrc_t rg = rows_rsrc(M.grad, e0, BF16 ? 2 : 4, ne);
+    const unsigned colm = act ? static_cast<unsigned>(t) * 16u : OOB_OFFSET;
+    const unsigned colg = act ? static_cast<unsigned>(t) * (BF16 ? 8u : 16u) : OOB_OFFSET;
+    const unsigned rowm = static_cast<unsigned>(m) * 4u, rowg = static_cast<unsigned>(m) * (BF16 ? 2u : 4u);
+
+    RawChunk<BF16> raw[RG];
+    auto load_group = [&](int k) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const unsigned kr = static_cast<unsigned>(k + r);
+            raw[r].m = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, colm + kr * rowm, 0, 0));
+            if constexpr (BF16)
+                raw[r].g = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, colg + kr * rowg, 0, 0));
+            else
+                raw[r].g = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, colg + kr * rowg, 0, 0));
         }
-    }
-}
+    };
 
-template <int S>
-__device__ __forceinline__ void partial_p(const float4 (&v)[S], const float (&q)[S][4][4], float (&pp)[4]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pp[j] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const float vv[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pp[j] = fmaf(vv[cc], q[s][cc][j], pp[j]);
-    }
-}
-
-template <int S>
-__device__ __forceinline__ void add_mtp(const float4 (&v)[S], const float (&p)[4], float (&qt)[S][4][4]) {
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const float vv[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) qt[s][cc][j] = fmaf(vv[cc], p[j], qt[s][cc][j]);
-    }
-}
-
-__device__ __forceinline__ double gram_term(const float (&p)[4], int ga, int gb) {
-    float pa = p[0], pb = p[0];
-#pragma unroll
-    for (int j = 1; j < 4; ++j) {
-        pa = (ga == j) ? p[j] : pa;
-        pb = (gb == j) ? p[j] : pb;
-    }
-    return static_cast<double>(pa) * static_cast<double>(pb);
-}
-
-constexpr int PQ_SW = 4;   // float4 chunks per lane, wave team (m <= 1024)
-constexpr int PQ_SB = 4;   // float4 chunks per thread, workgroup team (m <= 4096)
-constexpr int PQ_WAVE_MAX_M = 64 * 4 * PQ_SW;
-constexpr int PQ_BLOCK_MAX_M = PS_THREADS * 4 * PQ_SB;
-
-// Wave team: the workgroup's rows [r0, r1) are split into four contiguous
-// runs, one per wave; lane l owns float4 chunks l, l+64, ...; P of a row is a
-// DPP wave sum (no barrier).  NS raw slots form a ring: a step converts its
-// slot's row to M (waiting only for that row) and refills the slot with the
-// row NS ahead before the arithmetic.  The four waves' M^T P accumulators are
-// combined in LDS in wave order and written as partial `part`.
-template <bool BF16>
-__device__ __forceinline__ void pq_wave_team(const PsMat& M, float eta, int r0, int r1, int part, float4* s_qt,
-                                             double (*s_g)[16]) {
-    constexpr int S = PQ_SW;
-    constexpr int NS = GC_PQW_NS;
-    const int m = M.m, c4 = m / 4;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int R = r1 - r0;
-    const int rbeg = r0 + (w * R) / 4;
-    const int rend = r0 + ((w + 1) * R) / 4;
-    float q[S][4][4], qt[S][4][4];
-    load_q<S>(M, lane, 64, c4, q);
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) qt[s][cc][j] = 0.0f;
+    const int li = lane & 15, lr = lane >> 4;
+    const int vi = lane % V, lg = lane / V;
     const int ga = (lane >> 2) & 3, gb = lane & 3;
     double g = 0.0;
-    if (rbeg < rend) {
-        const RowView<BF16> V = row_view<BF16>(M, rbeg, rend);
-        const int nr = rend - rbeg;
-        RawChunk<BF16> ring[NS][S];
+    load_group(0);
+    for (int k = 0; k < nr; k += RG) {
+        float v[RG][4];
 #pragma unroll
-        for (int k = 0; k < NS; ++k) load_view_row<BF16, S>(V, k, m, lane, 64, ring[k]);
-        auto step = [&](RawChunk<BF16> (&slot)[S], int k) {
-            float4 v[S];
-#pragma unroll
-            for (int s = 0; s < S; ++s) v[s] = raw_to_M<BF16>(slot[s], eta);
-            load_view_row<BF16, S>(V, k + NS, m, lane, 64, slot);
-            float pp[4], p[4];
-            partial_p<S>(v, q, pp);
-            const bool valid = k < nr;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p[j] = valid ? wave_sum(pp[j]) : 0.0f;
-            add_mtp<S>(v, p, qt);
-            if (valid) {
-                if (lane == 0) reinterpret_cast<float4*>(M.praw)[rbeg + k] = make_float4(p[0], p[1], p[2], p[3]);
-                g += gram_term(p, ga, gb);
-            }
-        };
-        for (int k = 0; k < nr; k += NS) {
-#pragma unroll
-            for (int t = 0; t < NS; ++t) step(ring[t], k + t);
+        for (int r = 0; r < RG; ++r) {
+            const float4 x = raw_to_M<BF16>(raw[r], eta);
+            v[r][0] = x.x; v[r][1] = x.y; v[r][2] = x.z; v[r][3] = x.w;
         }
-    }
-    for (int ww = 0; ww < 4; ++ww) {
-        if (w == ww) {
+        load_group(k + RG);
+        float x32[V];
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
-                const int c = lane + 64 * s;
-                if (c < c4) {
+        for (int r = 0; r < RG; ++r)
 #pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) {
-                        float4 t = make_float4(qt[s][cc][0], qt[s][cc][1], qt[s][cc][2], qt[s][cc][3]);
-                        if (ww > 0) {
-                            const float4 o = s_qt[4 * c + cc];
-                            t = make_float4(o.x + t.x, o.y + t.y, o.z + t.z, o.w + t.w);
-                        }
-                        s_qt[4 * c + cc] = t;
+            for (int j = 0; j < 4; ++j) {
+                float a = v[r][0] * q[0][j];
+                a = fmaf(v[r][1], q[1][j], a);
+                a = fmaf(v[r][2], q[2][j], a);
+                x32[4 * r + j] = fmaf(v[r][3], q[3][j], a);
+            }
+        float x16[V / 2], x8[V / 4], x4[V / 8], x2[V / 16];
+        scatter_step<DPP_XOR1, 1>(x32, x16, lane);
+        scatter_step<DPP_XOR2, 2>(x16, x8, lane);
+        scatter_step<DPP_ROR4, 4>(x8, x4, lane);
+        scatter_step<DPP_ROR8, 8>(x4, x2, lane);
+        // lane li of a 16-lane row now holds entries (V/16) rev4(li) + i
+        float* dst = &s_part[par][w * 4 + lr][(V / 16) * rev4(li)];
+#pragma unroll
+        for (int i = 0; i < V / 16; ++i) dst[i] = x2[i];
+        __syncthreads();
+        float pv = 0.0f;
+#pragma unroll
+        for (int u = 0; u < NP / L; ++u) pv += s_part[par][lg * (NP / L) + u][vi];
+        if constexpr (L == 4) pv += __shfl_xor(pv, 16, WAVE);
+        pv += __shfl_xor(pv, 32, WAVE);
+        par ^= 1;
+        float p[RG][4];
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[r][j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pv), 4 * r + j));
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) qt[cc][j] = fmaf(v[r][cc], p[r][j], qt[cc][j]);
+        if (w == 0) {
+            // rows past r1 read as zero: their P entries and Gram terms are zero
+            if (lane < V && k + vi / 4 < nr) M.praw[static_cast<long long>(r0 + k) * 4 + vi] = pv;
+            if (lane < 16) {
+#pragma unroll
+                for (int r = 0; r < RG; ++r) {
+                    float pa = p[r][0], pb = p[r][0];
+#pragma unroll
+                    for (int j = 1; j < 4; ++j) {
+                        pa = (ga == j) ? p[r][j] : pa;
+                        pb = (gb == j) ? p[r][j] : pb;
                     }
+                    g = fma(static_cast<double>(pa), static_cast<double>(pb), g);
                 }
             }
         }
-        __syncthreads();
     }
-    float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(part) * m;
-    for (int e = threadIdx.x; e < m; e += PS_THREADS) dst[e] = s_qt[e];
-    if (lane < 16) s_g[w][lane] = g;
-    __syncthreads();
-    if (threadIdx.x < 16) {
-        const int t = threadIdx.x;
-        M.gpart[static_cast<long long>(part) * 16 + t] = ((s_g[0][t] + s_g[1][t]) + s_g[2][t]) + s_g[3][t];
+    if (act) {
+        float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(part) * m + 4 * t;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) dst[cc] = make_float4(qt[cc][0], qt[cc][1], qt[cc][2], qt[cc][3]);
     }
+    if (w == 0 && lane < 16) M.gpart[static_cast<long long>(part) * 16 + lane] = g;
 }
 
-// Workgroup team: all four waves share each row of [r0, r1), thread t owns
-// float4 chunks t, t+256, ...; P of a row = wave sums combined through LDS
-// (double-buffered, one barrier per row).
-template <bool BF16>
-__device__ __forceinline__ void pq_block_team(const PsMat& M, float eta, int r0, int r1, int part,
-                                              float (*s_p)[4][4]) {
-    constexpr int S = PQ_SB;
-    const int m = M.m, c4 = m / 4;
-    const int t = threadIdx.x, w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
-    const int rbeg = r0, rend = r1;
-    float q[S][4][4], qt[S][4][4];
-    load_q<S>(M, t, PS_THREADS, c4, q);
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) qt[s][cc][j] = 0.0f;
-    const int ga = (lane >> 2) & 3, gb = lane & 3;
-    double g = 0.0;
-    constexpr int NS = BF16 ? 2 : 2;
-    {
-        RawChunk<BF16> ra[S], rb[S];
-        load_raw_row<BF16, S>(M, rbeg, t, PS_THREADS, c4, ra);
-        if constexpr (NS == 2) load_raw_row<BF16, S>(M, min(rbeg + 1, rend - 1), t, PS_THREADS, c4, rb);
-        auto step = [&](RawChunk<BF16> (&slot)[S], int i, int par) {
-            float4 v[S];
-#pragma unroll
-            for (int s = 0; s < S; ++s) v[s] = raw_to_M<BF16>(slot[s], eta);
-            load_raw_row<BF16, S>(M, min(i + NS, rend - 1), t, PS_THREADS, c4, slot);
-            float pp[4], p[4];
-            partial_p<S>(v, q, pp);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pp[j] = wave_sum(pp[j]);
-            if (lane == 0) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s_p[par][w][j] = pp[j];
-            }
-            __syncthreads();
-            const bool valid = i < rend;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                p[j] = valid ? ((s_p[par][0][j] + s_p[par][1][j]) + s_p[par][2][j]) + s_p[par][3][j] : 0.0f;
-            add_mtp<S>(v, p, qt);
-            if (valid) {
-                if (t == 0) reinterpret_cast<float4*>(M.praw)[i] = make_float4(p[0], p[1], p[2], p[3]);
-                g += gram_term(p, ga, gb);
-            }
-        };
-        if constexpr (NS == 2) {
-            for (int i = rbeg; i < rend; i += 2) {
-                step(ra, i, 0);
-                step(rb, i + 1, 1);
-            }
-        } else {
-            for (int i = rbeg; i < rend; i += 2) {
-                step(ra, i, 0);
-                step(ra, i + 1, 1);
-            }
-        }
-    }
-    float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(part) * m;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int c = t + PS_THREADS * s;
-        if (c < c4) {
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc)
-                dst[4 * c + cc] = make_float4(qt[s][cc][0], qt[s][cc][1], qt[s][cc][2], qt[s][cc][3]);
-        }
-    }
-    if (t < 16) M.gpart[static_cast<long long>(part) * 16 + t] = g;
-}
+// Waves per SIMD the fused pass is compiled for (bounds its registers).
+template <int NT>
+constexpr int pq_min_waves() { return NT == 256 ? 3 : NT == 512 ? 4 : 4; }
 
-// One pass over the wave-team matrices (m % 4 == 0, m <= 1024): workgroup b
-// takes its balanced share of their rows, matrix by matrix.
-template <bool BF16>
-__global__ __launch_bounds__(PS_THREADS, GC_PQW_MINB) void psgd_pq_w(const PsBatch B) {
-    __shared__ float4 s_qt[PQ_WAVE_MAX_M];
-    __shared__ double s_g[4][16];
-    const int b = blockIdx.x, G = B.gw;
-    const long long E = B.ew;
-    const long long s_lo = share_lo(E, G, b), s_hi = share_lo(E, G, b + 1);
-    for (int i = mat_of_entry(B, B.nwave, s_lo); i < B.nwave; ++i) {
-        const PsMat& M = B.mat[i];
-        if (M.off >= s_hi) break;
-        int r0, r1;
-        rows_in_share(M, s_lo, s_hi, r0, r1);
-        if (r0 >= r1) continue;
-        pq_wave_team<BF16>(M, B.eta, r0, r1, b - owner_of(M.off, E, G), s_qt, s_g);
-        __syncthreads();
-    }
-}
-
-// One pass over the workgroup-team matrices (m % 4 == 0, 1024 < m <= 4096),
-// whose entries start at B.ew in the table.
-template <bool BF16>
-__global__ __launch_bounds__(PS_THREADS, 2) void psgd_pq_b(const PsBatch B) {
-    __shared__ float s_p[2][4][4];
-    const int b = blockIdx.x, G = B.gb;
-    const long long E = B.eb, base = B.ew;
+// One pass over the matrices of fused class CLS (m % 4 == 0, m <= 4 NT):
+// workgroup b takes its balanced share of their rows, matrix by matrix.
+template <bool BF16, int NT, int RG>
+__global__ __launch_bounds__(NT, pq_min_waves<NT>()) void psgd_pq(const PsBatch B, int cls) {
+    __shared__ float s_part[2][NT / 16][4 * RG];
+    const int b = blockIdx.x, G = B.cgrid[cls];
+    const int i0 = B.cbeg[cls], i1 = B.cbeg[cls + 1];
+    const long long E = B.cent[cls], base = B.cbase[cls];
     const long long s_lo = base + share_lo(E, G, b), s_hi = base + share_lo(E, G, b + 1);
-    for (int i = B.nwave + mat_of_entry_from(B, B.nwave, B.nfused, s_lo); i < B.nfused; ++i) {
+    int par = 0;
+    for (int i = i0 + mat_of_entry_from(B, i0, i1, s_lo); i < i1; ++i) {
         const PsMat& M = B.mat[i];
         if (M.off >= s_hi) break;
         int r0, r1;
         rows_in_share(M, s_lo, s_hi, r0, r1);
         if (r0 >= r1) continue;
-        pq_block_team<BF16>(M, B.eta, r0, r1, b - owner_of(M.off - base, E, G), s_p);
-        __syncthreads();
+        pq_rows<BF16, NT, RG>(M, B.eta, r0, r1, b - owner_of(M.off - base, E, G), s_part, par);
     }
 }
 
@@ -885,10 +748,15 @@ int nstrips_host(int m) {
     return (m + w - 1) / w;
 }
 
-// 0: wave-team fused pass, 1: workgroup-team fused pass, 2: split path
+// Fused-pass class of a row length (SPLIT_CLASS: the split path)
+struct PqClass { int max_m, threads, blocks_per_cu; };
+constexpr PqClass PQ_CLASS[PQ_CLASSES] = {{1024, 256, 3}, {2048, 512, 2}, {4096, 1024, 1}};
+
 int shape_class(int m) {
-    if (m % 4 != 0 || m > PQ_BLOCK_MAX_M) return 2;
-    return m <= PQ_WAVE_MAX_M ? 0 : 1;
+    if (m % 4 != 0) return SPLIT_CLASS;
+    for (int c = 0; c < PQ_CLASSES; ++c)
+        if (m <= PQ_CLASS[c].max_m) return c;
+    return SPLIT_CLASS;
 }
 
 // How the matrices are grouped and partitioned.  Shapes only (not ranks, not
@@ -900,9 +768,12 @@ struct PlanMat {
     size_t ws_off;      // workspace offset of this matrix's scratch
 };
 struct PlanBatch {
-    int first, count, nwave, nfused;   // into Plan::mats
-    long long ew, eb, eall;
-    int gw, gb, gout;
+    int first, count;                  // into Plan::mats
+    int cbeg[PQ_CLASSES + 2];
+    int cgrid[PQ_CLASSES];
+    long long cbase[PQ_CLASSES], cent[PQ_CLASSES];
+    long long eall;
+    int gout;
 };
 struct Plan {
     std::vector<PlanMat> mats;
@@ -931,16 +802,24 @@ Plan make_plan(const gc_mat* mats, int nmats) {
         PlanBatch pb{};
         pb.first = static_cast<int>(P.mats.size());
         pb.count = j - i;
-        int mw = 1, mb = 1;
+        int ccount[PQ_CLASSES + 1] = {0, 0, 0, 0};
+        int cmax[PQ_CLASSES] = {1, 1, 1};
         for (int a : idx) {
-            const long long e = static_cast<long long>(mats[a].n) * mats[a].m;
             const int c = shape_class(mats[a].m);
-            if (c == 0) { ++pb.nwave; pb.ew += e; mw = std::max(mw, mats[a].m); }
-            if (c == 1) { pb.eb += e; mb = std::max(mb, mats[a].m); }
-            if (c < 2) ++pb.nfused;
+            ++ccount[c];
+            if (c < PQ_CLASSES) {
+                pb.cent[c] += static_cast<long long>(mats[a].n) * mats[a].m;
+                cmax[c] = std::max(cmax[c], mats[a].m);
+            }
         }
-        pb.gw = balanced_grid(pb.ew, mw, PQ_GRID_MAX);
-        pb.gb = balanced_grid(pb.eb, mb, PQ_GRID_MAX);
+        pb.cbeg[0] = 0;
+        for (int c = 0; c <= PQ_CLASSES; ++c) pb.cbeg[c + 1] = pb.cbeg[c] + ccount[c];
+        long long base = 0;
+        for (int c = 0; c < PQ_CLASSES; ++c) {
+            pb.cbase[c] = base;
+            base += pb.cent[c];
+            pb.cgrid[c] = balanced_grid(pb.cent[c], cmax[c], CUS * PQ_CLASS[c].blocks_per_cu);
+        }
         long long eall = 0;
         for (int a : idx) {
             PlanMat pm{};
@@ -948,13 +827,10 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             pm.off = eall;
             const int n = mats[a].n, m = mats[a].m;
             const int c = shape_class(m);
-            if (c < 2) {
-                const long long base = c == 0 ? 0 : pb.ew;
-                const long long E = c == 0 ? pb.ew : pb.eb;
-                const int G = c == 0 ? pb.gw : pb.gb;
-                const int first = owner_of(pm.off - base, E, G);
-                const int last = owner_of(pm.off - base + static_cast<long long>(n - 1) * m, E, G);
-                pm.nq = pm.ng = last - first + 1;
+            if (c < PQ_CLASSES) {
+                const long long E = pb.cent[c], rel = pm.off - pb.cbase[c];
+                const int G = pb.cgrid[c];
+                pm.nq = pm.ng = owner_of(rel + static_cast<long long>(n - 1) * m, E, G) - owner_of(rel, E, G) + 1;
             } else {
                 pm.nq = (n + Q_ROWS - 1) / Q_ROWS;
                 pm.ng = (n + P_ROWS_WG - 1) / P_ROWS_WG;
@@ -998,7 +874,7 @@ int validate_mat(const gc_mat& a, int i, int dtype) {
     return GC_OK;
 }
 
-// Launches all kernels of one batch (fused-shape entries first).
+// Launches all kernels of one batch (fused classes first, then the split path).
 template <bool BF16>
 int run_batch(PsBatch& B, hipStream_t s) {
     int rc;
@@ -1007,31 +883,30 @@ int run_batch(PsBatch& B, hipStream_t s) {
         B.begin_r[i] = nr;
         nr += (B.mat[i].m + QR_COLS - 1) / QR_COLS;
     }
-    if (B.nwave > 0) {
-        TimedLaunch tl("psgd_pq_w", s);
-        psgd_pq_w<BF16><<<B.gw, PS_THREADS, 0, s>>>(B);
-        if ((rc = check_launch("psgd_pq_w")) != GC_OK) return rc;
+    for (int c = 0; c < PQ_CLASSES; ++c) {
+        if (B.cbeg[c + 1] == B.cbeg[c]) continue;
+        TimedLaunch tl("psgd_pq", s);
+        if (c == 0) psgd_pq<BF16, 256, 8><<<B.cgrid[c], 256, 0, s>>>(B, c);
+        else if (c == 1) psgd_pq<BF16, 512, 4><<<B.cgrid[c], 512, 0, s>>>(B, c);
+        else psgd_pq<BF16, 1024, 4><<<B.cgrid[c], 1024, 0, s>>>(B, c);
+        if ((rc = check_launch("psgd_pq")) != GC_OK) return rc;
     }
-    if (B.nfused > B.nwave) {
-        TimedLaunch tl("psgd_pq_b", s);
-        psgd_pq_b<BF16><<<B.gb, PS_THREADS, 0, s>>>(B);
-        if ((rc = check_launch("psgd_pq_b")) != GC_OK) return rc;
-    }
-    if (B.nfused < B.count) {
+    const int s0 = B.cbeg[SPLIT_CLASS];
+    if (s0 < B.count) {
         int np = 0, nq = 0;
-        for (int i = B.nfused; i < B.count; ++i) {
+        for (int i = s0; i < B.count; ++i) {
             const PsMat& M = B.mat[i];
             B.begin_p[i] = np; np += (M.n + P_ROWS_WG - 1) / P_ROWS_WG;
             B.begin_q[i] = nq; nq += nstrips_host(M.m) * ((M.n + Q_ROWS - 1) / Q_ROWS);
         }
         {
             TimedLaunch tl("psgd_p", s);
-            psgd_p<BF16><<<np, PS_THREADS, 0, s>>>(B, B.nfused, B.count);
+            psgd_p<BF16><<<np, PS_THREADS, 0, s>>>(B, s0, B.count);
             if ((rc = check_launch("psgd_p")) != GC_OK) return rc;
         }
         {
             TimedLaunch tl("psgd_q", s);
-            psgd_q<BF16><<<nq, PS_THREADS, 0, s>>>(B, B.nfused, B.count);
+            psgd_q<BF16><<<nq, PS_THREADS, 0, s>>>(B, s0, B.count);
             if ((rc = check_launch("psgd_q")) != GC_OK) return rc;
         }
     }
@@ -1084,14 +959,14 @@ int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta
     for (const PlanBatch& pb : P.batches) {
         PsBatch B{};
         B.count = pb.count;
-        B.nwave = pb.nwave;
-        B.nfused = pb.nfused;
         B.eta = eta;
-        B.ew = pb.ew;
-        B.eb = pb.eb;
+        for (int c = 0; c < PQ_CLASSES + 2; ++c) B.cbeg[c] = pb.cbeg[c];
+        for (int c = 0; c < PQ_CLASSES; ++c) {
+            B.cgrid[c] = pb.cgrid[c];
+            B.cbase[c] = pb.cbase[c];
+            B.cent[c] = pb.cent[c];
+        }
         B.eall = pb.eall;
-        B.gw = pb.gw;
-        B.gb = pb.gb;
         B.gout = pb.gout;
         for (int k = 0; k < pb.count; ++k) {
             const PlanMat& pm = P.mats[pb.first + k];
