@@ -38,14 +38,14 @@ namespace gc {
 namespace {
 
 constexpr int PS_THREADS = 256;
-constexpr int PS_MAXB = 28;          // matrices per launch (kernel-argument table)
+constexpr int PS_MAXB = 4096;        // matrices per launch group
 constexpr int P_ROWS_WAVE = 4;       // rows per wave in psgd_p
 constexpr int P_ROWS_WG = 16;        // rows per workgroup in psgd_p
 constexpr int Q_ROWS = 32;           // rows per chunk in psgd_q
 constexpr int ROW_GROUP = 8;         // rows whose loads are issued together in psgd_q / psgd_out
-constexpr int QR_COLS = 64;          // columns per workgroup in psgd_qreduce
+constexpr int QR_PER_THREAD = 16;    // M^T P partials per psgd_qreduce thread before slicing a column
 constexpr int CUS = 256;             // MI355X compute units
-constexpr int OUT_GRID_MAX = CUS * 8;
+constexpr int OUT_GRID_MAX = CUS * 4;   // psgd_out holds 4 workgroups per CU
 
 struct PsMat {
     const void* grad;
@@ -60,16 +60,23 @@ struct PsMat {
     long long off;   // first entry of the matrix in the batch (matrices back to back)
     int n, m, rank;
     int nq, ng;      // number of M^T P / Gram partials
+    int begin_p;     // split path: first workgroup of the matrix in psgd_p
+    int begin_q;     // split path: first workgroup in psgd_q
+    int begin_r;     // first workgroup in psgd_qreduce
+    int qs;          // psgd_qreduce threads per column
     int pad;
 };
+static_assert(sizeof(PsMat) % 8 == 0, "table entries are copied as words");
 
 // Fused-pass classes by row length: m <= 1024, m <= 2048, m <= 4096 (m % 4 == 0),
 // each with its own workgroup width; the rest take the split path.
 constexpr int PQ_CLASSES = 3;
 constexpr int SPLIT_CLASS = PQ_CLASSES;
 
-// Matrix table of one launch group, matrices sorted by class.
+// Launch parameters of one launch group; the matrices (sorted by class) are
+// in a device table (in the workspace) copied there at the start of the step.
 struct PsBatch {
+    const PsMat* tbl;
     int count;
     float eta;
     int cbeg[PQ_CLASSES + 2];      // matrices [cbeg[c], cbeg[c+1]) are of class c
@@ -79,10 +86,6 @@ struct PsBatch {
     long long eall;                // entries of all matrices
     int gout;                      // psgd_out grid
     int pad;
-    int begin_p[PS_MAXB];   // split path: first workgroup of each matrix in psgd_p / psgd_q
-    int begin_q[PS_MAXB];
-    int begin_r[PS_MAXB];   // psgd_qreduce
-    PsMat mat[PS_MAXB];
 };
 static_assert(sizeof(PsBatch) <= 4096, "kernel argument table must fit 4 KB");
 
@@ -95,26 +98,54 @@ __host__ __device__ __forceinline__ int owner_of(long long s, long long e, int g
     return static_cast<int>((s * g) / e);
 }
 
-// Matrix holding entry s among entries [0, cnt) of the table (last i with off <= s).
-__device__ __forceinline__ int mat_of_entry(const PsBatch& B, int cnt, long long s) {
-    int lo = 0, hi = cnt;
+// The table is read through the constant address space: uniform indices give
+// scalar loads, and a matrix's fields are copied into scalar registers.
+typedef const __attribute__((address_space(4))) PsMat* MatTable;
+
+__device__ __forceinline__ MatTable mat_table(const PsBatch& B) { return (MatTable)(B.tbl); }
+
+__device__ __forceinline__ PsMat mat_at(const PsBatch& B, int i) {
+    typedef const __attribute__((address_space(4))) unsigned long long* WordTable;
+    const WordTable w = (WordTable)(B.tbl + i);
+    PsMat r;
+    unsigned long long* d = reinterpret_cast<unsigned long long*>(&r);
+#pragma unroll
+    for (int k = 0; k < static_cast<int>(sizeof(PsMat) / 8); ++k) d[k] = w[k];
+    return r;
+}
+
+// Last i in [i0, i1) whose first entry is <= s.
+__device__ __forceinline__ int mat_of_entry(const PsBatch& B, int i0, int i1, long long s) {
+    const MatTable T = mat_table(B);
+    int lo = i0, hi = i1;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (B.mat[mid].off <= s) lo = mid;
+        if (T[mid].off <= s) lo = mid;
         else hi = mid;
     }
     return lo;
 }
 
-// Same, among entries [i0, i1); returns the index relative to i0.
-__device__ __forceinline__ int mat_of_entry_from(const PsBatch& B, int i0, int i1, long long s) {
+enum BlockMap { MAP_P, MAP_Q, MAP_R };
+
+template <BlockMap K>
+__device__ __forceinline__ int first_block(MatTable T, int i) {
+    if constexpr (K == MAP_P) return T[i].begin_p;
+    else if constexpr (K == MAP_Q) return T[i].begin_q;
+    else return T[i].begin_r;
+}
+
+// Matrix of workgroup blk among matrices [i0, i1) (last i with first block <= blk).
+template <BlockMap K>
+__device__ __forceinline__ int mat_of_block(const PsBatch& B, int i0, int i1, int blk) {
+    const MatTable T = mat_table(B);
     int lo = i0, hi = i1;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (B.mat[mid].off <= s) lo = mid;
+        if (first_block<K>(T, mid) <= blk) lo = mid;
         else hi = mid;
     }
-    return lo - i0;
+    return lo;
 }
 
 // Rows of matrix M whose first entry lies in [s_lo, s_hi).
@@ -151,17 +182,6 @@ __device__ __forceinline__ void load_Mv(const PsMat& M, float eta, long long e, 
     } else {
         v[0] = load_M1<BF16>(M, eta, e);
     }
-}
-
-// Matrix of block `blk` among entries [i0, i1) of a launch table.
-__device__ __forceinline__ int find_in_range(const int* begin, int i0, int i1, int blk) {
-    int lo = i0, hi = i1;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (begin[mid] <= blk) lo = mid;
-        else hi = mid;
-    }
-    return lo;
 }
 
 // ------------------------------------------------------------------ psgd_p / psgd_q (split path)
@@ -212,9 +232,8 @@ __device__ __forceinline__ void p_rows(const PsMat& M, float eta, int row0, floa
 template <bool BF16>
 __global__ __launch_bounds__(PS_THREADS) void psgd_p(const PsBatch B, int i0, int i1) {
     __shared__ double s_g[4][16];
-    const int mi = find_in_range(B.begin_p, i0, i1, blockIdx.x);
-    const PsMat& M = B.mat[mi];
-    const int lwg = blockIdx.x - B.begin_p[mi];
+    const PsMat M = mat_at(B, mat_of_block<MAP_P>(B, i0, i1, blockIdx.x));
+    const int lwg = blockIdx.x - M.begin_p;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row0 = lwg * P_ROWS_WG + w * P_ROWS_WAVE;
     float acc[P_ROWS_WAVE][4];
@@ -300,9 +319,8 @@ __device__ __forceinline__ void q_chunk(const PsMat& M, float eta, int strip, in
 
 template <bool BF16>
 __global__ __launch_bounds__(PS_THREADS) void psgd_q(const PsBatch B, int i0, int i1) {
-    const int mi = find_in_range(B.begin_q, i0, i1, blockIdx.x);
-    const PsMat& M = B.mat[mi];
-    const int lwg = blockIdx.x - B.begin_q[mi];
+    const PsMat M = mat_at(B, mat_of_block<MAP_Q>(B, i0, i1, blockIdx.x));
+    const int lwg = blockIdx.x - M.begin_q;
     const int ns = nstrips_of(M.m);
     const int strip = lwg % ns, chunk = lwg / ns;
     if (M.m % 4 == 0)
@@ -519,8 +537,8 @@ __global__ __launch_bounds__(NT, pq_min_waves<NT>()) void psgd_pq(const PsBatch 
     const long long E = B.cent[cls], base = B.cbase[cls];
     const long long s_lo = base + share_lo(E, G, b), s_hi = base + share_lo(E, G, b + 1);
     int par = 0;
-    for (int i = i0 + mat_of_entry_from(B, i0, i1, s_lo); i < i1; ++i) {
-        const PsMat& M = B.mat[i];
+    for (int i = mat_of_entry(B, i0, i1, s_lo); i < i1; ++i) {
+        const PsMat M = mat_at(B, i);
         if (M.off >= s_hi) break;
         int r0, r1;
         rows_in_share(M, s_lo, s_hi, r0, r1);
@@ -566,54 +584,63 @@ __device__ __forceinline__ void gram_schmidt_coeffs(const double G[16], int r, d
     }
 }
 
-// One workgroup per QR_COLS columns of one matrix: sums the M^T P partials of
-// its columns (waves split the partials, combined in a fixed order), rebuilds
-// G and T from the Gram partials, writes Q' = (M^T P) T.
-__global__ __launch_bounds__(PS_THREADS) void psgd_qreduce(const PsBatch B) {
-    __shared__ double s_red[PS_THREADS / 64][16];
+// Q reduction.  A matrix with nq M^T P partials uses S = qr_slices(nq)
+// threads per column (a power of two): workgroup lwg takes columns
+// [lwg 256/S, (lwg+1) 256/S), thread t sums the partials c = t / (256/S) + S i
+// of column t % (256/S) in order, and the S slice sums are added in slice
+// order through LDS.  The Gram partials are summed the same way with 16
+// slices.  Thread 0 builds T; the column threads write Q' = (M^T P) T.
+__global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
+    __shared__ double s_g[16][16];
     __shared__ double s_T[16];
-    __shared__ double s_part[PS_THREADS / 64][QR_COLS][4];
-    const int mi = find_in_range(B.begin_r, 0, B.count, blockIdx.x);
-    const PsMat& M = B.mat[mi];
-    const int lwg = blockIdx.x - B.begin_r[mi];
-    const int m = M.m, r = M.rank;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // Gram matrix: fixed-order sum of the partials
-    double g[16];
+    __shared__ double4 s_q[PS_THREADS];
+    const PsMat M = mat_at(B, mat_of_block<MAP_R>(B, 0, B.count, blockIdx.x));
+    const int lwg = blockIdx.x - M.begin_r;
+    const int m = M.m, r = M.rank, t = threadIdx.x;
+    const int S = M.qs, QC = PS_THREADS / S;
+    {
+        const int e = t & 15, sl = t >> 4;
+        double g = 0.0;
+        for (int b = sl; b < M.ng; b += 64) {
+            // loads issued together, added in partial order
+            double x[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) g[i] = 0.0;
-    for (int b = threadIdx.x; b < M.ng; b += PS_THREADS) {
-        const double* src = M.gpart + static_cast<long long>(b) * 16;
+            for (int u = 0; u < 4; ++u) {
+                const int bu = b + 16 * u;
+                x[u] = bu < M.ng ? M.gpart[static_cast<long long>(bu) * 16 + e] : 0.0;
+            }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) g[i] += src[i];
+            for (int u = 0; u < 4; ++u) g += x[u];
+        }
+        s_g[sl][e] = g;
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) g[i] = wave_sum(g[i]);
-    if (lane == 0) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s_red[w][i] = g[i];
-    }
-    // column partials: lane = column, waves take every 4th partial
-    const int col = lwg * QR_COLS + lane;
-    const bool valid = col < m;
-    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
-    if (valid) {
+    const int cl = t % QC, sl = t / QC;
+    const int col = lwg * QC + cl;
+    double4 sv = make_double4(0.0, 0.0, 0.0, 0.0);
+    if (col < m) {
         const float4* qp = reinterpret_cast<const float4*>(M.qpart) + col;
-#pragma unroll 4
-        for (int c = w; c < M.nq; c += 4) {
-            const float4 t = qp[static_cast<long long>(c) * m];
-            s0 += t.x; s1 += t.y; s2 += t.z; s3 += t.w;
+        for (int c = sl; c < M.nq; c += 4 * S) {
+            float4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int cu = c + S * u;
+                x[u] = cu < M.nq ? qp[static_cast<long long>(cu) * m] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                sv.x += x[u].x; sv.y += x[u].y; sv.z += x[u].z; sv.w += x[u].w;
+            }
         }
     }
-    s_part[w][lane][0] = s0;
-    s_part[w][lane][1] = s1;
-    s_part[w][lane][2] = s2;
-    s_part[w][lane][3] = s3;
+    s_q[t] = sv;
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (t == 0) {
         double G[16], T[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) G[i] = ((s_red[0][i] + s_red[1][i]) + s_red[2][i]) + s_red[3][i];
+        for (int i = 0; i < 16; ++i) {
+            double g = 0.0;
+            for (int k = 0; k < 16; ++k) g += s_g[k][i];
+            G[i] = g;
+        }
         gram_schmidt_coeffs(G, r, T);
 #pragma unroll
         for (int i = 0; i < 16; ++i) s_T[i] = T[i];
@@ -623,17 +650,19 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_qreduce(const PsBatch B) {
         }
     }
     __syncthreads();
-    if (w == 0 && valid) {
-        double sv[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-            sv[a] = ((s_part[0][lane][a] + s_part[1][lane][a]) + s_part[2][lane][a]) + s_part[3][lane][a];
+    if (t < QC && col < m) {
+        double4 a = s_q[t];
+        for (int k = 1; k < S; ++k) {
+            const double4 x = s_q[k * QC + t];
+            a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+        }
+        const double sa[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (j < r) {
                 double v = 0.0;
 #pragma unroll
-                for (int a = 0; a <= j; ++a) v += sv[a] * s_T[a * 4 + j];
+                for (int i = 0; i <= j; ++i) v += sa[i] * s_T[i * 4 + j];
                 M.q[static_cast<long long>(j) * m + col] = static_cast<float>(v);
             }
         }
@@ -647,10 +676,15 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_qreduce(const PsBatch B) {
 template <bool BF16, int VEC>
 __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int r1) {
     const int n = M.n, m = M.m, r = M.rank;
+    // P and T were written by earlier kernels and are only read here: the
+    // constant address space gives scalar loads that no store has to wait for
+    typedef const __attribute__((address_space(4))) double* ConstD;
+    typedef const __attribute__((address_space(4))) float* ConstF;
+    const ConstD tm = (ConstD)(M.tmat);
+    const ConstF pr = (ConstF)(M.praw);
     float T[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) T[i] = static_cast<float>(M.tmat[i]);
-    const float4* praw4 = reinterpret_cast<const float4*>(M.praw);
+    for (int i = 0; i < 16; ++i) T[i] = static_cast<float>(tm[i]);
     const int ns = nstrips_of(m);
     for (int strip = 0; strip < ns; ++strip) {
         const int col0 = strip * (PS_THREADS * VEC) + threadIdx.x * VEC;
@@ -682,8 +716,7 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
             for (int u = 0; u < ROW_GROUP; ++u) {
                 const int i = i0 + u;
                 if (i >= r1) break;
-                const float4 pr = praw4[i];
-                const float prv[4] = {pr.x, pr.y, pr.z, pr.w};
+                const float prv[4] = {pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
                 float ph[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -728,8 +761,8 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_out(const PsBatch B) {
     const int b = blockIdx.x, G = B.gout;
     const long long E = B.eall;
     const long long s_lo = share_lo(E, G, b), s_hi = share_lo(E, G, b + 1);
-    for (int i = mat_of_entry(B, B.count, s_lo); i < B.count; ++i) {
-        const PsMat& M = B.mat[i];
+    for (int i = mat_of_entry(B, 0, B.count, s_lo); i < B.count; ++i) {
+        const PsMat M = mat_at(B, i);
         if (M.off >= s_hi) break;
         int r0, r1;
         rows_in_share(M, s_lo, s_hi, r0, r1);
@@ -765,15 +798,19 @@ struct PlanMat {
     int idx;            // index in the caller's array
     long long off;      // first entry within the batch
     int nq, ng;         // partial counts
+    int begin_p, begin_q, begin_r;
+    int qs;             // psgd_qreduce threads per column
     size_t ws_off;      // workspace offset of this matrix's scratch
 };
 struct PlanBatch {
     int first, count;                  // into Plan::mats
+    size_t tbl_off;                    // workspace offset of the device table
     int cbeg[PQ_CLASSES + 2];
     int cgrid[PQ_CLASSES];
     long long cbase[PQ_CLASSES], cent[PQ_CLASSES];
     long long eall;
     int gout;
+    int np, nq, nr;                    // psgd_p / psgd_q / psgd_qreduce grids
 };
 struct Plan {
     std::vector<PlanMat> mats;
@@ -782,6 +819,14 @@ struct Plan {
 };
 
 size_t ws_round(size_t x) { return round_up(x, 256); }
+
+// Threads per column in psgd_qreduce: the smallest power of two that leaves
+// each thread at most QR_PER_THREAD partials, at most 64.
+int qr_slices(int nq) {
+    int sl = 1;
+    while (sl < 64 && sl * QR_PER_THREAD < nq) sl *= 2;
+    return sl;
+}
 
 // Grid of a balanced pass over e entries whose widest row has mmax entries:
 // every share is at least one such row, so a workgroup owns a row of every
@@ -802,6 +847,8 @@ Plan make_plan(const gc_mat* mats, int nmats) {
         PlanBatch pb{};
         pb.first = static_cast<int>(P.mats.size());
         pb.count = j - i;
+        pb.tbl_off = o;
+        o += ws_round(static_cast<size_t>(pb.count) * sizeof(PsMat));
         int ccount[PQ_CLASSES + 1] = {0, 0, 0, 0};
         int cmax[PQ_CLASSES] = {1, 1, 1};
         for (int a : idx) {
@@ -834,7 +881,15 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             } else {
                 pm.nq = (n + Q_ROWS - 1) / Q_ROWS;
                 pm.ng = (n + P_ROWS_WG - 1) / P_ROWS_WG;
+                pm.begin_p = pb.np;
+                pb.np += pm.ng;
+                pm.begin_q = pb.nq;
+                pb.nq += nstrips_host(m) * pm.nq;
             }
+            pm.qs = qr_slices(pm.nq);
+            pm.begin_r = pb.nr;
+            const int qc = PS_THREADS / pm.qs;
+            pb.nr += (m + qc - 1) / qc;
             pm.ws_off = o;
             o += ws_round(static_cast<size_t>(n) * 16);                       // praw
             o += ws_round(static_cast<size_t>(pm.ng) * 16 * 8);               // gpart
@@ -874,15 +929,17 @@ int validate_mat(const gc_mat& a, int i, int dtype) {
     return GC_OK;
 }
 
-// Launches all kernels of one batch (fused classes first, then the split path).
+// Launches all kernels of one batch: the table copy, the fused classes,
+// the split path, the Q reduction and the output pass.
 template <bool BF16>
-int run_batch(PsBatch& B, hipStream_t s) {
+int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& tbl, hipStream_t s) {
     int rc;
-    int nr = 0;
-    for (int i = 0; i < B.count; ++i) {
-        B.begin_r[i] = nr;
-        nr += (B.mat[i].m + QR_COLS - 1) / QR_COLS;
-    }
+    // The table goes to the device in stream order.  From pageable memory the
+    // runtime stages the bytes before returning, so `tbl` may go out of scope.
+    const hipError_t e = hipMemcpyAsync(const_cast<PsMat*>(B.tbl), tbl.data(), tbl.size() * sizeof(PsMat),
+                                        hipMemcpyHostToDevice, s);
+    if (e != hipSuccess)
+        return fail(GC_ERR_HIP, std::string("gc_powersgd_ef_step: matrix table copy: ") + hipGetErrorString(e));
     for (int c = 0; c < PQ_CLASSES; ++c) {
         if (B.cbeg[c + 1] == B.cbeg[c]) continue;
         TimedLaunch tl("psgd_pq", s);
@@ -893,26 +950,20 @@ int run_batch(PsBatch& B, hipStream_t s) {
     }
     const int s0 = B.cbeg[SPLIT_CLASS];
     if (s0 < B.count) {
-        int np = 0, nq = 0;
-        for (int i = s0; i < B.count; ++i) {
-            const PsMat& M = B.mat[i];
-            B.begin_p[i] = np; np += (M.n + P_ROWS_WG - 1) / P_ROWS_WG;
-            B.begin_q[i] = nq; nq += nstrips_host(M.m) * ((M.n + Q_ROWS - 1) / Q_ROWS);
-        }
         {
             TimedLaunch tl("psgd_p", s);
-            psgd_p<BF16><<<np, PS_THREADS, 0, s>>>(B, s0, B.count);
+            psgd_p<BF16><<<pb.np, PS_THREADS, 0, s>>>(B, s0, B.count);
             if ((rc = check_launch("psgd_p")) != GC_OK) return rc;
         }
         {
             TimedLaunch tl("psgd_q", s);
-            psgd_q<BF16><<<nq, PS_THREADS, 0, s>>>(B, s0, B.count);
+            psgd_q<BF16><<<pb.nq, PS_THREADS, 0, s>>>(B, s0, B.count);
             if ((rc = check_launch("psgd_q")) != GC_OK) return rc;
         }
     }
     {
         TimedLaunch tl("psgd_qreduce", s);
-        psgd_qreduce<<<nr, PS_THREADS, 0, s>>>(B);
+        psgd_qreduce<<<pb.nr, PS_THREADS, 0, s>>>(B);
         if ((rc = check_launch("psgd_qreduce")) != GC_OK) return rc;
     }
     {
@@ -958,6 +1009,7 @@ int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta
     char* wp = static_cast<char*>(ws);
     for (const PlanBatch& pb : P.batches) {
         PsBatch B{};
+        B.tbl = reinterpret_cast<const PsMat*>(wp + pb.tbl_off);
         B.count = pb.count;
         B.eta = eta;
         for (int c = 0; c < PQ_CLASSES + 2; ++c) B.cbeg[c] = pb.cbeg[c];
@@ -968,11 +1020,12 @@ int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta
         }
         B.eall = pb.eall;
         B.gout = pb.gout;
+        std::vector<PsMat> tbl(pb.count);
         for (int k = 0; k < pb.count; ++k) {
             const PlanMat& pm = P.mats[pb.first + k];
             const gc_mat& a = mats[pm.idx];
             char* base = wp + pm.ws_off;
-            PsMat& M = B.mat[k];
+            PsMat& M = tbl[k];
             M.grad = a.grad;
             M.mem = a.mem;
             M.q = a.q;
@@ -991,8 +1044,12 @@ int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta
             M.rank = a.rank;
             M.nq = pm.nq;
             M.ng = pm.ng;
+            M.begin_p = pm.begin_p;
+            M.begin_q = pm.begin_q;
+            M.begin_r = pm.begin_r;
+            M.qs = pm.qs;
         }
-        const int rc = grad_dtype == GC_BF16 ? run_batch<true>(B, s) : run_batch<false>(B, s);
+        const int rc = grad_dtype == GC_BF16 ? run_batch<true>(B, pb, tbl, s) : run_batch<false>(B, pb, tbl, s);
         if (rc != GC_OK) return rc;
     }
     return GC_OK;
