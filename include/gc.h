@@ -123,7 +123,9 @@ typedef struct gc_mat {
 } gc_mat;
 
 /* Workspace bytes for gc_powersgd_ef_step on these matrices ([host] array).
- * Returns 0 when an entry is out of range. */
+ * The workspace layout is planned from the shapes and their order (not the
+ * ranks, dtype or pointers): query with the same array, in the same order,
+ * that the step will receive.  Returns 0 when an entry is out of range. */
 size_t gc_powersgd_workspace_bytes(const gc_mat* mats, int nmats);
 
 /* One PowerSGD step with error feedback on every matrix of mats ([host], nmats >= 1):
@@ -133,6 +135,9 @@ size_t gc_powersgd_workspace_bytes(const gc_mat* mats, int nmats);
  *     out = P^ Q^T;  mem = M - out
  * float32 storage; the Gram matrix and the orthonormalisation are in float64.
  * Buffers of different matrices must not overlap.
+ * The call copies a small matrix table (120 bytes per matrix) from host memory
+ * into ws with one hipMemcpyAsync on `stream`, then enqueues the kernels; the
+ * host array may be reused as soon as the call returns.
  * Errors: GC_ERR_ARG, GC_ERR_DTYPE, GC_ERR_WORKSPACE, GC_ERR_HIP. */
 int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta,
                         void* ws, size_t ws_bytes, void* stream);
