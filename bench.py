@@ -169,7 +169,7 @@ class C5(Workload):
         mat_elems = sum(n * m for n, m in shapes)
         self.kernel_bytes = {
             **psgd_kernel_bytes(shapes, self.ps.ranks, 2),
-            "topk_accum_hist": 10 * emb_d, "topk_capture": 4 * emb_d,
+            "topk_accum_hist": 10 * emb_d,
             "topk_decode_set": 4 * emb_d + 8 * self.k,
             "norm_partial": 2 * total / 10.0,
         }
@@ -233,7 +233,7 @@ class C3(Workload):
         self.ws = torch.empty(gc.gc_topk_workspace_bytes(d, k), dtype=torch.uint8, device=dev)
         self.grad_bytes = 4 * d
         self.alg_bytes = 16 * d + 16 * k
-        self.kernel_bytes = {"topk_accum_hist": 12 * d, "topk_capture": 4 * d, "topk_decode_set": 4 * d + 8 * k}
+        self.kernel_bytes = {"topk_accum_hist": 12 * d, "topk_decode_set": 4 * d + 8 * k}
         self.description = gen.WORKLOADS["c3"].description + f" (k={k})"
         self.config = {"workload": "resnet50-sized flat gradient", "params": d, "topk_k": k,
                        "grad_dtype": "f32", "memory_dtype": "f32", "eta": 1.0}

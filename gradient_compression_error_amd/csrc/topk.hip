@@ -8,25 +8,35 @@
 // without the sign (31 bits; key order == |x| order for non-NaN x).  The
 // threshold key T is found by a three-level radix select (12 + 12 + 7 bits):
 //
+//   topk_prep        zeroes the histograms; one workgroup samples 16384 entries
+//                    of acc and sets a guess G below the expected threshold
 //   topk_accum_hist  acc = fl32(m + fl32(eta*g)) written over m; 4096-bin LDS
 //                    histogram of key>>19 per workgroup, merged with device
-//                    atomics into one of 8 copies.                       topk_select1 -> bin b1
-//   topk_capture     re-reads acc; every entry with key>>19 >= b1 is appended,
-//                    in index order, to its tile's slot region (wave ballots +
-//                    a cross-wave prefix); entries in bin b1 feed the level-2
-//                    histogram.                     topk_select2 -> bin b2
+//                    atomics into one of 8 copies; every entry with key >= G
+//                    is appended, in index order, to its tile's slot region
+//                    (wave ballots + a cross-wave prefix).  topk_select1 -> bin b1
+//   topk_capture     when G <= b1's lower edge every candidate is already in
+//                    the slots: only the level-2 histogram of bin b1 is built
+//                    from them.  Otherwise re-reads acc and appends every
+//                    entry with key>>19 >= b1 instead.  topk_select2 -> bin b2
 //   topk_refine      level-3 histogram over the captured entries only.
-//                                                   topk_select3 -> T, ties to take
-//   topk_count       per tile: #(key > T), #(key == T).
-//                                                   topk_scan -> per-tile offsets
-//   topk_emit        writes the k (index, value) pairs in ascending index
-//                    order and zeroes the selected memory entries.
+//   topk_count       threshold T and ties to take from the level-3 histogram
+//                    (every workgroup), then #(key > T) and #(key == T) over
+//                    the workgroup's contiguous range of tiles.
+//   topk_emit        same ranges: output offset from the earlier ranges'
+//                    counts, then the k (index, value) pairs in ascending
+//                    index order; zeroes the selected memory entries.
 //
-// Only the first two kernels touch all d entries (16 B/entry for fp32
-// gradients); the rest work on the captured entries.  The select/scan steps
+// Only topk_accum_hist touches all d entries when the guess holds (12 B/entry
+// for fp32 gradients); the rest work on the captured entries, which are a
+// superset of the candidates at or above the threshold in index order, so
+// the later kernels filter by key.  The guess only decides how much work is
+// done, never the result.  The select steps
 // are single-workgroup kernels: the kernel boundary is the only cross-
 // workgroup synchronisation (a per-workgroup device-scope release fence
 // would write back the L2 once per workgroup).
+#include <cmath>
+
 #include "gc_common.h"
 
 namespace gc {
@@ -44,20 +54,23 @@ constexpr int H3_BINS = 128;   // key bits 6..0
 constexpr int NCOPY = 8;       // copies of the level-1/2 histograms (spreads the device atomics)
 constexpr int TK_SMALL_GRID = 1024;
 constexpr int DEC_TILE = 4096;
-constexpr int INIT_BLOCKS = 64;
+constexpr int PREP_ZERO_BLOCKS = 32;     // topk_prep blocks that zero the histograms
+constexpr int FAST_GRID = 512;           // workgroups of topk_capture's slot pass
 
 struct TopkState {
     unsigned b1, above1;       // level-1 bin, #keys in higher level-1 bins
     unsigned prefix2, above2;  // (b1 << 12) | b2, #keys with (key >> 7) > prefix2
     unsigned thr, above3;      // threshold key T, #keys > T
     unsigned need;             // #keys == T taken (lowest indices first)
-    unsigned pad[9];
+    unsigned guess;            // keys >= guess are captured by topk_accum_hist
+    unsigned fast;             // 1: the captured slots hold every key >= b1 << 19
+    unsigned pad[7];
 };
 static_assert(sizeof(TopkState) == 64, "TopkState layout");
 
 struct TopkLayout {
-    size_t state, hist1, hist2, hist3, tile_cnt, tile_gt, tile_eq, eq_before, out_off;
-    size_t slot_idx, slot_val, total, zero_bytes;
+    size_t state, hist1, hist2, hist3, tile_cnt, wg_gt, wg_eq;
+    size_t slot_idx, slot_val, total, zero_from, zero_end;
     long long ntiles;
 };
 
@@ -67,15 +80,14 @@ TopkLayout topk_layout(long long d) {
     const size_t nt = static_cast<size_t>(L.ntiles);
     size_t o = 0;
     L.state = o;     o += round_up(sizeof(TopkState), 256);
+    L.zero_from = o;
     L.hist1 = o;     o += NCOPY * H1_BINS * 4;
     L.hist2 = o;     o += NCOPY * H2_BINS * 4;
     L.hist3 = o;     o += round_up(H3_BINS * 4, 256);
-    L.zero_bytes = o;
+    L.zero_end = o;
     L.tile_cnt = o;  o += round_up(nt * 4, 256);
-    L.tile_gt = o;   o += round_up(nt * 4, 256);
-    L.tile_eq = o;   o += round_up(nt * 4, 256);
-    L.eq_before = o; o += round_up(nt * 4, 256);
-    L.out_off = o;   o += round_up(nt * 4, 256);
+    L.wg_gt = o;     o += TK_SMALL_GRID * 4;
+    L.wg_eq = o;     o += TK_SMALL_GRID * 4;
     L.slot_idx = o;  o += round_up(nt * TK_TILE * 4, 256);
     L.slot_val = o;  o += round_up(nt * TK_TILE * 4, 256);
     L.total = o;
@@ -91,10 +103,10 @@ TopkLayout topk_layout(long long d) {
 // The histogram was completed by the previous kernel; its copies are summed
 // into LDS first (all loads independent).  Whole block; results in shared
 // memory after the final barrier.
-template <int NBINS, int NC>
-__device__ void select_bin_256(const unsigned* __restrict__ hist, int stride, unsigned need, unsigned* s_h,
-                               unsigned* s_tmp, unsigned* s_bin, unsigned* s_above) {
-    constexpr int PER = (NBINS + TK_THREADS - 1) / TK_THREADS;
+template <int NBINS, int NC, int NT = TK_THREADS>
+__device__ void select_bin(const unsigned* hist, int stride, unsigned need, unsigned* s_h,
+                           unsigned* s_tmp, unsigned* s_bin, unsigned* s_above) {
+    constexpr int PER = (NBINS + NT - 1) / NT;
     const int t = threadIdx.x;
     if (t == 0) {
         *s_bin = 0u;
@@ -103,13 +115,13 @@ __device__ void select_bin_256(const unsigned* __restrict__ hist, int stride, un
     unsigned v[PER][NC];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int b = t + i * TK_THREADS;
+        const int b = t + i * NT;
 #pragma unroll
         for (int k = 0; k < NC; ++k) v[i][k] = (b < NBINS) ? hist[k * stride + b] : 0u;
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int b = t + i * TK_THREADS;
+        const int b = t + i * NT;
         unsigned c = 0;
 #pragma unroll
         for (int k = 0; k < NC; ++k) c += v[i][k];
@@ -127,7 +139,7 @@ __device__ void select_bin_256(const unsigned* __restrict__ hist, int stride, un
         s += cnt[i];
     }
     unsigned total;
-    const unsigned incl = block_inclusive_scan_256(s, s_tmp, &total);
+    const unsigned incl = block_inclusive_scan<NT / 64>(s, s_tmp, &total);
     const unsigned excl = incl - s;
     if (s > 0 && excl < need && need <= incl) {
         unsigned run = excl;
@@ -150,8 +162,63 @@ __device__ void select_bin_256(const unsigned* __restrict__ hist, int stride, un
 
 // ---------------------------------------------------------------- kernels
 
-__global__ __launch_bounds__(256) void topk_init(uint4* __restrict__ zero, int n16) {
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < n16; i += gridDim.x * 256) zero[i] = make_uint4(0u, 0u, 0u, 0u);
+constexpr int PREP_THREADS = 1024;
+constexpr int SAMPLE_RUN = 64;                       // consecutive entries per sampled run
+constexpr int SAMPLE_RUNS = 256;
+constexpr int SAMPLES = SAMPLE_RUN * SAMPLE_RUNS;    // entries sampled for the guess
+constexpr int SAMPLES_PER_THREAD = SAMPLES / PREP_THREADS;
+
+// Block 0: writes the state record (zeros and the guess).  It samples
+// S = min(d, 16384) entries of acc -- all of them when d <= 16384, else 256
+// runs of 64 consecutive entries starting at floor(r d / 256) (a wave reads
+// one run: few cache lines and pages) -- histograms their level-1 bins and
+// sets guess = lower edge of the bin holding the sample of rank `rank_g` from
+// the top (rank_g >= S: guess = 0, capture all).  Blocks 1..: zero the
+// histograms.
+template <bool BF16>
+__global__ __launch_bounds__(PREP_THREADS) void topk_prep(
+        const void* __restrict__ grad, const float* __restrict__ mem, long long d, float eta,
+        unsigned rank_g, TopkState* __restrict__ st, uint4* __restrict__ zero, int n16) {
+    if (blockIdx.x > 0) {
+        const int stride = (gridDim.x - 1) * PREP_THREADS;
+        for (int i = (blockIdx.x - 1) * PREP_THREADS + threadIdx.x; i < n16; i += stride)
+            zero[i] = make_uint4(0u, 0u, 0u, 0u);
+        return;
+    }
+    __shared__ unsigned h[H1_BINS];
+    __shared__ unsigned s_tmp[PREP_THREADS / 64];
+    __shared__ unsigned s_bin, s_above;
+    for (int i = threadIdx.x; i < H1_BINS; i += PREP_THREADS) h[i] = 0u;
+    __syncthreads();
+    const long long S = d < SAMPLES ? d : SAMPLES;
+    float mv[SAMPLES_PER_THREAD], gv[SAMPLES_PER_THREAD];
+#pragma unroll
+    for (int u = 0; u < SAMPLES_PER_THREAD; ++u) {
+        const long long smp = threadIdx.x + static_cast<long long>(u) * PREP_THREADS;
+        long long pos = 0;
+        if (smp < S) {
+            const long long run = smp / SAMPLE_RUN;
+            pos = S == d ? smp : run * d / SAMPLE_RUNS + smp % SAMPLE_RUN;
+        }
+        mv[u] = mem[pos];
+        gv[u] = load_grad1<BF16>(grad, pos);
+    }
+#pragma unroll
+    for (int u = 0; u < SAMPLES_PER_THREAD; ++u) {
+        const long long smp = threadIdx.x + static_cast<long long>(u) * PREP_THREADS;
+        if (smp < S) atomicAdd(&h[key_of(ef_acc(mv[u], eta, gv[u])) >> H1_SHIFT], 1u);
+    }
+    __syncthreads();
+    unsigned guess = 0u;
+    if (rank_g < static_cast<unsigned>(S)) {
+        select_bin<H1_BINS, 1, PREP_THREADS>(h, H1_BINS, rank_g, h, s_tmp, &s_bin, &s_above);
+        guess = s_bin << H1_SHIFT;
+    }
+    if (threadIdx.x == 0) {
+        TopkState z{};
+        z.guess = guess;
+        *st = z;
+    }
 }
 
 template <bool BF16>
@@ -165,17 +232,77 @@ __device__ __forceinline__ void load_sub(const void* __restrict__ grad, const fl
     }
 }
 
+// In-order append of the flagged entries of U chunks of the tile.  In chunk u
+// entry j of thread t comes after every flagged entry of lower threads (all
+// waves) and of lower j, and chunks follow each other.  `cnt` holds the
+// per-(chunk, wave) counts, double-buffered by parity: one barrier.  Returns
+// the number appended by the whole workgroup.
+template <int U, int J>
+__device__ __forceinline__ unsigned append_chunks(const bool (&flag)[U][J], const float (&val)[U][J],
+                                                  const long long (&idx0)[U], unsigned running,
+                                                  int* __restrict__ sidx, float* __restrict__ sval,
+                                                  unsigned (*cnt)[TK_SUBS][4], int& parity) {
+    static_assert(U <= TK_SUBS, "chunks per append");
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const unsigned long long lt = lanemask_lt();
+    unsigned before[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        unsigned b = 0, wtot = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const unsigned long long bal = __ballot(flag[u][j]);
+            b += __popcll(bal & lt);
+            wtot += __popcll(bal);
+        }
+        before[u] = b;
+        if (lane == 0) cnt[parity][u][w] = wtot;
+    }
+    __syncthreads();
+    unsigned run = running;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        unsigned wbefore = 0, ctot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const unsigned c = cnt[parity][u][i];
+            wbefore += (i < w) ? c : 0u;
+            ctot += c;
+        }
+        unsigned pos = run + wbefore + before[u];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            if (flag[u][j]) {
+                sidx[pos] = static_cast<int>(idx0[u] + j);
+                sval[pos] = val[u][j];
+                ++pos;
+            }
+        }
+        run += ctot;
+    }
+    parity ^= 1;
+    return run - running;
+}
+
 // acc = fl32(m + fl32(eta*g)) over TK_TILE entries per workgroup (sub-tile s+1
-// is loaded before sub-tile s is stored), with a level-1 histogram in LDS.
+// is loaded before sub-tile s is stored), with a level-1 histogram in LDS;
+// entries with key >= guess go to the tile's slots in index order.
 template <bool BF16>
 __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
         const void* __restrict__ grad, float* __restrict__ mem, long long d, float eta,
-        unsigned* __restrict__ hist1) {
+        const TopkState* __restrict__ st, unsigned* __restrict__ hist1, int* __restrict__ slot_idx,
+        float* __restrict__ slot_val, unsigned* __restrict__ tile_cnt) {
     __shared__ unsigned h[H1_BINS];
+    __shared__ unsigned s_cnt[2][TK_SUBS][4];
     for (int i = threadIdx.x; i < H1_BINS; i += TK_THREADS) h[i] = 0u;
     __syncthreads();
 
+    const unsigned guess = st->guess;
     const long long base = static_cast<long long>(blockIdx.x) * TK_TILE;
+    int* const sidx = slot_idx + base;
+    float* const sval = slot_val + base;
+    unsigned running = 0;
+    int parity = 0;
     long long nfull = (d - base) / TK_SUB;
     if (nfull > TK_SUBS) nfull = TK_SUBS;
     float4 gv[4], mv[4];
@@ -184,19 +311,26 @@ __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
         const long long b4 = (base + static_cast<long long>(sb) * TK_SUB) / 4;
         float4 gn[4], mn[4];
         if (sb + 1 < nfull) load_sub<BF16>(grad, mem, b4 + TK_SUB / 4, gn, mn);
+        float a[4][4];
+        bool cap[4][4];
+        long long e0[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            float4 a;
-            a.x = ef_acc(mv[u].x, eta, gv[u].x);
-            a.y = ef_acc(mv[u].y, eta, gv[u].y);
-            a.z = ef_acc(mv[u].z, eta, gv[u].z);
-            a.w = ef_acc(mv[u].w, eta, gv[u].w);
-            reinterpret_cast<float4*>(mem)[b4 + u * TK_THREADS + threadIdx.x] = a;
-            atomicAdd(&h[key_of(a.x) >> H1_SHIFT], 1u);
-            atomicAdd(&h[key_of(a.y) >> H1_SHIFT], 1u);
-            atomicAdd(&h[key_of(a.z) >> H1_SHIFT], 1u);
-            atomicAdd(&h[key_of(a.w) >> H1_SHIFT], 1u);
+            a[u][0] = ef_acc(mv[u].x, eta, gv[u].x);
+            a[u][1] = ef_acc(mv[u].y, eta, gv[u].y);
+            a[u][2] = ef_acc(mv[u].z, eta, gv[u].z);
+            a[u][3] = ef_acc(mv[u].w, eta, gv[u].w);
+            const long long i4 = b4 + u * TK_THREADS + threadIdx.x;
+            e0[u] = i4 * 4;
+            reinterpret_cast<float4*>(mem)[i4] = make_float4(a[u][0], a[u][1], a[u][2], a[u][3]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned key = key_of(a[u][j]);
+                atomicAdd(&h[key >> H1_SHIFT], 1u);
+                cap[u][j] = key >= guess;
+            }
         }
+        running += append_chunks<4, 4>(cap, a, e0, running, sidx, sval, s_cnt, parity);
         if (sb + 1 < nfull) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -207,11 +341,21 @@ __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
     }
     const long long t0 = base + nfull * TK_SUB;
     const long long t1 = min(d, base + static_cast<long long>(TK_TILE));
-    for (long long i = t0 + threadIdx.x; i < t1; i += TK_THREADS) {
-        const float a = ef_acc(mem[i], eta, load_grad1<BF16>(grad, i));
-        mem[i] = a;
-        atomicAdd(&h[key_of(a) >> H1_SHIFT], 1u);
+    for (long long i0 = t0; i0 < t1; i0 += TK_THREADS) {
+        const long long i = i0 + threadIdx.x;
+        bool cap[1][1] = {{false}};
+        float a[1][1] = {{0.0f}};
+        const long long e0[1] = {i};
+        if (i < t1) {
+            a[0][0] = ef_acc(mem[i], eta, load_grad1<BF16>(grad, i));
+            mem[i] = a[0][0];
+            const unsigned key = key_of(a[0][0]);
+            atomicAdd(&h[key >> H1_SHIFT], 1u);
+            cap[0][0] = key >= guess;
+        }
+        running += append_chunks<1, 1>(cap, a, e0, running, sidx, sval, s_cnt, parity);
     }
+    if (threadIdx.x == 0) tile_cnt[blockIdx.x] = running;
     __syncthreads();
     unsigned* dst = hist1 + (blockIdx.x % NCOPY) * H1_BINS;
     for (int i = threadIdx.x; i < H1_BINS; i += TK_THREADS) {
@@ -225,90 +369,82 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select1(const unsigned* __res
     __shared__ unsigned s_h[H1_BINS];
     __shared__ unsigned s_tmp[4];
     __shared__ unsigned s_bin, s_above;
-    select_bin_256<H1_BINS, NCOPY>(hist1, H1_BINS, k, s_h, s_tmp, &s_bin, &s_above);
+    select_bin<H1_BINS, NCOPY>(hist1, H1_BINS, k, s_h, s_tmp, &s_bin, &s_above);
     if (threadIdx.x == 0) {
         st->b1 = s_bin;
         st->above1 = s_above;
+        st->fast = st->guess <= (s_bin << H1_SHIFT) ? 1u : 0u;
     }
 }
 
-// Re-reads acc; appends every entry with key>>19 >= b1, in index order, to the
-// workgroup's slot tile; entries in bin b1 feed the level-2 histogram.
+// Level-2 histogram of bin b1.  Fast case (every key >= b1 << 19 is already in
+// the slots): from the tile's slots.  Otherwise re-reads acc and replaces the
+// tile's slots with the entries of key>>19 >= b1, in index order.
 __global__ __launch_bounds__(TK_THREADS) void topk_capture(
         const float* __restrict__ acc, long long d, const TopkState* __restrict__ st,
         unsigned* __restrict__ hist2, int* __restrict__ slot_idx, float* __restrict__ slot_val,
         unsigned* __restrict__ tile_cnt) {
     __shared__ unsigned h[H2_BINS];
-    __shared__ unsigned s_wave[2][4];
+    __shared__ unsigned s_cnt[2][TK_SUBS][4];
     for (int i = threadIdx.x; i < H2_BINS; i += TK_THREADS) h[i] = 0u;
     __syncthreads();
 
     const unsigned b1 = st->b1;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const unsigned long long lt = lanemask_lt();
     const long long base = static_cast<long long>(blockIdx.x) * TK_TILE;
     int* const sidx = slot_idx + base;
     float* const sval = slot_val + base;
-    unsigned running = 0;
-    int parity = 0;
-    for (int sb = 0; sb < TK_SUBS; ++sb) {
-        const long long sbase = base + static_cast<long long>(sb) * TK_SUB;
-        if (sbase >= d) break;
-        float v[4][4];
-        bool ok[4][4];
+    if (st->fast) {
+        // the first FAST_GRID workgroups stride over the tiles' slots; the rest exit
+        const int ntiles = static_cast<int>(gridDim.x);
+        if (static_cast<int>(blockIdx.x) >= FAST_GRID) return;
+        for (int t = blockIdx.x; t < ntiles; t += FAST_GRID) {
+            const unsigned cnt = tile_cnt[t];
+            const float* tv = slot_val + static_cast<long long>(t) * TK_TILE;
+            for (unsigned e = threadIdx.x; e < cnt; e += TK_THREADS) {
+                const unsigned key = key_of(tv[e]);
+                if ((key >> H1_SHIFT) == b1) atomicAdd(&h[(key >> H2_SHIFT) & (H2_BINS - 1)], 1u);
+            }
+        }
+    } else {
+        unsigned running = 0;
+        int parity = 0;
+        for (int sb = 0; sb < TK_SUBS; ++sb) {
+            const long long sbase = base + static_cast<long long>(sb) * TK_SUB;
+            if (sbase >= d) break;
+            float v[4][4];
+            bool ok[4][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const long long e0 = sbase + u * (TK_THREADS * 4) + threadIdx.x * 4;
-            if (e0 + 3 < d) {
-                const float4 a = reinterpret_cast<const float4*>(acc)[e0 / 4];
-                v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
-                ok[u][0] = ok[u][1] = ok[u][2] = ok[u][3] = true;
-            } else {
+            for (int u = 0; u < 4; ++u) {
+                const long long e0 = sbase + u * (TK_THREADS * 4) + threadIdx.x * 4;
+                if (e0 + 3 < d) {
+                    const float4 x = reinterpret_cast<const float4*>(acc)[e0 / 4];
+                    v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+                    ok[u][0] = ok[u][1] = ok[u][2] = ok[u][3] = true;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        ok[u][j] = (e0 + j) < d;
+                        v[u][j] = ok[u][j] ? acc[e0 + j] : 0.0f;
+                    }
+                }
+            }
+            bool cap[4][4];
+            long long e0[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                e0[u] = sbase + u * (TK_THREADS * 4) + threadIdx.x * 4;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    ok[u][j] = (e0 + j) < d;
-                    v[u][j] = ok[u][j] ? acc[e0 + j] : 0.0f;
+                    const unsigned key = key_of(v[u][j]);
+                    const unsigned bin = key >> H1_SHIFT;
+                    cap[u][j] = ok[u][j] && bin >= b1;
+                    if (ok[u][j] && bin == b1) atomicAdd(&h[(key >> H2_SHIFT) & (H2_BINS - 1)], 1u);
                 }
             }
+            running += append_chunks<4, 4>(cap, v, e0, running, sidx, sval, s_cnt, parity);
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const long long e0 = sbase + u * (TK_THREADS * 4) + threadIdx.x * 4;
-            bool cap[4];
-            unsigned before = 0, wtot = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const unsigned key = key_of(v[u][j]);
-                const unsigned bin = key >> H1_SHIFT;
-                cap[j] = ok[u][j] && bin >= b1;
-                if (ok[u][j] && bin == b1) atomicAdd(&h[(key >> H2_SHIFT) & (H2_BINS - 1)], 1u);
-                const unsigned long long bal = __ballot(cap[j]);
-                before += __popcll(bal & lt);
-                wtot += __popcll(bal);
-            }
-            if (lane == 0) s_wave[parity][w] = wtot;
-            __syncthreads();
-            unsigned wbefore = 0, ctot = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const unsigned t = s_wave[parity][i];
-                wbefore += (i < w) ? t : 0u;
-                ctot += t;
-            }
-            parity ^= 1;
-            unsigned pos = running + wbefore + before;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (cap[j]) {
-                    sidx[pos] = static_cast<int>(e0 + j);
-                    sval[pos] = v[u][j];
-                    ++pos;
-                }
-            }
-            running += ctot;
-        }
+        if (threadIdx.x == 0) tile_cnt[blockIdx.x] = running;
     }
-    if (threadIdx.x == 0) tile_cnt[blockIdx.x] = running;
     __syncthreads();
     unsigned* dst = hist2 + (blockIdx.x % NCOPY) * H2_BINS;
     for (int i = threadIdx.x; i < H2_BINS; i += TK_THREADS) {
@@ -323,7 +459,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_select2(const unsigned* __res
     __shared__ unsigned s_tmp[4];
     __shared__ unsigned s_bin, s_above;
     const unsigned above1 = st->above1;
-    select_bin_256<H2_BINS, NCOPY>(hist2, H2_BINS, k - above1, s_h, s_tmp, &s_bin, &s_above);
+    select_bin<H2_BINS, NCOPY>(hist2, H2_BINS, k - above1, s_h, s_tmp, &s_bin, &s_above);
     if (threadIdx.x == 0) {
         st->prefix2 = (st->b1 << 12) | s_bin;
         st->above2 = above1 + s_above;
@@ -352,29 +488,36 @@ __global__ __launch_bounds__(TK_THREADS) void topk_refine(
     }
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_select3(const unsigned* __restrict__ hist3, unsigned k,
-                                                           TopkState* __restrict__ st) {
+// Tiles [b n / G, (b+1) n / G) of workgroup b of G (the same partition in
+// topk_count and topk_emit).
+__device__ __forceinline__ int tile_lo(int b, int g, int ntiles) {
+    return static_cast<int>(static_cast<long long>(b) * ntiles / g);
+}
+
+// Every workgroup finds the threshold key T from the level-3 histogram (128
+// bins); workgroup 0 records it.  Then per tile of the workgroup's range:
+// #(key > T), #(key == T), and the range totals.
+__global__ __launch_bounds__(TK_THREADS) void topk_count(
+        TopkState* __restrict__ st, const unsigned* __restrict__ hist3, unsigned k,
+        const float* __restrict__ slot_val, const unsigned* __restrict__ tile_cnt, int ntiles,
+        unsigned* __restrict__ wg_gt, unsigned* __restrict__ wg_eq) {
+    __shared__ unsigned s_red[8];
     __shared__ unsigned s_h[H3_BINS];
     __shared__ unsigned s_tmp[4];
     __shared__ unsigned s_bin, s_above;
-    const unsigned above2 = st->above2;
-    select_bin_256<H3_BINS, 1>(hist3, H3_BINS, k - above2, s_h, s_tmp, &s_bin, &s_above);
-    if (threadIdx.x == 0) {
+    const unsigned above2 = st->above2, prefix2 = st->prefix2;
+    select_bin<H3_BINS, 1>(hist3, H3_BINS, k - above2, s_h, s_tmp, &s_bin, &s_above);
+    const unsigned thr = (prefix2 << H2_SHIFT) | s_bin;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         const unsigned above3 = above2 + s_above;
-        st->thr = (st->prefix2 << H2_SHIFT) | s_bin;
+        st->thr = thr;
         st->above3 = above3;
         st->need = k - above3;
     }
-}
-
-__global__ __launch_bounds__(TK_THREADS) void topk_count(
-        const TopkState* __restrict__ st, const float* __restrict__ slot_val,
-        const unsigned* __restrict__ tile_cnt, int ntiles, unsigned* __restrict__ tile_gt,
-        unsigned* __restrict__ tile_eq) {
-    __shared__ unsigned s_red[8];
-    const unsigned thr = st->thr;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int t0 = tile_lo(blockIdx.x, gridDim.x, ntiles), t1 = tile_lo(blockIdx.x + 1, gridDim.x, ntiles);
+    unsigned rgt = 0, req = 0;
+    for (int t = t0; t < t1; ++t) {
         const unsigned cnt = tile_cnt[t];
         const float* sv = slot_val + static_cast<long long>(t) * TK_TILE;
         unsigned gt = 0, eq = 0;
@@ -390,62 +533,47 @@ __global__ __launch_bounds__(TK_THREADS) void topk_count(
             s_red[4 + w] = eq;
         }
         __syncthreads();
-        if (threadIdx.x == 0) {
-            tile_gt[t] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-            tile_eq[t] = s_red[4] + s_red[5] + s_red[6] + s_red[7];
-        }
+        rgt += s_red[0] + s_red[1] + s_red[2] + s_red[3];
+        req += s_red[4] + s_red[5] + s_red[6] + s_red[7];
         __syncthreads();
     }
-}
-
-constexpr int SCAN_THREADS = 1024;
-
-__global__ __launch_bounds__(SCAN_THREADS) void topk_scan(
-        const TopkState* __restrict__ st, const unsigned* __restrict__ tile_gt,
-        const unsigned* __restrict__ tile_eq, int ntiles, unsigned* __restrict__ eq_before,
-        unsigned* __restrict__ out_off) {
-    __shared__ unsigned s_tmp[SCAN_THREADS / 64];
-    const unsigned need = st->need;
-    const int per = (ntiles + SCAN_THREADS - 1) / SCAN_THREADS;
-    const int lo = min(ntiles, static_cast<int>(threadIdx.x) * per);
-    const int hi = min(ntiles, lo + per);
-    unsigned s_eq = 0;
-    for (int t = lo; t < hi; ++t) s_eq += tile_eq[t];
-    unsigned total;
-    unsigned eqb = block_inclusive_scan<SCAN_THREADS / 64>(s_eq, s_tmp, &total) - s_eq;
-    unsigned s_sel = 0;
-    for (int t = lo; t < hi; ++t) {
-        const unsigned e = tile_eq[t];
-        const unsigned take = need > eqb ? min(e, need - eqb) : 0u;
-        eq_before[t] = eqb;
-        eqb += e;
-        s_sel += tile_gt[t] + take;
-    }
-    unsigned off = block_inclusive_scan<SCAN_THREADS / 64>(s_sel, s_tmp, &total) - s_sel;
-    for (int t = lo; t < hi; ++t) {
-        const unsigned e = tile_eq[t];
-        const unsigned eb = eq_before[t];
-        const unsigned take = need > eb ? min(e, need - eb) : 0u;
-        out_off[t] = off;
-        off += tile_gt[t] + take;
+    if (threadIdx.x == 0) {
+        wg_gt[blockIdx.x] = rgt;
+        wg_eq[blockIdx.x] = req;
     }
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_emit(
         const TopkState* __restrict__ st, const int* __restrict__ slot_idx,
         const float* __restrict__ slot_val, const unsigned* __restrict__ tile_cnt,
-        const unsigned* __restrict__ eq_before, const unsigned* __restrict__ out_off, int ntiles,
+        const unsigned* __restrict__ wg_gt, const unsigned* __restrict__ wg_eq, int ntiles,
         unsigned k, int* __restrict__ out_idx, float* __restrict__ out_val, float* __restrict__ mem) {
     __shared__ unsigned s_eq[4], s_sel[4];
     const unsigned thr = st->thr;
     const unsigned need = st->need;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const unsigned long long lt = lanemask_lt();
-    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    // ties and selected entries before this workgroup's tile range: the ties
+    // are taken in index order, so min(need, ties before) of them precede it
+    unsigned pgt = 0, peq = 0;
+    for (int b = threadIdx.x; b < static_cast<int>(blockIdx.x); b += TK_THREADS) {
+        pgt += wg_gt[b];
+        peq += wg_eq[b];
+    }
+    pgt = wave_sum(pgt);
+    peq = wave_sum(peq);
+    if (lane == 0) {
+        s_eq[w] = pgt;
+        s_sel[w] = peq;
+    }
+    __syncthreads();
+    unsigned eqr = ((s_sel[0] + s_sel[1]) + s_sel[2]) + s_sel[3];
+    unsigned off = (((s_eq[0] + s_eq[1]) + s_eq[2]) + s_eq[3]) + min(need, eqr);
+    __syncthreads();
+    const int t0 = tile_lo(blockIdx.x, gridDim.x, ntiles), t1 = tile_lo(blockIdx.x + 1, gridDim.x, ntiles);
+    for (int t = t0; t < t1; ++t) {
         const unsigned cnt = tile_cnt[t];
         const long long sbase = static_cast<long long>(t) * TK_TILE;
-        unsigned eqr = eq_before[t];
-        unsigned off = out_off[t];
         for (unsigned c0 = 0; c0 < cnt; c0 += TK_THREADS) {
             const unsigned e = c0 + threadIdx.x;
             const bool valid = e < cnt;
@@ -552,6 +680,18 @@ __global__ __launch_bounds__(256) void topk_decode_add(
     }
 }
 
+// Rank (from the top, among the sampled entries) whose level-1 bin edge is
+// taken as the capture guess: the expected sample count above the threshold
+// plus 25%, four standard deviations and 16, so that a sampled guess above
+// the true threshold is practically impossible (it would only cost the
+// re-reading capture pass).  >= the sample count: capture everything.
+unsigned guess_rank(long long d, long long k) {
+    const double S = static_cast<double>(d < SAMPLES ? d : SAMPLES);
+    const double mean = S * static_cast<double>(k) / static_cast<double>(d);
+    const double r = std::ceil(1.25 * mean + 4.0 * std::sqrt(mean) + 16.0);
+    return r >= S ? static_cast<unsigned>(S) : static_cast<unsigned>(r);
+}
+
 }  // namespace
 }  // namespace gc
 
@@ -593,10 +733,8 @@ int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, f
     auto* hist2 = reinterpret_cast<unsigned*>(w + L.hist2);
     auto* hist3 = reinterpret_cast<unsigned*>(w + L.hist3);
     auto* tile_cnt = reinterpret_cast<unsigned*>(w + L.tile_cnt);
-    auto* tile_gt = reinterpret_cast<unsigned*>(w + L.tile_gt);
-    auto* tile_eq = reinterpret_cast<unsigned*>(w + L.tile_eq);
-    auto* eq_before = reinterpret_cast<unsigned*>(w + L.eq_before);
-    auto* out_off = reinterpret_cast<unsigned*>(w + L.out_off);
+    auto* wg_gt = reinterpret_cast<unsigned*>(w + L.wg_gt);
+    auto* wg_eq = reinterpret_cast<unsigned*>(w + L.wg_eq);
     auto* slot_idx = reinterpret_cast<int*>(w + L.slot_idx);
     auto* slot_val = reinterpret_cast<float*>(w + L.slot_val);
     const int ntiles = static_cast<int>(L.ntiles);
@@ -605,16 +743,24 @@ int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, f
     int rc;
 
     {
-        TimedLaunch tl("topk_init", s);
-        topk_init<<<INIT_BLOCKS, 256, 0, s>>>(reinterpret_cast<uint4*>(w), static_cast<int>(L.zero_bytes / 16));
-        if ((rc = check_launch("topk_init")) != GC_OK) return rc;
+        TimedLaunch tl("topk_prep", s);
+        const unsigned rank_g = guess_rank(d, k);
+        uint4* zero = reinterpret_cast<uint4*>(w + L.zero_from);
+        const int n16 = static_cast<int>((L.zero_end - L.zero_from) / 16);
+        if (grad_dtype == GC_BF16)
+            topk_prep<true><<<1 + PREP_ZERO_BLOCKS, PREP_THREADS, 0, s>>>(grad, mem, d, eta, rank_g, st, zero, n16);
+        else
+            topk_prep<false><<<1 + PREP_ZERO_BLOCKS, PREP_THREADS, 0, s>>>(grad, mem, d, eta, rank_g, st, zero, n16);
+        if ((rc = check_launch("topk_prep")) != GC_OK) return rc;
     }
     {
         TimedLaunch tl("topk_accum_hist", s);
         if (grad_dtype == GC_BF16)
-            topk_accum_hist<true><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, hist1);
+            topk_accum_hist<true><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx, slot_val,
+                                                                tile_cnt);
         else
-            topk_accum_hist<false><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, hist1);
+            topk_accum_hist<false><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx, slot_val,
+                                                                 tile_cnt);
         if ((rc = check_launch("topk_accum_hist")) != GC_OK) return rc;
     }
     {
@@ -638,23 +784,13 @@ int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, f
         if ((rc = check_launch("topk_refine")) != GC_OK) return rc;
     }
     {
-        TimedLaunch tl("topk_select3", s);
-        topk_select3<<<1, TK_THREADS, 0, s>>>(hist3, ku, st);
-        if ((rc = check_launch("topk_select3")) != GC_OK) return rc;
-    }
-    {
         TimedLaunch tl("topk_count", s);
-        topk_count<<<small_grid, TK_THREADS, 0, s>>>(st, slot_val, tile_cnt, ntiles, tile_gt, tile_eq);
+        topk_count<<<small_grid, TK_THREADS, 0, s>>>(st, hist3, ku, slot_val, tile_cnt, ntiles, wg_gt, wg_eq);
         if ((rc = check_launch("topk_count")) != GC_OK) return rc;
     }
     {
-        TimedLaunch tl("topk_scan", s);
-        topk_scan<<<1, SCAN_THREADS, 0, s>>>(st, tile_gt, tile_eq, ntiles, eq_before, out_off);
-        if ((rc = check_launch("topk_scan")) != GC_OK) return rc;
-    }
-    {
         TimedLaunch tl("topk_emit", s);
-        topk_emit<<<small_grid, TK_THREADS, 0, s>>>(st, slot_idx, slot_val, tile_cnt, eq_before, out_off,
+        topk_emit<<<small_grid, TK_THREADS, 0, s>>>(st, slot_idx, slot_val, tile_cnt, wg_gt, wg_eq,
                                                     ntiles, ku, out_idx, out_val, mem);
         if ((rc = check_launch("topk_emit")) != GC_OK) return rc;
     }
