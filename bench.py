@@ -1,6 +1,6 @@
 """Benchmark: gradient GB/s through encode + decode + error feedback on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c2|c3|c4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c2|c3|c3acc|c4]
 
 A step is one pass of the whole compressor hot path over one gradient set:
   c5 (default): BERT-large gradient set (bf16 grads, fp32 memory):
@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c3acc", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", action="store_true", help="write 1 GiB between timed steps (cold Infinity Cache)")
     ap.add_argument("--copy-calib", action="store_true", help="only run a 1 GiB device copy (counter calibration)")
@@ -243,6 +243,61 @@ class C3(Workload):
         self.gc.gc_topk_decode(self.idx, self.val, self.out)
 
 
+class C3Acc(Workload):
+    """Accordion on top-k: the 25.6M vector with a norm trajectory; the norm is
+    checked every 10 steps and picks k = 1% (l_low) or 0.1% (l_high)."""
+    name = "c3acc"
+
+    def __init__(self, torch, gc, dev):
+        self.torch, self.gc, self.dev = torch, gc, dev
+        d = self.d = gen.C3_D
+        self.k_low, self.k_high = gen.acc_topk_ks(d)
+        self.base = [torch.from_numpy(gen.acc_topk_base(s, d)).to(dev) for s in range(2)]
+        self.g = {}
+        self.mem = torch.zeros(d, device=dev)
+        self.out = torch.zeros(d, device=dev)
+        self.idx = torch.empty(self.k_low, dtype=torch.int32, device=dev)
+        self.val = torch.empty(self.k_low, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(max(gc.gc_topk_workspace_bytes(d, self.k_low), gc.gc_topk_workspace_bytes(d, self.k_high)),
+                              dtype=torch.uint8, device=dev)
+        self.norms = torch.empty(1, device=dev)
+        self.nws = torch.empty(gc.gc_grad_norm_workspace_bytes([self.base[0]]), dtype=torch.uint8, device=dev)
+        self.prev = np.zeros(1, np.float32)
+        self.k = self.k_low
+        self.ks = []
+        self.grad_bytes = 4 * d
+        self.kernel_bytes = {"topk_accum_hist": 12 * d, "topk_decode_set": 4 * d + 8 * self.k_low,
+                             "norm_partial": 4 * d / 10.0}
+        self.description = gen.WORKLOADS["c3acc"].description
+        self.config = {"workload": "resnet50-sized flat gradient, accordion top-k", "params": d,
+                       "levels": f"l_low=k {self.k_low} (1%), l_high=k {self.k_high} (0.1%)",
+                       "grad_dtype": "f32", "memory_dtype": "f32", "eta": 1.0, "accordion_check_every": 10}
+
+    def prepare(self, tmax):
+        # the scaled gradient of every step the run uses, made on the device before timing
+        for t in range(tmax):
+            self.g[t] = self.base[t % 2] * float(gen.acc_topk_scale(t))
+
+    def timed_begin(self):
+        self.ks = []
+
+    @property
+    def alg_bytes(self):
+        ks = self.ks or [self.k_low]
+        kavg = sum(ks) / len(ks)
+        return 16 * self.d + 16 * kavg + 4 * self.d / 10.0
+
+    def step(self, t):
+        gc, g = self.gc, self.g[t]
+        if t % 10 == 0:
+            gc.gc_grad_norm([g], self.norms, self.nws)
+            lv, self.prev = gc.gc_accordion_select(self.norms.cpu().numpy(), self.prev, gen.C4_THRESHOLD, t > 0)
+            self.k = self.k_low if lv[0] == gc.GC_LEVEL_LOW else self.k_high
+        self.ks.append(self.k)
+        gc.gc_topk_ef_encode(g, self.mem, 1.0, self.k, self.idx[:self.k], self.val[:self.k], self.ws)
+        gc.gc_topk_decode(self.idx[:self.k], self.val[:self.k], self.out)
+
+
 class C4(Workload):
     name = "c4"
 
@@ -308,7 +363,7 @@ def cpu_baseline(name):
                     oracle.powersgd_ef_step(g.reshape(n, m), np.zeros((n, m), np.float32), q[l], 1.0, 4)
                 r = oracle.topk_ef_step(np.zeros(emb.size, np.float32), emb, 1.0, ek)
                 oracle.topk_decode(r["idx"], r["val"], emb.size)
-        elif name == "c3":
+        elif name in ("c3", "c3acc"):
             g = gen.c3_grad(0)[:2_560_000]
             k = int(0.01 * g.size)
             sample = "first 2.56M entries of the ResNet-50-sized gradient, top-k 1% EF"
@@ -396,7 +451,9 @@ def main():
         return
 
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
-    W = {"c5": C5, "c2": C2, "c3": C3, "c4": C4}[args.workload](torch, gc, dev)
+    W = {"c5": C5, "c2": C2, "c3": C3, "c3acc": C3Acc, "c4": C4}[args.workload](torch, gc, dev)
+    if hasattr(W, "prepare"):
+        W.prepare(args.warmup + args.steps + 2)
     torch.cuda.synchronize()
     flush_buf = torch.empty(1 << 28, device=dev) if args.flush else None
 
@@ -418,6 +475,8 @@ def main():
 
     print(f"[bench] timing {args.steps} steps (dominant kernel {dominant})", file=sys.stderr, flush=True)
     gc.gc_timing_enable(dominant)
+    if hasattr(W, "timed_begin"):
+        W.timed_begin()
     torch.cuda.synchronize()
     if args.flush:
         total_ms = 0.0

@@ -40,6 +40,7 @@ CFG_C2 = 2
 CFG_C3 = 3
 CFG_C4 = 4
 CFG_C5 = 5
+CFG_ACC_TOPK = 6    # Accordion on top-k (the C3 vector with a norm trajectory)
 
 
 def rng(config: int, kind: int, step: int = 0, layer: int = 0) -> np.random.Generator:
@@ -175,6 +176,35 @@ def c4_grads(step: int) -> list[np.ndarray]:
 
 
 # --------------------------------------------------------------------------
+# Accordion on top-k: the C3 vector shape with a norm trajectory
+# --------------------------------------------------------------------------
+
+ACC_TOPK_JUMP = (15, 25)           # scale x4 on [15, 25): one up jump, one down jump
+ACC_TOPK_FRACTIONS = (0.01, 0.001)  # k / d at l_low (critical: low compression) and l_high
+
+
+def acc_topk_scale(t: int) -> float:
+    """Trajectory factor exp(-t/200) * J(t); J = 4 on [15, 25), else 1."""
+    j = 4.0 if ACC_TOPK_JUMP[0] <= t < ACC_TOPK_JUMP[1] else 1.0
+    return math.exp(-t / 200.0) * j
+
+
+def acc_topk_ks(d: int) -> tuple[int, int]:
+    """(k at l_low, k at l_high) = floor(fraction * d), at least 1."""
+    return tuple(max(1, int(math.floor(f * d))) for f in ACC_TOPK_FRACTIONS)
+
+
+def acc_topk_base(step: int, d: int) -> np.ndarray:
+    """Unscaled draw of step `step`: 1e-3 * Student-t(3), float32."""
+    t = rng(CFG_ACC_TOPK, KIND_GRAD, step).standard_t(3.0, size=d)
+    return (t * 1e-3).astype(np.float32)
+
+
+def acc_topk_grad(step: int, d: int) -> np.ndarray:
+    return (acc_topk_base(step, d) * np.float32(acc_topk_scale(step))).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
 # C5: BERT-large bf16 gradient set
 # --------------------------------------------------------------------------
 
@@ -221,5 +251,6 @@ WORKLOADS = {
     "c2": Workload("c2", "ResNet-18 (CIFAR-100) gradient set, 21 matrices, PowerSGD EF rank 1/2"),
     "c3": Workload("c3", "ResNet-50-sized flat fp32 gradient d=25.6M, Student-t(3)*1e-3, top-k EF k=0.1%/1%"),
     "c4": Workload("c4", "VGG-19 (CIFAR-100) gradient set, Accordion PowerSGD rank 4/2, checks every 10 steps"),
+    "c3acc": Workload("c3acc", "ResNet-50-sized flat fp32 gradient d=25.6M with a norm trajectory, Accordion top-k EF: k=1% (l_low) / 0.1% (l_high), checks every 10 steps"),
     "c5": Workload("c5", "BERT-large gradient set: 144 matrices PowerSGD EF rank 4 + 30522x1024 embedding top-k 1% EF, bf16 grads, fp32 memory"),
 }

@@ -94,3 +94,29 @@ def test_c4_schedule_on_sampled_layers():
             lows.append(t)
         prev = newp
     assert lows == gold["low_checks"]
+
+
+def test_accordion_topk_schedule_closed_form():
+    """Accordion on top-k (oracle only): the norm trajectory gives the closed-form
+    schedule, and each step's top-k takes the k of the level chosen at the last check."""
+    gold = json.load(open(os.path.join(GOLD, "acc_topk_schedule.json")))
+    d = 1 << 18
+    k_low, k_high = gen.acc_topk_ks(d)
+    assert (k_low, k_high) == (int(d * gold["k_fraction_low"]), int(d * gold["k_fraction_high"]))
+    prev = np.zeros(1, np.float32)
+    low, high = [], []
+    mem = np.zeros(d, np.float32)
+    k = None
+    for t in range(gold["steps"]):
+        g = gen.acc_topk_grad(t, d)
+        if t % gold["check_every"] == 0:
+            norm = np.array([oracle.grad_norm(g)], np.float32)
+            lv, prev = oracle.accordion_select(norm, prev, t > 0, gold["threshold"])
+            (low if lv[0] == oracle.LEVEL_LOW else high).append(t)
+            k = k_low if lv[0] == oracle.LEVEL_LOW else k_high
+        if t in (0, 10, 20):   # a few full steps: k pairs, memory invariant
+            r = oracle.topk_ef_step(mem, g, 1.0, k)
+            assert r["idx"].size == k and np.count_nonzero(r["g"]) == k
+            assert np.array_equal((r["mem"] + r["g"]).view(np.uint32), r["acc"].view(np.uint32))
+            mem = r["mem"]
+    assert low == gold["low_checks"] and high == gold["high_checks"]
