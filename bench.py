@@ -1,6 +1,6 @@
 """Benchmark: gradient GB/s through encode + decode + error feedback on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c2|c3|c3acc|c4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c2|c3|c3acc|c3randk|c4]
 
 A step is one pass of the whole compressor hot path over one gradient set:
   c5 (default): BERT-large gradient set (bf16 grads, fp32 memory):
@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c3acc", "c4", "c5"])
+    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c3acc", "c3randk", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", action="store_true", help="write 1 GiB between timed steps (cold Infinity Cache)")
     ap.add_argument("--copy-calib", action="store_true", help="only run a 1 GiB device copy (counter calibration)")
@@ -243,6 +243,33 @@ class C3(Workload):
         self.gc.gc_topk_decode(self.idx, self.val, self.out)
 
 
+class C3Randk(Workload):
+    """Rand-k with memory on the 25.6M vector: k = 1%, seeded subsets (two
+    gradient/subset pairs alternate)."""
+    name = "c3randk"
+
+    def __init__(self, torch, gc, dev):
+        self.gc = gc
+        d = gen.C3_D
+        self.k = k = d // 100
+        self.g = [torch.from_numpy(gen.c3_grad(s)).to(dev) for s in range(2)]
+        self.idx = [torch.from_numpy(gen.randk_indices(gen.CFG_C3, s, d, k)).to(dev) for s in range(2)]
+        self.mem = torch.zeros(d, device=dev)
+        self.out = torch.zeros(d, device=dev)
+        self.val = torch.empty(k, dtype=torch.float32, device=dev)
+        self.grad_bytes = 4 * d
+        self.alg_bytes = 16 * d + 16 * k
+        self.kernel_bytes = {"randk_encode": 12 * d + 8 * k, "topk_decode_set": 4 * d + 8 * k}
+        self.description = gen.WORKLOADS["c3randk"].description
+        self.config = {"workload": "resnet50-sized flat gradient, rand-k", "params": d, "randk_k": k,
+                       "grad_dtype": "f32", "memory_dtype": "f32", "eta": 1.0}
+
+    def step(self, t):
+        s = t % 2
+        self.gc.gc_randk_ef_encode(self.g[s], self.mem, 1.0, self.idx[s], self.val)
+        self.gc.gc_topk_decode(self.idx[s], self.val, self.out)
+
+
 class C3Acc(Workload):
     """Accordion on top-k: the 25.6M vector with a norm trajectory; the norm is
     checked every 10 steps and picks k = 1% (l_low) or 0.1% (l_high)."""
@@ -363,6 +390,15 @@ def cpu_baseline(name):
                     oracle.powersgd_ef_step(g.reshape(n, m), np.zeros((n, m), np.float32), q[l], 1.0, 4)
                 r = oracle.topk_ef_step(np.zeros(emb.size, np.float32), emb, 1.0, ek)
                 oracle.topk_decode(r["idx"], r["val"], emb.size)
+        elif name == "c3randk":
+            g = gen.c3_grad(0)[:2_560_000]
+            idx = gen.randk_indices(gen.CFG_C3, 0, g.size, g.size // 100)
+            sample = "first 2.56M entries of the ResNet-50-sized gradient, rand-k 1% EF"
+            nbytes = 4 * g.size
+
+            def run():
+                r = oracle.randk_ef_step(np.zeros(g.size, np.float32), g, 1.0, idx)
+                oracle.topk_decode(r["idx"], r["val"], g.size)
         elif name in ("c3", "c3acc"):
             g = gen.c3_grad(0)[:2_560_000]
             k = int(0.01 * g.size)
@@ -417,7 +453,7 @@ def traffic_from_profiles(kernel, workload, src_hash):
 
 
 def kernel_source_hash(kernel):
-    fname = "powersgd.hip" if kernel.startswith("psgd") else "norm.hip" if kernel.startswith("norm") else "topk.hip"
+    fname = "powersgd.hip" if kernel.startswith("psgd") else "norm.hip" if kernel.startswith("norm") else "topk.hip"   # randk_* is in topk.hip
     p = os.path.join(ROOT, "gradient_compression_error_amd", "csrc", fname)
     h = hashlib.sha256(open(p, "rb").read())
     h.update(open(os.path.join(ROOT, "gradient_compression_error_amd", "csrc", "gc_common.h"), "rb").read())
@@ -451,7 +487,7 @@ def main():
         return
 
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
-    W = {"c5": C5, "c2": C2, "c3": C3, "c3acc": C3Acc, "c4": C4}[args.workload](torch, gc, dev)
+    W = {"c5": C5, "c2": C2, "c3": C3, "c3acc": C3Acc, "c3randk": C3Randk, "c4": C4}[args.workload](torch, gc, dev)
     if hasattr(W, "prepare"):
         W.prepare(args.warmup + args.steps + 2)
     torch.cuda.synchronize()

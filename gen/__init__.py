@@ -224,6 +224,13 @@ def c5_embedding_bf16(set_id: int) -> np.ndarray:
 # Small structured inputs for edge cases
 # --------------------------------------------------------------------------
 
+def randk_indices(config: int, step: int, d: int, k: int) -> np.ndarray:
+    """The rand-k draw of one step: k distinct coordinates of [0, d), uniform,
+    sorted ascending (int32)."""
+    r = rng(config, KIND_MISC, step, 777)
+    return np.sort(r.choice(d, size=k, replace=False)).astype(np.int32)
+
+
 def tie_heavy(d: int, seed_layer: int, levels: int = 6) -> np.ndarray:
     """Values in {+-0.25*j : j = 0..levels-1}: many exact magnitude ties."""
     r = rng(0, KIND_MISC, 0, seed_layer)
@@ -250,6 +257,7 @@ WORKLOADS = {
     "c1": Workload("c1", "Mem-SGD top-k tiny: fp32 d=10,000, k=100, eta=0.1, 10 steps"),
     "c2": Workload("c2", "ResNet-18 (CIFAR-100) gradient set, 21 matrices, PowerSGD EF rank 1/2"),
     "c3": Workload("c3", "ResNet-50-sized flat fp32 gradient d=25.6M, Student-t(3)*1e-3, top-k EF k=0.1%/1%"),
+    "c3randk": Workload("c3randk", "ResNet-50-sized flat fp32 gradient d=25.6M, Student-t(3)*1e-3, rand-k EF k=1% (seeded subsets)"),
     "c4": Workload("c4", "VGG-19 (CIFAR-100) gradient set, Accordion PowerSGD rank 4/2, checks every 10 steps"),
     "c3acc": Workload("c3acc", "ResNet-50-sized flat fp32 gradient d=25.6M with a norm trajectory, Accordion top-k EF: k=1% (l_low) / 0.1% (l_high), checks every 10 steps"),
     "c5": Workload("c5", "BERT-large gradient set: 144 matrices PowerSGD EF rank 4 + 30522x1024 embedding top-k 1% EF, bf16 grads, fp32 memory"),

@@ -54,6 +54,7 @@ _sig("gc_last_error", C.c_char_p)
 _sig("gc_topk_workspace_bytes", _sz, _i64, _i64)
 _sig("gc_topk_ef_encode", _i32, _vp, _i32, _vp, _i64, _f32, _i64, _vp, _vp, _vp, _sz, _vp)
 _sig("gc_topk_decode", _i32, _vp, _vp, _i64, _vp, _i64, _i32, _vp)
+_sig("gc_randk_ef_encode", _i32, _vp, _i32, _vp, _i64, _f32, _vp, _i64, _vp, _vp)
 _sig("gc_powersgd_workspace_bytes", _sz, C.POINTER(gc_mat), _i32)
 _sig("gc_powersgd_ef_step", _i32, C.POINTER(gc_mat), _i32, _i32, _f32, _vp, _sz, _vp)
 _sig("gc_grad_norm_workspace_bytes", _sz, C.POINTER(gc_span), _i32)
@@ -65,7 +66,7 @@ _sig("gc_timing_read", _i32, C.POINTER(C.c_double), C.POINTER(C.c_int64))
 _sig("gc_kernel_names", C.c_char_p)
 
 EXPORTED = ["gc_status_str", "gc_last_error", "gc_topk_workspace_bytes", "gc_topk_ef_encode",
-            "gc_topk_decode", "gc_powersgd_workspace_bytes", "gc_powersgd_ef_step",
+            "gc_topk_decode", "gc_randk_ef_encode", "gc_powersgd_workspace_bytes", "gc_powersgd_ef_step",
             "gc_grad_norm_workspace_bytes", "gc_grad_norm", "gc_accordion_select",
             "gc_timing_enable", "gc_timing_read", "gc_kernel_names"]
 
@@ -136,6 +137,12 @@ def gc_topk_ef_encode(grad, mem, eta: float, k: int, out_idx, out_val, ws, strea
     _check(lib.gc_topk_ef_encode(_ptr(grad), _dtype_code(grad), _ptr(mem), mem.numel(), float(eta), int(k),
                                  _ptr(out_idx), _ptr(out_val), _ptr(ws), _nbytes(ws), _stream(stream)),
            "gc_topk_ef_encode")
+
+
+def gc_randk_ef_encode(grad, mem, eta: float, idx, out_val, stream=None) -> None:
+    """Rand-k EF step on the given ascending index subset; k = idx.numel()."""
+    _check(lib.gc_randk_ef_encode(_ptr(grad), _dtype_code(grad), _ptr(mem), mem.numel(), float(eta), _ptr(idx),
+                                  idx.numel(), _ptr(out_val), _stream(stream)), "gc_randk_ef_encode")
 
 
 def gc_topk_decode(idx, val, out, accumulate: bool = False, stream=None) -> None:

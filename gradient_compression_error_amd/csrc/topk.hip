@@ -680,6 +680,65 @@ __global__ __launch_bounds__(256) void topk_decode_add(
     }
 }
 
+// ---------------------------------------------------------------- rand-k
+
+// Rand-k with memory ("Sparsified SGD with Memory", method section): comp_k
+// keeps k given coordinates.  One workgroup per RK_TILE entries: acc of the
+// tile into LDS, the tile's slice of the (ascending) index list found by two
+// wave searches, the selected values read out and zeroed in LDS, then the
+// memory written once.  Indices outside [0, d) fall in no tile's slice.
+constexpr int RK_TILE = 4096;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void randk_encode(const void* __restrict__ grad, float* __restrict__ mem, long long d,
+                                                    float eta, const int* __restrict__ idx, long long k,
+                                                    float* __restrict__ out_val) {
+    __shared__ float4 s_acc4[RK_TILE / 4];
+    __shared__ long long s_range[2];
+    float* const s_acc = reinterpret_cast<float*>(s_acc4);
+    const int t = threadIdx.x;
+    const long long lo = static_cast<long long>(blockIdx.x) * RK_TILE;
+    const long long hi = min(d, lo + RK_TILE);
+    const int n = static_cast<int>(hi - lo);
+    if (t < 64) {
+        const long long a = wave_lower_bound(idx, k, lo);
+        const long long b = wave_lower_bound(idx, k, hi);
+        if (t == 0) {
+            s_range[0] = a;
+            s_range[1] = b;
+        }
+    }
+    if (n == RK_TILE) {
+        float4 g[4], m[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const long long i4 = lo / 4 + u * 256 + t;
+            g[u] = load_grad4<BF16>(grad, i4);
+            m[u] = reinterpret_cast<const float4*>(mem)[i4];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            s_acc4[u * 256 + t] = make_float4(ef_acc(m[u].x, eta, g[u].x), ef_acc(m[u].y, eta, g[u].y),
+                                              ef_acc(m[u].z, eta, g[u].z), ef_acc(m[u].w, eta, g[u].w));
+    } else {
+        for (int e = t; e < n; e += 256) s_acc[e] = ef_acc(mem[lo + e], eta, load_grad1<BF16>(grad, lo + e));
+    }
+    __syncthreads();
+    const long long a = s_range[0], b = s_range[1];
+    for (long long j = a + t; j < b; j += 256) {
+        const int e = static_cast<int>(idx[j] - lo);
+        out_val[j] = s_acc[e];
+        s_acc[e] = 0.0f;
+    }
+    __syncthreads();
+    if (n == RK_TILE) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) reinterpret_cast<float4*>(mem)[lo / 4 + u * 256 + t] = s_acc4[u * 256 + t];
+    } else {
+        for (int e = t; e < n; e += 256) mem[lo + e] = s_acc[e];
+    }
+}
+
 // Rank (from the top, among the sampled entries) whose level-1 bin edge is
 // taken as the capture guess: the expected sample count above the threshold
 // plus 25%, four standard deviations and 16, so that a sampled guess above
@@ -820,6 +879,30 @@ int gc_topk_decode(const int32_t* idx, const float* val, int64_t k, float* out, 
     const long long blocks = (d + DEC_TILE - 1) / DEC_TILE;
     topk_decode_set<<<static_cast<unsigned>(blocks), 256, 0, s>>>(idx, val, k, out, d);
     return check_launch("topk_decode_set");
+}
+
+int gc_randk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, float eta,
+                       const int32_t* idx, int64_t k, float* out_val, void* stream) {
+    if (!grad || !mem || !idx || !out_val) return fail(GC_ERR_ARG, "gc_randk_ef_encode: null pointer argument");
+    if (grad_dtype != GC_F32 && grad_dtype != GC_BF16)
+        return fail(GC_ERR_DTYPE, "gc_randk_ef_encode: grad_dtype must be GC_F32 or GC_BF16");
+    if (d < 1 || d > INT32_MAX) return fail(GC_ERR_ARG, "gc_randk_ef_encode: d must be in [1, INT32_MAX]");
+    if (k < 1 || k > d) return fail(GC_ERR_ARG, "gc_randk_ef_encode: k must be in [1, d]");
+    if (!aligned16(grad) || !aligned16(mem) || !aligned16(idx) || !aligned16(out_val))
+        return fail(GC_ERR_ARG, "gc_randk_ef_encode: device pointers must be 16-byte aligned");
+    const size_t gbytes = static_cast<size_t>(d) * (grad_dtype == GC_BF16 ? 2 : 4);
+    const size_t mbytes = static_cast<size_t>(d) * 4, kbytes = static_cast<size_t>(k) * 4;
+    if (overlaps(out_val, kbytes, mem, mbytes) || overlaps(out_val, kbytes, grad, gbytes) ||
+        overlaps(out_val, kbytes, idx, kbytes) || overlaps(idx, kbytes, mem, mbytes) || overlaps(grad, gbytes, mem, mbytes))
+        return fail(GC_ERR_ARG, "gc_randk_ef_encode: buffers overlap");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TimedLaunch tl("randk_encode", s);
+    const long long blocks = (d + RK_TILE - 1) / RK_TILE;
+    if (grad_dtype == GC_BF16)
+        randk_encode<true><<<static_cast<unsigned>(blocks), 256, 0, s>>>(grad, mem, d, eta, idx, k, out_val);
+    else
+        randk_encode<false><<<static_cast<unsigned>(blocks), 256, 0, s>>>(grad, mem, d, eta, idx, k, out_val);
+    return check_launch("randk_encode");
 }
 
 }  // extern "C"

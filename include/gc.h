@@ -104,6 +104,24 @@ int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, f
 int gc_topk_decode(const int32_t* idx, const float* val, int64_t k, float* out, int64_t d,
                    int accumulate, void* stream);
 
+/* Rand-k sparsification with error-feedback memory ("Sparsified SGD with
+ * Memory", method section: rand-k is the second k-contraction operator beside
+ * top-k).  The caller draws the random subset and passes it in:
+ *     acc = fl32(mem + fl32(eta*grad))          (as in gc_topk_ef_encode)
+ *     out_val[j] = acc[idx[j]];  mem = acc, with mem[idx[j]] = +0.0
+ * The message (idx, out_val) decodes with gc_topk_decode.
+ *   grad      [d] float32 or bf16 (grad_dtype), read only
+ *   mem       [d] float32, in/out
+ *   idx       [k] int32, strictly ascending, within [0, d), read only
+ *   out_val   [k] float32 out
+ * No workspace.  Indices outside [0, d) are never dereferenced (their out_val
+ * entries are not written); an index list that is not strictly ascending gives
+ * unspecified values but no access outside the buffers.
+ * Errors: GC_ERR_ARG (null pointer, d or k out of range, misalignment,
+ * overlapping buffers), GC_ERR_DTYPE, GC_ERR_HIP. */
+int gc_randk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, float eta,
+                       const int32_t* idx, int64_t k, float* out_val, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* PowerSGD rank-r with error feedback                                      */
 /* ------------------------------------------------------------------------ */

@@ -9,8 +9,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 
 Sources (the three review pages):
   * "Sparsified SGD with Memory" (Stich, Cordonnier, Jaggi) -- method section:
-    the memory update of Mem-SGD, the k-contraction operator, the step size
-    eta_t = 8/(mu(a+t)); abstract: "only the most significant entries" (top-k).
+    the memory update of Mem-SGD, the k-contraction operators (top-k, rand-k),
+    the step size eta_t = 8/(mu(a+t)); abstract: the most significant entries
+    (top-k).
   * "Accordion: Adaptive Gradient Communication via Critical Learning Regime
     Identification" -- method section: two compression levels l_low / l_high
     chosen from the rate of change of the gradient norm; works with PowerSGD
@@ -30,6 +31,7 @@ the SGD rate) -- parity unpinned beyond that claim.
 """
 from .topk_ef import (ef_accumulate, grad_to_f64, topk_select, topk_ef_step,
                       topk_decode, magnitude_order)
+from .randk_ef import randk_ef_step
 from .powersgd import orthonormalize_mgs, powersgd_ef_step
 from .norms import grad_norm
 from .accordion import accordion_select, LEVEL_LOW, LEVEL_HIGH
@@ -37,6 +39,6 @@ from .memsgd import run_memsgd, QuadraticProblem
 
 __all__ = [
     "ef_accumulate", "grad_to_f64", "topk_select", "topk_ef_step", "topk_decode",
-    "magnitude_order", "orthonormalize_mgs", "powersgd_ef_step", "grad_norm",
+    "magnitude_order", "randk_ef_step", "orthonormalize_mgs", "powersgd_ef_step", "grad_norm",
     "accordion_select", "LEVEL_LOW", "LEVEL_HIGH", "run_memsgd", "QuadraticProblem",
 ]

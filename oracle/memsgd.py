@@ -39,9 +39,17 @@ def _topk64(v: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
+def _subset64(v: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    out = np.zeros_like(v)
+    out[idx] = v[idx]
+    return out
+
+
 def run_memsgd(prob: QuadraticProblem, x0: np.ndarray, noise: np.ndarray, sigma: float,
-               k: int | None, mu: float, a: float):
+               k: int | None, mu: float, a: float, subsets: np.ndarray | None = None):
     """Run len(noise) steps.  k=None means no compression (vanilla SGD).
+    With ``subsets`` (one row of k coordinates per step) the compressor is
+    rand-k on those coordinates instead of top-k.
 
     Returns (x_T, x_bar_T) where x_bar_T is the uniform average of x_1..x_T.
     """
@@ -52,7 +60,12 @@ def run_memsgd(prob: QuadraticProblem, x0: np.ndarray, noise: np.ndarray, sigma:
         eta = 8.0 / (mu * (a + t))
         grad = prob.grad(x) + sigma * noise[t]
         acc = mem + eta * grad
-        g = acc if k is None else _topk64(acc, k)
+        if k is None:
+            g = acc
+        elif subsets is not None:
+            g = _subset64(acc, subsets[t])
+        else:
+            g = _topk64(acc, k)
         mem = acc - g
         x = x - g
         xsum += x

@@ -113,6 +113,27 @@ def test_topk_validation(gcl):
 
 
 @no_gpu
+def test_randk_validation(gcl):
+    L = gcl.lib
+    A, B, I, V = 0x100000, 0x200000, 0x300000, 0x400000
+
+    def call(grad=A, dt=gcl.GC_F32, mem=B, d=1000, eta=1.0, idx=I, k=10, val=V):
+        return L.gc_randk_ef_encode(grad, dt, mem, d, eta, idx, k, val, None)
+
+    assert call(grad=None) == gcl.GC_ERR_ARG
+    assert call(idx=None) == gcl.GC_ERR_ARG
+    assert call(val=None) == gcl.GC_ERR_ARG
+    assert call(dt=3) == gcl.GC_ERR_DTYPE
+    assert call(d=0) == gcl.GC_ERR_ARG
+    assert call(k=0) == gcl.GC_ERR_ARG
+    assert call(k=1001) == gcl.GC_ERR_ARG
+    assert call(val=B + 32) == gcl.GC_ERR_ARG                 # out_val inside memory
+    assert call(idx=V + 16) == gcl.GC_ERR_ARG                 # idx overlaps out_val
+    assert call(mem=B + 8) == gcl.GC_ERR_ARG                  # misaligned
+    assert "overlap" in gcl.gc_last_error() or "aligned" in gcl.gc_last_error()
+
+
+@no_gpu
 def test_powersgd_validation(gcl):
     L = gcl.lib
 
