@@ -67,6 +67,31 @@ __device__ __forceinline__ float load_grad1(const void* g, long long i) {
     }
 }
 
+// Streaming accesses: data touched once per kernel and not again before far
+// more than the caches hold has gone by (non-temporal hint on the access).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void store_stream(float4* p, float4 v) {
+    __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// load_grad4 with the streaming hint
+template <bool BF16>
+__device__ __forceinline__ float4 load_grad4_stream(const void* g, long long i4) {
+    if constexpr (BF16) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(g) + i4);
+        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+    } else {
+        return load_stream(reinterpret_cast<const float4*>(g) + i4);
+    }
+}
+
 // fl32(m + fl32(eta*g)), two roundings (the library is built with -ffp-contract=off too)
 __device__ __forceinline__ float ef_acc(float m, float eta, float g) {
     return __fadd_rn(m, __fmul_rn(eta, g));

@@ -160,11 +160,13 @@ __device__ __forceinline__ int nstrips_of(int m) {
     return (m + w - 1) / w;
 }
 
-// M values of 4 consecutive entries starting at flat element e (16-byte aligned)
-template <bool BF16>
+// M values of 4 consecutive entries starting at flat element e (16-byte
+// aligned); STREAM: last read of these entries in the step
+template <bool BF16, bool STREAM = false>
 __device__ __forceinline__ float4 load_M4(const PsMat& M, float eta, long long e) {
-    const float4 g = load_grad4<BF16>(M.grad, e / 4);
-    const float4 mm = reinterpret_cast<const float4*>(M.mem)[e / 4];
+    const float4 g = STREAM ? load_grad4_stream<BF16>(M.grad, e / 4) : load_grad4<BF16>(M.grad, e / 4);
+    const float4 mm = STREAM ? load_stream(reinterpret_cast<const float4*>(M.mem) + e / 4)
+                             : reinterpret_cast<const float4*>(M.mem)[e / 4];
     return make_float4(ef_acc(mm.x, eta, g.x), ef_acc(mm.y, eta, g.y), ef_acc(mm.z, eta, g.z),
                        ef_acc(mm.w, eta, g.w));
 }
@@ -174,10 +176,10 @@ __device__ __forceinline__ float load_M1(const PsMat& M, float eta, long long e)
     return ef_acc(M.mem[e], eta, load_grad1<BF16>(M.grad, e));
 }
 
-template <bool BF16, int VEC>
+template <bool BF16, int VEC, bool STREAM = false>
 __device__ __forceinline__ void load_Mv(const PsMat& M, float eta, long long e, float (&v)[VEC]) {
     if constexpr (VEC == 4) {
-        const float4 t = load_M4<BF16>(M, eta, e);
+        const float4 t = load_M4<BF16, STREAM>(M, eta, e);
         v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
     } else {
         v[0] = load_M1<BF16>(M, eta, e);
@@ -710,7 +712,7 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
 #pragma unroll
             for (int u = 0; u < ROW_GROUP; ++u) {
                 const int row = min(i0 + u, r1 - 1);
-                load_Mv<BF16, VEC>(M, eta, static_cast<long long>(row) * m + colc, mv[u]);
+                load_Mv<BF16, VEC, true>(M, eta, static_cast<long long>(row) * m + colc, mv[u]);
             }
 #pragma unroll
             for (int u = 0; u < ROW_GROUP; ++u) {
@@ -743,8 +745,8 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
                     nm[v] = mv[u][v] - sacc;
                 }
                 if constexpr (VEC == 4) {
-                    if (M.out) reinterpret_cast<float4*>(M.out)[e / 4] = make_float4(o[0], o[1], o[2], o[3]);
-                    reinterpret_cast<float4*>(M.mem)[e / 4] = make_float4(nm[0], nm[1], nm[2], nm[3]);
+                    if (M.out) store_stream(reinterpret_cast<float4*>(M.out) + e / 4, make_float4(o[0], o[1], o[2], o[3]));
+                    store_stream(reinterpret_cast<float4*>(M.mem) + e / 4, make_float4(nm[0], nm[1], nm[2], nm[3]));
                 } else {
                     if (M.out) M.out[e] = o[0];
                     M.mem[e] = nm[0];
