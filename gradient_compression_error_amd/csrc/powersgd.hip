@@ -45,6 +45,7 @@ constexpr int Q_ROWS = 32;           // rows per chunk in psgd_q
 constexpr int ROW_GROUP = 8;         // rows whose loads are issued together in psgd_q / psgd_out
 constexpr int QR_PER_THREAD = 16;    // M^T P partials per psgd_qreduce thread before slicing a column
 constexpr int CUS = 256;             // MI355X compute units
+constexpr double STREAM_MIN_BYTES = 1e9;   // psgd_out traffic above which it streams
 constexpr int OUT_GRID_MAX = CUS * 4;   // psgd_out holds 4 workgroups per CU
 
 struct PsMat {
@@ -674,8 +675,10 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
 // ------------------------------------------------------------------ psgd_out
 
 // Rows [r0, r1) of one matrix, one column strip at a time (Q of the strip in
-// registers); loads of ROW_GROUP rows are issued together.
-template <bool BF16, int VEC>
+// registers); loads of ROW_GROUP rows are issued together.  STREAM marks the
+// last reads of mem/grad and the writes of mem/out non-temporal, for batches
+// far larger than the last-level cache.
+template <bool BF16, int VEC, bool STREAM>
 __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int r1) {
     const int n = M.n, m = M.m, r = M.rank;
     // P and T were written by earlier kernels and are only read here: the
@@ -712,7 +715,7 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
 #pragma unroll
             for (int u = 0; u < ROW_GROUP; ++u) {
                 const int row = min(i0 + u, r1 - 1);
-                load_Mv<BF16, VEC, true>(M, eta, static_cast<long long>(row) * m + colc, mv[u]);
+                load_Mv<BF16, VEC, STREAM>(M, eta, static_cast<long long>(row) * m + colc, mv[u]);
             }
 #pragma unroll
             for (int u = 0; u < ROW_GROUP; ++u) {
@@ -745,8 +748,16 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
                     nm[v] = mv[u][v] - sacc;
                 }
                 if constexpr (VEC == 4) {
-                    if (M.out) store_stream(reinterpret_cast<float4*>(M.out) + e / 4, make_float4(o[0], o[1], o[2], o[3]));
-                    store_stream(reinterpret_cast<float4*>(M.mem) + e / 4, make_float4(nm[0], nm[1], nm[2], nm[3]));
+                    const float4 ov = make_float4(o[0], o[1], o[2], o[3]), mv4 = make_float4(nm[0], nm[1], nm[2], nm[3]);
+                    float4* const op = reinterpret_cast<float4*>(M.out) + e / 4;
+                    float4* const mp = reinterpret_cast<float4*>(M.mem) + e / 4;
+                    if constexpr (STREAM) {
+                        if (M.out) store_stream(op, ov);
+                        store_stream(mp, mv4);
+                    } else {
+                        if (M.out) *op = ov;
+                        *mp = mv4;
+                    }
                 } else {
                     if (M.out) M.out[e] = o[0];
                     M.mem[e] = nm[0];
@@ -758,7 +769,7 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
 
 // Decode + residual for every matrix of the table: workgroup b takes its
 // balanced share of rows.
-template <bool BF16>
+template <bool BF16, bool STREAM>
 __global__ __launch_bounds__(PS_THREADS) void psgd_out(const PsBatch B) {
     const int b = blockIdx.x, G = B.gout;
     const long long E = B.eall;
@@ -770,9 +781,9 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_out(const PsBatch B) {
         rows_in_share(M, s_lo, s_hi, r0, r1);
         if (r0 >= r1) continue;
         if (M.m % 4 == 0)
-            out_rows<BF16, 4>(M, B.eta, r0, r1);
+            out_rows<BF16, 4, STREAM>(M, B.eta, r0, r1);
         else
-            out_rows<BF16, 1>(M, B.eta, r0, r1);
+            out_rows<BF16, 1, STREAM>(M, B.eta, r0, r1);
     }
 }
 
@@ -970,7 +981,11 @@ int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& t
     }
     {
         TimedLaunch tl("psgd_out", s);
-        psgd_out<BF16><<<B.gout, PS_THREADS, 0, s>>>(B);
+        // streaming accesses only pay when the pass moves far more than the
+        // 256 MB last-level cache holds
+        const bool stream = static_cast<double>(B.eall) * (BF16 ? 14.0 : 16.0) > STREAM_MIN_BYTES;
+        if (stream) psgd_out<BF16, true><<<B.gout, PS_THREADS, 0, s>>>(B);
+        else psgd_out<BF16, false><<<B.gout, PS_THREADS, 0, s>>>(B);
         if ((rc = check_launch("psgd_out")) != GC_OK) return rc;
     }
     return GC_OK;
