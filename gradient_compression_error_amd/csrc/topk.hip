@@ -364,12 +364,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
     }
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_select1(const unsigned* __restrict__ hist1, unsigned k,
-                                                           TopkState* __restrict__ st) {
+constexpr int SEL_THREADS = 1024;   // single-workgroup selection kernels
+
+__global__ __launch_bounds__(SEL_THREADS) void topk_select1(const unsigned* __restrict__ hist1, unsigned k,
+                                                            TopkState* __restrict__ st) {
     __shared__ unsigned s_h[H1_BINS];
-    __shared__ unsigned s_tmp[4];
+    __shared__ unsigned s_tmp[SEL_THREADS / 64];
     __shared__ unsigned s_bin, s_above;
-    select_bin<H1_BINS, NCOPY>(hist1, H1_BINS, k, s_h, s_tmp, &s_bin, &s_above);
+    select_bin<H1_BINS, NCOPY, SEL_THREADS>(hist1, H1_BINS, k, s_h, s_tmp, &s_bin, &s_above);
     if (threadIdx.x == 0) {
         st->b1 = s_bin;
         st->above1 = s_above;
@@ -453,13 +455,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_capture(
     }
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_select2(const unsigned* __restrict__ hist2, unsigned k,
-                                                           TopkState* __restrict__ st) {
+__global__ __launch_bounds__(SEL_THREADS) void topk_select2(const unsigned* __restrict__ hist2, unsigned k,
+                                                            TopkState* __restrict__ st) {
     __shared__ unsigned s_h[H2_BINS];
-    __shared__ unsigned s_tmp[4];
+    __shared__ unsigned s_tmp[SEL_THREADS / 64];
     __shared__ unsigned s_bin, s_above;
     const unsigned above1 = st->above1;
-    select_bin<H2_BINS, NCOPY>(hist2, H2_BINS, k - above1, s_h, s_tmp, &s_bin, &s_above);
+    select_bin<H2_BINS, NCOPY, SEL_THREADS>(hist2, H2_BINS, k - above1, s_h, s_tmp, &s_bin, &s_above);
     if (threadIdx.x == 0) {
         st->prefix2 = (st->b1 << 12) | s_bin;
         st->above2 = above1 + s_above;
@@ -824,7 +826,7 @@ int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, f
     }
     {
         TimedLaunch tl("topk_select1", s);
-        topk_select1<<<1, TK_THREADS, 0, s>>>(hist1, ku, st);
+        topk_select1<<<1, SEL_THREADS, 0, s>>>(hist1, ku, st);
         if ((rc = check_launch("topk_select1")) != GC_OK) return rc;
     }
     {
@@ -834,7 +836,7 @@ int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, f
     }
     {
         TimedLaunch tl("topk_select2", s);
-        topk_select2<<<1, TK_THREADS, 0, s>>>(hist2, ku, st);
+        topk_select2<<<1, SEL_THREADS, 0, s>>>(hist2, ku, st);
         if ((rc = check_launch("topk_select2")) != GC_OK) return rc;
     }
     {
