@@ -687,9 +687,13 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
     typedef const __attribute__((address_space(4))) float* ConstF;
     const ConstD tm = (ConstD)(M.tmat);
     const ConstF pr = (ConstF)(M.praw);
-    float T[16];
+    // P^ = P T in float64: T's entries scale like 1 / sigma_min(P), so float32
+    // T would scale its rounding by the condition number of P
+    double T[10];   // upper triangle, column by column: T[a][j] (a <= j) at j (j + 1) / 2 + a
 #pragma unroll
-    for (int i = 0; i < 16; ++i) T[i] = static_cast<float>(tm[i]);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int a = 0; a <= j; ++a) T[j * (j + 1) / 2 + a] = tm[a * 4 + j];
     const int ns = nstrips_of(m);
     for (int strip = 0; strip < ns; ++strip) {
         const int col0 = strip * (PS_THREADS * VEC) + threadIdx.x * VEC;
@@ -725,10 +729,10 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
                 float ph[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    float v = 0.0f;
+                    double v = 0.0;
 #pragma unroll
-                    for (int a = 0; a <= j; ++a) v = fmaf(prv[a], T[a * 4 + j], v);
-                    ph[j] = v;
+                    for (int a = 0; a <= j; ++a) v = fma(static_cast<double>(prv[a]), T[j * (j + 1) / 2 + a], v);
+                    ph[j] = static_cast<float>(v);
                 }
                 if (write_p) {
                     float mine = ph[0];

@@ -50,8 +50,18 @@ class PsgdSet:
         gc.gc_powersgd_ef_step(mats, eta, self.ws)
 
 
-def check_step(ps, grads_h, eta, label=""):
-    """One GPU step compared with the oracle from the same state; returns max error."""
+def cond_p(grad_h, mem_h, q_h, eta, r):
+    """Condition number of P = M Q_in (float64) for one matrix."""
+    M = mem_h.astype(np.float64) + np.float64(np.float32(eta)) * oracle.grad_to_f64(grad_h).reshape(mem_h.shape)
+    return float(np.linalg.cond(M @ q_h[:r].T.astype(np.float64)))
+
+
+def check_step(ps, grads_h, eta, label="", cond_scaled=False):
+    """One GPU step compared with the oracle from the same state; returns max error.
+
+    cond_scaled: allow max(1e-4, 10 * 2^-24 * cond(P)) per matrix -- the float32
+    limit of any method on a nearly rank-deficient P (the pages' 1e-4 holds for
+    the configured data, whose P are well conditioned)."""
     mem_before = [t.cpu().numpy() for t in ps.mem]
     q_before = [t.cpu().numpy() for t in ps.q]
     ps.step([to_dev(g) for g in grads_h], eta)
@@ -60,6 +70,9 @@ def check_step(ps, grads_h, eta, label=""):
     for i, (n, m) in enumerate(ps.shapes):
         r = ps.ranks[i]
         ref = oracle.powersgd_ef_step(grads_h[i], mem_before[i], q_before[i].T, eta, r)
+        tol = TOL
+        if cond_scaled:
+            tol = max(TOL, 10.0 * 2.0 ** -24 * cond_p(grads_h[i], mem_before[i], q_before[i], eta, r))
         Mn = np.linalg.norm(ref["M"])
         checks = [("mem", ps.mem[i].cpu().numpy(), ref["mem"]), ("Q", ps.q[i].cpu().numpy()[:r].T, ref["Q"])]
         if ps.out[i] is not None:
@@ -73,7 +86,7 @@ def check_step(ps, grads_h, eta, label=""):
             else:
                 err = rel_err(got, want)
             worst = max(worst, err)
-            assert err <= TOL, f"{label} matrix {i} ({n}x{m}, r={r}) {name}: rel err {err:.3e}"
+            assert err <= tol, f"{label} matrix {i} ({n}x{m}, r={r}) {name}: rel err {err:.3e} (tol {tol:.1e})"
         # columns of Q beyond the rank are untouched
         if r < 4:
             assert np.array_equal(ps.q[i].cpu().numpy()[r:], q_before[i][r:])
@@ -110,8 +123,19 @@ def test_c2_resnet18(rank):
         check_step(ps, gen.c2_grads(t), 1.0, f"C2 step {t}")
 
 
+def test_more_matrices_than_one_launch_group():
+    """4100 matrices: more than one launch group (4096), fused and split shapes mixed."""
+    print("case: 4100 small matrices", flush=True)
+    shapes = [(3 + i % 5, 8 if i % 3 else 5) for i in range(4100)]
+    ranks = [1 + i % 3 for i in range(4100)]
+    ps = PsgdSet(shapes, ranks)
+    grads = [gen.gaussian_mat(n, m, 7000 + i, 1e-2) for i, (n, m) in enumerate(shapes)]
+    # a few of these random small P are nearly singular (cond up to 1.2e4)
+    check_step(ps, grads, 1.0, "4100 matrices", cond_scaled=True)
+
+
 def test_many_matrices_multi_batch():
-    """More matrices than one launch table holds, with mixed ranks and widths."""
+    """70 matrices of mixed ranks and widths in one launch group (all classes and the split path)."""
     print("case: 70 mixed matrices", flush=True)
     r = gen.rng(0, gen.KIND_MISC, 400)
     shapes = [(int(r.integers(1, 300)), int(r.choice([5, 64, 100, 576, 1030]))) for _ in range(70)]

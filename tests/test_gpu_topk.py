@@ -168,3 +168,19 @@ def test_c5_embedding_full_size():
     g = gen.c5_embedding_bf16(0)
     m = gen.gaussian_vector(d, 13, 1e-3)
     one_step(TopkRunner(d, gen.C5_EMB_K), g, m, 1.0)
+
+
+def test_guess_too_high_takes_full_capture():
+    """The sampled guess can only make the capture pass cheaper, never change the
+    result: 64 large entries inside one sampled run make the guess exceed the true
+    threshold (k = 1000), so the re-reading capture path must run -- bit-exact all the same."""
+    d, k = 1 << 20, 1000
+    print(f"case: top-k guess above threshold d={d} k={k}", flush=True)
+    g = gen.gaussian_vector(d, 77, 1e-3)
+    run0 = 5 * (d // 256)                    # start of the 6th sampled run of 64 entries
+    g[run0:run0 + 64] = 2.0
+    r = TopkRunner(d, k)
+    ref = one_step(r, g, np.zeros(d, np.float32), 1.0)
+    state = r.ws[:64].view(torch.int32).cpu().numpy()
+    assert state[8] == 0, "expected the re-reading capture path (guess above the level-1 bin)"
+    assert np.count_nonzero(ref["g"]) == k
