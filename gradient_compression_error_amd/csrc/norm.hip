@@ -5,7 +5,7 @@
 // critical regime, the high-compression level l_high outside it.
 //
 //   norm_partial  one pass over all layers at once: each workgroup squares and
-//                 sums (float64) one 4096-entry tile of one layer
+//                 sums (float64) one 16384-entry tile of one layer
 //   norm_final    one workgroup per layer sums its tile partials in a fixed
 //                 order and writes sqrt(sum) as float32
 // gc_accordion_select is plain host code: the decision needs the norms of
@@ -18,8 +18,8 @@ namespace gc {
 namespace {
 
 constexpr int NM_THREADS = 256;
-constexpr int NM_UNROLL = 4;
-constexpr int NM_TILE = NM_THREADS * 4 * NM_UNROLL;   // 4096
+constexpr int NM_UNROLL = 16;
+constexpr int NM_TILE = NM_THREADS * 4 * NM_UNROLL;   // 16384
 constexpr int NM_MAXL = 160;
 
 // Layer table of one launch; begin[l] = first workgroup of layer l.
@@ -56,6 +56,7 @@ __global__ __launch_bounds__(NM_THREADS) void norm_partial(const NmBatch B) {
 #pragma unroll
         for (int u = 0; u < NM_UNROLL; ++u) acc += sq4(v[u]);
     } else {
+#pragma unroll 4
         for (long long i = base + threadIdx.x; i < len; i += NM_THREADS) {
             const double x = load_grad1<BF16>(ptr, i);
             acc += x * x;
