@@ -211,3 +211,15 @@ def test_accordion_host_c4_schedule(gcl):
         if lv[0] == gcl.GC_LEVEL_LOW:
             lows.append(t)
     assert lows == gold["low_checks"]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU only: --gpus N > 1 exits with a message (before touching a GPU)."""
+    import json
+    import subprocess
+    import sys
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert p.returncode == 2
+    msg = json.loads(p.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
