@@ -39,8 +39,12 @@ namespace {
 
 constexpr int PS_THREADS = 256;
 constexpr int PS_MAXB = 4096;        // matrices per launch group
-constexpr int P_ROWS_WAVE = 4;       // rows per wave in psgd_p
-constexpr int P_ROWS_WG = 16;        // rows per workgroup in psgd_p
+constexpr int P_ROWS_WAVE = 2;       // rows per wave in psgd_p
+constexpr int P_ROWS_WG = 4 * P_ROWS_WAVE;   // rows per workgroup in psgd_p
+// A fused-pass workgroup takes at least this many rows of the class's longest
+// row length: on small classes one-row shares cost more in per-workgroup
+// set-up and M^T P partials than they gain in parallelism.
+constexpr int PQ_ROWS_MIN = 8;
 constexpr int Q_ROWS = 32;           // rows per chunk in psgd_q
 constexpr int ROW_GROUP = 8;         // rows whose loads are issued together in psgd_q / psgd_out
 constexpr int QR_PER_THREAD = 16;    // M^T P partials per psgd_qreduce thread before slicing a column
@@ -850,7 +854,7 @@ int qr_slices(int nq) {
 // Grid of a balanced pass over e entries whose widest row has mmax entries:
 // every share is at least one such row, so a workgroup owns a row of every
 // matrix its share overlaps.
-int balanced_grid(long long e, int mmax, int gmax) {
+int balanced_grid(long long e, long long mmax, int gmax) {
     return e > 0 ? static_cast<int>(std::min<long long>(gmax, std::max<long long>(1, e / mmax))) : 0;
 }
 
@@ -884,7 +888,8 @@ Plan make_plan(const gc_mat* mats, int nmats) {
         for (int c = 0; c < PQ_CLASSES; ++c) {
             pb.cbase[c] = base;
             base += pb.cent[c];
-            pb.cgrid[c] = balanced_grid(pb.cent[c], cmax[c], CUS * PQ_CLASS[c].blocks_per_cu);
+            pb.cgrid[c] = balanced_grid(pb.cent[c], static_cast<long long>(cmax[c]) * PQ_ROWS_MIN,
+                                        CUS * PQ_CLASS[c].blocks_per_cu);
             // psgd_pq addresses a workgroup's share with 32-bit buffer offsets
             // (plus two row groups of look-ahead and the 2^31 idle-lane
             // offset): keep every share below PQ_SHARE_MAX_ENTRIES, running
