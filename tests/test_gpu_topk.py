@@ -184,3 +184,56 @@ def test_guess_too_high_takes_full_capture():
     state = r.ws[:64].view(torch.int32).cpu().numpy()
     assert state[8] == 0, "expected the re-reading capture path (guess above the level-1 bin)"
     assert np.count_nonzero(ref["g"]) == k
+
+
+def test_max_size():
+    """d = INT32_MAX, the longest vector the ABI takes, k = 1%.  The oracle cannot
+    run at this size, so the checks are ones that fix the answer:
+      * the accumulated values, rebuilt as memory + decoded vector (one of the two
+        is +0 at every position), equal the oracle's bit for bit at 2^20 seeded
+        positions and at both ends of the vector;
+      * indices ascend; every key above the smallest selected key is selected, and
+        of the keys equal to it the lowest indices are taken (the unique top-k set
+        under |value| descending, index ascending);
+      * values, decoded vector and memory agree with that set bit for bit."""
+    d = 2**31 - 1
+    k = d // 100
+    eta = 0.75
+    print(f"case: top-k max size d={d} k={k} eta={eta}", flush=True)
+    # a seeded normal draw made on the device (a host draw of 2^31 values takes
+    # half a minute); the oracle gets the sampled positions of this same tensor
+    rng_t = torch.Generator(device=DEV)
+    rng_t.manual_seed(91)
+    g_t = torch.randn(d, generator=rng_t, dtype=torch.float32, device=DEV).mul_(1e-3)
+    rs = np.random.default_rng(5)
+    pos = np.unique(np.concatenate([rs.integers(0, d, 1 << 20), np.arange(4096), np.arange(d - 4096, d)]))
+    pos_t = torch.from_numpy(pos).to(DEV)
+    g_samples = g_t[pos_t].cpu().numpy()
+    mem_t = torch.zeros(d, dtype=torch.float32, device=DEV)
+    r = TopkRunner(d, k)
+    r.encode(g_t, mem_t, eta)
+    r.decode()
+    torch.cuda.synchronize()
+    del g_t
+    acc = mem_t + r.out
+    want = oracle.ef_accumulate(np.zeros(pos.size, np.float32), g_samples, eta)
+    assert np.array_equal(f32_bits(acc[pos_t]), f32_bits(want))
+
+    idx = r.idx.long()
+    assert int(idx[0]) >= 0 and int(idx[-1]) < d and bool((idx[1:] > idx[:-1]).all())
+    key = acc.view(torch.int32) & 0x7FFFFFFF
+    ksel = key[idx]
+    thr = int(ksel.min())
+    n_gt = int((key > thr).sum())
+    assert int((ksel > thr).sum()) == n_gt
+    ties = torch.nonzero(key == thr).flatten()
+    n_take = k - n_gt
+    assert 1 <= n_take <= ties.numel()
+    assert torch.equal(idx[ksel == thr], ties[:n_take])
+    del key, ksel, ties
+
+    assert torch.equal(r.val.view(torch.int32), acc[idx].view(torch.int32))
+    assert bool((mem_t[idx].view(torch.int32) == 0).all())
+    assert int((r.out != 0).sum()) == k
+    del acc, idx, mem_t, r
+    torch.cuda.empty_cache()
