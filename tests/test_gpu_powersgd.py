@@ -186,3 +186,50 @@ def test_c5_bert_full():
     grads = [gen.c5_matrix_bf16(0, l) for l in range(len(gen.BERT_MATS))]
     worst = check_step(ps, grads, 1.0, "C5")
     print(f"C5 worst relative error {worst:.2e}")
+
+
+def test_max_size_one_matrix():
+    """One 524287 x 4096 matrix: n*m = 2^31 - 4096, the largest a matrix may be.
+    bf16 gradient from a seeded draw on the device, m0 = 0, eta = 1 (so M is the
+    gradient exactly), rank 4.  The oracle's steps at this size, in pieces:
+    P = M Q_in as float64 row-chunk products, P^ by the oracle's Gram-Schmidt,
+    Q = M^T P^ as float64 chunk products; out and mem compared at 2048 sampled rows
+    (including the first and last).  Same 1e-4 relative bar as the other cases."""
+    n, m, r = 524287, 4096, 4
+    print(f"case: PowerSGD max size {n}x{m} r={r} bf16", flush=True)
+    rng_t = torch.Generator(device=DEV)
+    rng_t.manual_seed(92)
+    g32 = torch.randn(n, m, generator=rng_t, dtype=torch.float32, device=DEV).mul_(1e-3)
+    g_t = g32.to(torch.bfloat16)
+    del g32
+    ps = PsgdSet([(n, m)], [r], q_cfg=gen.CFG_C5)
+    q_in = ps.q[0].clone()
+    ps.step([g_t], 1.0)
+    torch.cuda.synchronize()
+
+    chunk = 1 << 16
+    qd = q_in.double().t().contiguous()                   # m x 4
+    P = torch.empty(n, 4, dtype=torch.float64, device=DEV)
+    for i0 in range(0, n, chunk):
+        P[i0:i0 + chunk] = g_t[i0:i0 + chunk].double() @ qd
+    p_ref = oracle.orthonormalize_mgs(P.cpu().numpy())
+    p_ref_t = torch.from_numpy(p_ref).to(DEV)
+    Q = torch.zeros(m, 4, dtype=torch.float64, device=DEV)
+    for i0 in range(0, n, chunk):
+        Q += g_t[i0:i0 + chunk].double().t() @ p_ref_t[i0:i0 + chunk]
+    q_ref = Q.cpu().numpy()
+
+    rs = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([rs.integers(0, n, 2046), [0, n - 1]]))
+    rows_t = torch.from_numpy(rows).to(DEV)
+    out_ref = p_ref[rows] @ q_ref.T
+    M_rows = g_t[rows_t].double().cpu().numpy()
+    errs = {"P": rel_err(ps.p[0].cpu().numpy()[:r].T, p_ref),
+            "Q": rel_err(ps.q[0].cpu().numpy()[:r].T, q_ref),
+            "out": rel_err(ps.out[0][rows_t].cpu().numpy(), out_ref),
+            "mem": rel_err(ps.mem[0][rows_t].cpu().numpy(), M_rows - out_ref)}
+    print("max-size relative errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for name, err in errs.items():
+        assert err <= TOL, f"{name}: rel err {err:.3e}"
+    del P, Q, p_ref_t, g_t, ps
+    torch.cuda.empty_cache()
