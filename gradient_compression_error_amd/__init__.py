@@ -126,6 +126,19 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
+# The C ABI sees pointers and one length per call, so the sizes and dtypes of
+# the tensors behind them are checked here, before any pointer is passed on.
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dtype_is(t, dtype, name: str):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
 # ------------------------------------------------------------------ top-k
 
 def gc_topk_workspace_bytes(d: int, k: int) -> int:
@@ -134,6 +147,12 @@ def gc_topk_workspace_bytes(d: int, k: int) -> int:
 
 def gc_topk_ef_encode(grad, mem, eta: float, k: int, out_idx, out_val, ws, stream=None) -> None:
     """Mem-SGD top-k encode: mem <- acc - top_k(acc), (out_idx, out_val) <- top_k(acc)."""
+    import torch
+    _dtype_is(mem, torch.float32, "mem")
+    _dtype_is(out_idx, torch.int32, "out_idx")
+    _dtype_is(out_val, torch.float32, "out_val")
+    _need(grad.numel() == mem.numel(), "grad and mem must have the same number of entries")
+    _need(out_idx.numel() >= k and out_val.numel() >= k, "out_idx and out_val need room for k entries")
     _check(lib.gc_topk_ef_encode(_ptr(grad), _dtype_code(grad), _ptr(mem), mem.numel(), float(eta), int(k),
                                  _ptr(out_idx), _ptr(out_val), _ptr(ws), _nbytes(ws), _stream(stream)),
            "gc_topk_ef_encode")
@@ -141,11 +160,22 @@ def gc_topk_ef_encode(grad, mem, eta: float, k: int, out_idx, out_val, ws, strea
 
 def gc_randk_ef_encode(grad, mem, eta: float, idx, out_val, stream=None) -> None:
     """Rand-k EF step on the given ascending index subset; k = idx.numel()."""
+    import torch
+    _dtype_is(mem, torch.float32, "mem")
+    _dtype_is(idx, torch.int32, "idx")
+    _dtype_is(out_val, torch.float32, "out_val")
+    _need(grad.numel() == mem.numel(), "grad and mem must have the same number of entries")
+    _need(out_val.numel() >= idx.numel(), "out_val needs room for idx.numel() entries")
     _check(lib.gc_randk_ef_encode(_ptr(grad), _dtype_code(grad), _ptr(mem), mem.numel(), float(eta), _ptr(idx),
                                   idx.numel(), _ptr(out_val), _stream(stream)), "gc_randk_ef_encode")
 
 
 def gc_topk_decode(idx, val, out, accumulate: bool = False, stream=None) -> None:
+    import torch
+    _dtype_is(idx, torch.int32, "idx")
+    _dtype_is(val, torch.float32, "val")
+    _dtype_is(out, torch.float32, "out")
+    _need(val.numel() == idx.numel(), "idx and val must have the same number of entries")
     k = idx.numel()
     _check(lib.gc_topk_decode(_ptr(idx) if k else None, _ptr(val) if k else None, k, _ptr(out), out.numel(),
                               1 if accumulate else 0, _stream(stream)), "gc_topk_decode")
@@ -165,7 +195,24 @@ class Mat:
 
 
 def _mats(mats: Sequence[Mat]):
+    import torch
+    _need(len(mats) >= 1, "need at least one matrix")
     arr = (gc_mat * len(mats))()
+    for i, a in enumerate(mats):
+        _need(a.mem.dim() == 2, f"mats[{i}].mem must be 2-D (n, m)")
+        n, m = a.mem.shape
+        r = int(a.rank)
+        _dtype_is(a.mem, torch.float32, f"mats[{i}].mem")
+        _dtype_is(a.q, torch.float32, f"mats[{i}].q")
+        _need(a.grad.dtype == mats[0].grad.dtype, "every gradient must have the first one's dtype")
+        _need(a.grad.numel() == n * m, f"mats[{i}].grad must have n*m entries")
+        _need(a.q.numel() >= r * m, f"mats[{i}].q needs rank*m entries")
+        if a.p is not None:
+            _dtype_is(a.p, torch.float32, f"mats[{i}].p")
+            _need(a.p.numel() >= r * n, f"mats[{i}].p needs rank*n entries")
+        if a.out is not None:
+            _dtype_is(a.out, torch.float32, f"mats[{i}].out")
+            _need(a.out.numel() == n * m, f"mats[{i}].out must have n*m entries")
     for i, a in enumerate(mats):
         n, m = a.mem.shape
         arr[i] = gc_mat(_ptr(a.grad), _ptr(a.mem), _ptr(a.q), _ptr(a.p), _ptr(a.out), n, m, int(a.rank))
@@ -196,6 +243,10 @@ def gc_grad_norm_workspace_bytes(layers) -> int:
 
 
 def gc_grad_norm(layers, norms, ws, stream=None) -> None:
+    import torch
+    _dtype_is(norms, torch.float32, "norms")
+    _need(norms.numel() >= len(layers), "norms needs one entry per layer")
+    _need(all(t.dtype == layers[0].dtype for t in layers), "every layer must have the first one's dtype")
     _check(lib.gc_grad_norm(_spans(layers), len(layers), _dtype_code(layers[0]), _ptr(norms), _ptr(ws), _nbytes(ws),
                             _stream(stream)), "gc_grad_norm")
 
@@ -204,6 +255,7 @@ def gc_accordion_select(norm_now, norm_prev, threshold: float, has_prev: bool):
     """Host call.  Returns (levels int32[n], new norm_prev float32[n])."""
     now = np.ascontiguousarray(norm_now, np.float32)
     prev = np.ascontiguousarray(norm_prev, np.float32).copy()
+    _need(prev.size == now.size, "norm_now and norm_prev must have the same length")
     lv = np.zeros(now.size, np.int32)
     _check(lib.gc_accordion_select(now.ctypes.data_as(C.POINTER(C.c_float)), prev.ctypes.data_as(C.POINTER(C.c_float)),
                                    now.size, float(threshold), 1 if has_prev else 0,

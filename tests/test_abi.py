@@ -223,3 +223,47 @@ def test_bench_refuses_more_than_one_gpu():
     assert p.returncode == 2
     msg = json.loads(p.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_binding_checks_sizes_and_dtypes(gcl):
+    """The C ABI sees one length per call; the binding refuses tensors whose sizes
+    or dtypes disagree with it before any pointer is passed (checked with host
+    tensors: the checks run before the device-pointer check)."""
+    import torch
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32)
+    ws = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="same number of entries"):
+        gcl.gc_topk_ef_encode(f32(10), f32(12), 1.0, 2, i32(2), f32(2), ws)
+    with pytest.raises(ValueError, match="room for k"):
+        gcl.gc_topk_ef_encode(f32(10), f32(10), 1.0, 3, i32(2), f32(3), ws)
+    with pytest.raises(TypeError, match="out_idx"):
+        gcl.gc_topk_ef_encode(f32(10), f32(10), 1.0, 2, f32(2), f32(2), ws)
+    with pytest.raises(TypeError, match="mem"):
+        gcl.gc_topk_ef_encode(f32(10), torch.zeros(10, dtype=torch.float64), 1.0, 2, i32(2), f32(2), ws)
+    with pytest.raises(ValueError, match="same number of entries"):
+        gcl.gc_randk_ef_encode(f32(9), f32(10), 1.0, i32(2), f32(2))
+    with pytest.raises(ValueError, match="room"):
+        gcl.gc_randk_ef_encode(f32(10), f32(10), 1.0, i32(3), f32(2))
+    with pytest.raises(ValueError, match="same number of entries"):
+        gcl.gc_topk_decode(i32(3), f32(2), f32(10))
+    with pytest.raises(TypeError, match="idx"):
+        gcl.gc_topk_decode(torch.zeros(3, dtype=torch.int64), f32(3), f32(10))
+    M = gcl.Mat
+    n, m = 6, 8
+    mem = torch.zeros(n, m)
+    with pytest.raises(ValueError, match="n\\*m entries"):
+        gcl.gc_powersgd_workspace_bytes([M(grad=f32(n * m - 1), mem=mem, q=torch.zeros(4, m), rank=4)])
+    with pytest.raises(ValueError, match="rank\\*m"):
+        gcl.gc_powersgd_workspace_bytes([M(grad=f32(n * m), mem=mem, q=torch.zeros(2, m), rank=4)])
+    with pytest.raises(ValueError, match="rank\\*n"):
+        gcl.gc_powersgd_workspace_bytes([M(grad=f32(n * m), mem=mem, q=torch.zeros(4, m), rank=4,
+                                           p=torch.zeros(3, n))])
+    with pytest.raises(ValueError, match="first one's dtype"):
+        gcl.gc_powersgd_workspace_bytes([M(grad=f32(n * m), mem=mem, q=torch.zeros(4, m), rank=2),
+                                         M(grad=torch.zeros(n * m, dtype=torch.bfloat16), mem=mem.clone(),
+                                           q=torch.zeros(4, m), rank=2)])
+    with pytest.raises(ValueError, match="one entry per layer"):
+        gcl.gc_grad_norm([f32(4), f32(5)], f32(1), ws)
+    with pytest.raises(ValueError, match="same length"):
+        gcl.gc_accordion_select([1.0, 2.0], [1.0], 0.5, True)
