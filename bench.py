@@ -473,6 +473,25 @@ def kernel_source_hash(kernel):
 
 # ------------------------------------------------------------------ main
 
+def device_copy_gbs(torch, dev, nbytes=1 << 30, reps=5):
+    """Device-to-device copy rate on this machine (bytes read + written per second),
+    the practical reference beside the 8 TB/s peak; measured after the timed steps."""
+    a = torch.ones(nbytes // 4, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -527,6 +546,7 @@ def main():
     torch.cuda.synchronize()
     if args.flush:
         total_ms = 0.0
+        step_ms = []
         for t in range(args.steps):
             flush_buf.fill_(1.0)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -534,16 +554,24 @@ def main():
             W.step(args.warmup + 1 + t)
             e1.record()
             torch.cuda.synchronize()
-            total_ms += e0.elapsed_time(e1)
+            step_ms.append(e0.elapsed_time(e1))
+            total_ms += step_ms[-1]
         wall_ms = total_ms
     else:
+        # an event before each step and one after the last: per-step times for
+        # the median and p90 (the events are enqueued, nothing waits on them)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         t0 = time.perf_counter()
         for t in range(args.steps):
+            evs[t].record()
             W.step(args.warmup + 1 + t)
+        evs[-1].record()
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3
+        step_ms = [evs[t].elapsed_time(evs[t + 1]) for t in range(args.steps)]
     k_ms, k_launches = gc.gc_timing_read()
     gc.gc_timing_enable(None)
+    copy_gbs = device_copy_gbs(torch, dev)
 
     ms_step = wall_ms / args.steps
     gbs = W.grad_bytes / (ms_step * 1e-3) / 1e9
@@ -563,9 +591,14 @@ def main():
     line = {"metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "us_per_step": round(ms_step * 1e3, 1),
             "hbm_frac_step": round(step_frac, 4), "algorithmic_bytes_per_step": int(W.alg_bytes),
+            "us_per_step_median": round(float(np.median(step_ms)) * 1e3, 1),
+            "us_per_step_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 1),
+            "device_copy_gbs": round(copy_gbs, 1),
+            "frac_of_device_copy_step": round(W.alg_bytes / (ms_step * 1e-3) / 1e9 / copy_gbs, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic", "cache": "flushed between steps" if args.flush else "warm (back-to-back steps)",
             "config": W.config, "description": W.description, "device": torch.cuda.get_device_name(0),
+            "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
             "roofline": roof}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
