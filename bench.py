@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -464,12 +465,25 @@ def traffic_from_profiles(kernel, workload, src_hash):
     return rec.get("traffic_bytes_per_launch")
 
 
+def _code_only(text: str) -> bytes:
+    """Source text without comments and whitespace: edits to comments do not
+    change what the counters measured."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text).encode()
+
+
+def source_file_hash(fname):
+    """Hash of a kernel source file plus the shared header, code only."""
+    csrc = os.path.join(ROOT, "gradient_compression_error_amd", "csrc")
+    h = hashlib.sha256(_code_only(open(os.path.join(csrc, fname)).read()))
+    h.update(_code_only(open(os.path.join(csrc, "gc_common.h")).read()))
+    return h.hexdigest()
+
+
 def kernel_source_hash(kernel):
     fname = "powersgd.hip" if kernel.startswith("psgd") else "norm.hip" if kernel.startswith("norm") else "topk.hip"   # randk_* is in topk.hip
-    p = os.path.join(ROOT, "gradient_compression_error_amd", "csrc", fname)
-    h = hashlib.sha256(open(p, "rb").read())
-    h.update(open(os.path.join(ROOT, "gradient_compression_error_amd", "csrc", "gc_common.h"), "rb").read())
-    return h.hexdigest()
+    return source_file_hash(fname)
 
 
 # ------------------------------------------------------------------ main

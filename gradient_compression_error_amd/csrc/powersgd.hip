@@ -50,7 +50,7 @@ constexpr int ROW_GROUP = 8;         // rows whose loads are issued together in 
 constexpr int QR_PER_THREAD = 16;    // M^T P partials per psgd_qreduce thread before slicing a column
 constexpr int CUS = 256;             // MI355X compute units
 constexpr double STREAM_MIN_BYTES = 1e9;   // psgd_out traffic above which it streams
-// largest share (entries) of one psgd_pq workgroup: (share + rows of look-ahead) * 4 bytes < 2^31
+// largest share (entries) of one psgd_pq workgroup: (share + a row group of look-ahead) * 4 bytes < 2^31
 constexpr long long PQ_SHARE_MAX_ENTRIES = (1LL << 28) - (1LL << 20);
 constexpr int OUT_GRID_MAX = CUS * 4;   // psgd_out holds 4 workgroups per CU
 
@@ -891,9 +891,10 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             pb.cgrid[c] = balanced_grid(pb.cent[c], static_cast<long long>(cmax[c]) * PQ_ROWS_MIN,
                                         CUS * PQ_CLASS[c].blocks_per_cu);
             // psgd_pq addresses a workgroup's share with 32-bit buffer offsets
-            // (plus two row groups of look-ahead and the 2^31 idle-lane
-            // offset): keep every share below PQ_SHARE_MAX_ENTRIES, running
-            // extra workgroups in further rounds if a class is that large
+            // (plus the row group it loads ahead, past the share's last row,
+            // and the 2^31 idle-lane offset): keep every share below
+            // PQ_SHARE_MAX_ENTRIES, running extra workgroups in further rounds
+            // if a class is that large
             if (pb.cent[c] > 0) {
                 const long long need = (pb.cent[c] + PQ_SHARE_MAX_ENTRIES - 1) / PQ_SHARE_MAX_ENTRIES;
                 pb.cgrid[c] = static_cast<int>(std::max<long long>(pb.cgrid[c], need));
