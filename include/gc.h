@@ -155,7 +155,8 @@ size_t gc_powersgd_workspace_bytes(const gc_mat* mats, int nmats);
  * Buffers of different matrices must not overlap.
  * The call copies a small matrix table (120 bytes per matrix) from host memory
  * into ws with one hipMemcpyAsync on `stream`, then enqueues the kernels; the
- * host array may be reused as soon as the call returns.
+ * host array may be reused as soon as the call returns.  Because of that copy
+ * the call is not for graph capture (a replay would read freed host memory).
  * Errors: GC_ERR_ARG, GC_ERR_DTYPE, GC_ERR_WORKSPACE, GC_ERR_HIP. */
 int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta,
                         void* ws, size_t ws_bytes, void* stream);
