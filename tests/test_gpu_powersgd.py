@@ -94,7 +94,8 @@ def check_step(ps, grads_h, eta, label="", cond_scaled=False):
 
 
 SHAPES = [(64, 27, 1), (64, 27, 4), (7, 2, 2), (2, 9, 2), (1, 1, 1), (100, 512, 4), (128, 576, 2),
-          (33, 1030, 3), (1000, 3, 3), (4, 4608, 4), (513, 4608, 4), (17, 64, 4), (300, 2304, 1)]
+          (33, 1030, 3), (1000, 3, 3), (4, 4608, 4), (513, 4608, 4), (17, 64, 4), (300, 2304, 1),
+          (37, 8192, 4), (5, 8196, 2), (3, 4100, 1), (600, 6144, 3)]
 
 
 @pytest.mark.parametrize("n,m,r", SHAPES)
