@@ -52,7 +52,13 @@ constexpr int CUS = 256;             // MI355X compute units
 constexpr double STREAM_MIN_BYTES = 1e9;   // psgd_out traffic above which it streams
 // largest share (entries) of one psgd_pq workgroup: (share + a row group of look-ahead) * 4 bytes < 2^31
 constexpr long long PQ_SHARE_MAX_ENTRIES = (1LL << 28) - (1LL << 20);
-constexpr int OUT_GRID_MAX = CUS * 4;   // psgd_out holds 4 workgroups per CU
+// psgd_out grid: one resident round (about 4 workgroups fit per CU) for large
+// launch groups; two rounds for groups of at most OUT_TWO_ROUNDS_MAX entries.
+// On small sets of mixed row lengths the shares are even in entries but not in
+// time (short rows carry more per-row work), and the second round lets the
+// hardware balance them; on large uniform sets one round is slightly faster.
+constexpr int OUT_GRID_MAX = CUS * 4;
+constexpr long long OUT_TWO_ROUNDS_MAX = 1LL << 26;
 
 struct PsMat {
     const void* grad;
@@ -932,7 +938,8 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             P.mats.push_back(pm);
         }
         pb.eall = eall;
-        pb.gout = static_cast<int>(std::min<long long>(OUT_GRID_MAX, std::max<long long>(1, eall / 1024)));
+        const long long gmax = eall <= OUT_TWO_ROUNDS_MAX ? 2LL * OUT_GRID_MAX : OUT_GRID_MAX;
+        pb.gout = static_cast<int>(std::min<long long>(gmax, std::max<long long>(1, eall / 1024)));
         P.batches.push_back(pb);
         i = j;
     }
