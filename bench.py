@@ -388,6 +388,11 @@ def cpu_baseline(name):
     except ImportError:   # pragma: no cover
         threadpool_limits = None
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    # one core: pin the process to the lowest CPU it may use (the GPU timing is
+    # over by now), restore the mask afterwards
+    aff = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    if aff:
+        os.sched_setaffinity(0, {min(aff)})
     try:
         if name == "c5":
             mats = [(l, gen.c5_matrix_bf16(0, l)) for l in range(6)]          # encoder layer 0
@@ -444,10 +449,13 @@ def cpu_baseline(name):
                 break
         gbs = nbytes * reps / el / 1e9
         return {"value": round(gbs, 5), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"{sample}; {reps} repetition(s), {el:.1f} s, float64 NumPy, one BLAS/OpenMP thread"}
+                "sample": f"{sample}; {reps} repetition(s), {el:.1f} s, float64 NumPy, one BLAS/OpenMP thread "
+                          f"pinned to one CPU"}
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
+        if aff:
+            os.sched_setaffinity(0, aff)
 
 
 # ------------------------------------------------------------------ traffic from committed counters
