@@ -234,3 +234,28 @@ def test_max_size_one_matrix():
         assert err <= TOL, f"{name}: rel err {err:.3e}"
     del P, Q, p_ref_t, g_t, ps
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seed,dtype", [(1, "f32"), (2, "bf16"), (3, "f32")])
+def test_random_shape_sets(seed, dtype):
+    """Seeded random sets of 12 matrices mixing every row-length class and the
+    split path (m from 1 to 5000, some m % 4 != 0), random ranks: the plan's
+    class sort, balanced shares and partial counts on shapes no workload has."""
+    rs = np.random.default_rng(100 + seed)
+    shapes, ranks = [], []
+    for _ in range(12):
+        n = int(rs.integers(1, 600))
+        m = int(rs.choice([rs.integers(1, 64), rs.integers(64, 1025), rs.integers(1025, 2049),
+                           rs.integers(2049, 4097), rs.integers(4097, 5001)]))
+        if rs.uniform() < 0.7:
+            m = max(4, m - m % 4)
+        shapes.append((n, m))
+        ranks.append(int(rs.integers(1, min(4, n, m) + 1)))
+    print(f"case: random PowerSGD set seed={seed} {dtype} {shapes} ranks={ranks}", flush=True)
+    ps = PsgdSet(shapes, ranks, q_cfg=7)
+    grads = []
+    for l, (n, m) in enumerate(shapes):
+        g = gen.gaussian_mat(n, m, 300 + 13 * seed + l, 10.0 ** rs.uniform(-4, -2))
+        grads.append(gen.f32_to_bf16_bits(g).reshape(n, m) if dtype == "bf16" else g)
+    for step in range(2):
+        check_step(ps, grads, 1.0, f"random set {seed} step {step}", cond_scaled=True)

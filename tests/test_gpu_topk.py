@@ -237,3 +237,15 @@ def test_max_size():
     assert int((r.out != 0).sum()) == k
     del acc, idx, mem_t, r
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_random_sizes(seed):
+    """Seeded random (d, k) from 1 to 3M, bit-exact: tile tails, tiny and huge k."""
+    rs = np.random.default_rng(200 + seed)
+    d = int(rs.choice([rs.integers(1, 5000), rs.integers(5000, 200_000), rs.integers(200_000, 3_000_000)]))
+    k = int(rs.choice([1, rs.integers(1, d + 1), max(1, d // 100), d]))
+    print(f"case: random top-k seed={seed} d={d} k={k}", flush=True)
+    g = gen.gaussian_vector(d, 400 + seed, 1e-3)
+    m = gen.gaussian_vector(d, 500 + seed, 1e-3)
+    one_step(TopkRunner(d, k), g, m, 0.5)
