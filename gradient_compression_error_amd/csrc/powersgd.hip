@@ -41,9 +41,17 @@ constexpr int PS_THREADS = 256;
 constexpr int PS_MAXB = 4096;        // matrices per launch group
 constexpr int P_ROWS_WAVE = 2;       // rows per wave in psgd_p
 constexpr int P_ROWS_WG = 4 * P_ROWS_WAVE;   // rows per workgroup in psgd_p
-// A fused-pass workgroup takes at least this many rows of the class's longest
-// row length: on small classes one-row shares cost more in per-workgroup
-// set-up and M^T P partials than they gain in parallelism.
+// The fused pass partitions a class by cost, not by entries: a row of m
+// entries costs m + PQ_ROW_COST units, the constant standing for the per-row
+// work that does not scale with the row (its share of a row group's load
+// latency, the cross-wave reduction and the P and Gram updates).  On classes
+// of one row length the shares are those of an even split of the entries; on
+// mixed lengths short rows no longer pile up in one workgroup (ResNet-18's
+// 128 x 64 layer put about 72 rows into one share, against 8 for its widest).
+constexpr int PQ_ROW_COST = 1024;
+// A fused-pass workgroup takes at least this many rows of the class's costliest
+// row: on small classes one-row shares cost more in per-workgroup set-up and
+// M^T P partials than they gain in parallelism.
 constexpr int PQ_ROWS_MIN = 8;
 constexpr int Q_ROWS = 32;           // rows per chunk in psgd_q
 constexpr int ROW_GROUP = 8;         // rows whose loads are issued together in psgd_q / psgd_out
@@ -71,13 +79,14 @@ struct PsMat {
     float* qpart;    // [nq][m][4] partial M^T P
     double* tmat;    // [16] T, row-major 4x4
     long long off;   // first entry of the matrix in the batch (matrices back to back)
+    long long poff;  // fused classes: first unit of the matrix in its class's psgd_pq partition
     int n, m, rank;
     int nq, ng;      // number of M^T P / Gram partials
     int begin_p;     // split path: first workgroup of the matrix in psgd_p
     int begin_q;     // split path: first workgroup in psgd_q
     int begin_r;     // first workgroup in psgd_qreduce
     int qs;          // psgd_qreduce threads per column
-    int pad;
+    int rcost;       // fused classes: partition units per row (m + PQ_ROW_COST)
 };
 static_assert(sizeof(PsMat) % 8 == 0, "table entries are copied as words");
 
@@ -94,8 +103,8 @@ struct PsBatch {
     float eta;
     int cbeg[PQ_CLASSES + 2];      // matrices [cbeg[c], cbeg[c+1]) are of class c
     int cgrid[PQ_CLASSES];         // psgd_pq grid of each fused class
-    long long cbase[PQ_CLASSES];   // first entry of each fused class
-    long long cent[PQ_CLASSES];    // entries of each fused class
+    long long cbase[PQ_CLASSES];   // first partition unit of each fused class
+    long long cent[PQ_CLASSES];    // partition units of each fused class
     long long eall;                // entries of all matrices
     int gout;                      // psgd_out grid
     int pad;
@@ -127,13 +136,14 @@ __device__ __forceinline__ PsMat mat_at(const PsBatch& B, int i) {
     return r;
 }
 
-// Last i in [i0, i1) whose first entry is <= s.
+// Last i in [i0, i1) whose first entry (PART: first partition unit) is <= s.
+template <bool PART = false>
 __device__ __forceinline__ int mat_of_entry(const PsBatch& B, int i0, int i1, long long s) {
     const MatTable T = mat_table(B);
     int lo = i0, hi = i1;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (T[mid].off <= s) lo = mid;
+        if ((PART ? T[mid].poff : T[mid].off) <= s) lo = mid;
         else hi = mid;
     }
     return lo;
@@ -161,11 +171,21 @@ __device__ __forceinline__ int mat_of_block(const PsBatch& B, int i0, int i1, in
     return lo;
 }
 
+// Rows [r0, r1) of an n-row matrix that starts at unit off, w units per row,
+// whose first unit lies in [s_lo, s_hi).
+__device__ __forceinline__ void rows_in_range(long long off, int n, int w, long long s_lo, long long s_hi,
+                                              int& r0, int& r1) {
+    const long long a = s_lo - off, b = s_hi - off;
+    r0 = a <= 0 ? 0 : static_cast<int>(min(static_cast<long long>(n), (a + w - 1) / w));
+    r1 = b <= 0 ? 0 : static_cast<int>(min(static_cast<long long>(n), (b + w - 1) / w));
+}
 // Rows of matrix M whose first entry lies in [s_lo, s_hi).
 __device__ __forceinline__ void rows_in_share(const PsMat& M, long long s_lo, long long s_hi, int& r0, int& r1) {
-    const long long a = s_lo - M.off, b = s_hi - M.off;
-    r0 = a <= 0 ? 0 : static_cast<int>(min(static_cast<long long>(M.n), (a + M.m - 1) / M.m));
-    r1 = b <= 0 ? 0 : static_cast<int>(min(static_cast<long long>(M.n), (b + M.m - 1) / M.m));
+    rows_in_range(M.off, M.n, M.m, s_lo, s_hi, r0, r1);
+}
+// Rows of matrix M (of a fused class) whose first partition unit lies in [s_lo, s_hi).
+__device__ __forceinline__ void rows_in_part(const PsMat& M, long long s_lo, long long s_hi, int& r0, int& r1) {
+    rows_in_range(M.poff, M.n, M.rcost, s_lo, s_hi, r0, r1);
 }
 
 __device__ __forceinline__ int nstrips_of(int m) {
@@ -552,14 +572,233 @@ __global__ __launch_bounds__(NT, pq_min_waves<NT>()) void psgd_pq(const PsBatch 
     const long long E = B.cent[cls], base = B.cbase[cls];
     const long long s_lo = base + share_lo(E, G, b), s_hi = base + share_lo(E, G, b + 1);
     int par = 0;
-    for (int i = mat_of_entry(B, i0, i1, s_lo); i < i1; ++i) {
+    for (int i = mat_of_entry<true>(B, i0, i1, s_lo); i < i1; ++i) {
         const PsMat M = mat_at(B, i);
-        if (M.off >= s_hi) break;
+        if (M.poff >= s_hi) break;
         int r0, r1;
-        rows_in_share(M, s_lo, s_hi, r0, r1);
+        rows_in_part(M, s_lo, s_hi, r0, r1);
         if (r0 >= r1) continue;
-        pq_rows<BF16, NT, RG>(M, B.eta, r0, r1, b - owner_of(M.off - base, E, G), s_part, par);
+        pq_rows<BF16, NT, RG>(M, B.eta, r0, r1, b - owner_of(M.poff - base, E, G), s_part, par);
     }
+}
+
+// ------------------------------------------------------------------ psgd_pq_teams
+
+// Small launch groups are launch-bound, so their fused classes run in ONE
+// launch of 1024-thread workgroups.  The workgroups of class c follow those of
+// the classes before it; a class-c workgroup holds 1024 / TW teams of TW
+// threads (TW = 256, 512, 1024: the class's row width), and team j of its w-th
+// workgroup is virtual block w * (1024 / TW) + j of the class's balanced
+// partition (cgrid[c] virtual blocks): the share, the partial index and the
+// arithmetic of one workgroup of the separate class launch.  Every team runs
+// the same number of iterations -- the workgroup's largest row-group count --
+// with exactly one barrier each, outside any team-dependent branch, so the
+// barrier is uniform; a team that has run out of rows idles.
+constexpr int TEAM_NT = 1024;
+constexpr int TEAM_RG = 4;
+constexpr int TEAM_CLASSES = 3;   // the classes a team kernel runs (row widths 256, 512, 1024 threads)
+static_assert(TEAM_CLASSES == PQ_CLASSES, "one team width per fused class");
+constexpr long long TEAM_MAX_ENTRIES = 1LL << 26;   // launch groups up to this size use the team kernel
+
+__host__ __device__ constexpr int team_width(int cls) { return cls == 0 ? 256 : cls == 1 ? 512 : 1024; }
+__host__ __device__ inline int team_wgs(int vblocks, int cls) {
+    const int per = TEAM_NT / team_width(cls);
+    return (vblocks + per - 1) / per;
+}
+
+template <bool BF16, int TW>
+__device__ __forceinline__ void pq_teams(const PsBatch& B, int cls, int wg_in_class,
+                                         float (*s_part)[TEAM_NT / 16][4 * TEAM_RG], int* s_cnt) {
+    constexpr int RG = TEAM_RG, V = 4 * RG, NPT = TW / 16, L = 64 / V, TEAMS = TEAM_NT / TW;
+    static_assert(V == 16, "row groups of 4");
+    // a team spans whole waves: its index (and all its matrix state) is wave-uniform
+    const int tid = threadIdx.x, team = __builtin_amdgcn_readfirstlane(tid / TW), tt = tid % TW;
+    const int lane = tid & 63, wt = __builtin_amdgcn_readfirstlane(tt >> 6);
+    const int G = B.cgrid[cls];
+    const int vb = wg_in_class * TEAMS + team;
+    const bool valid = vb < G;
+    const int i0 = B.cbeg[cls], i1 = B.cbeg[cls + 1];
+    const long long E = B.cent[cls], base = B.cbase[cls];
+    long long s_lo = 0, s_hi = 0;
+    if (valid) {
+        s_lo = base + share_lo(E, G, vb);
+        s_hi = base + share_lo(E, G, vb + 1);
+    }
+    const MatTable T = mat_table(B);
+
+    // the team's row groups over all the matrices of its share
+    int ngroups = 0, mfirst = i1;
+    if (valid) {
+        mfirst = mat_of_entry<true>(B, i0, i1, s_lo);
+        for (int i = mfirst; i < i1; ++i) {
+            const long long off = T[i].poff;
+            if (off >= s_hi) break;
+            int a, b;
+            rows_in_range(off, T[i].n, T[i].rcost, s_lo, s_hi, a, b);
+            if (b > a) ngroups += (b - a + RG - 1) / RG;
+        }
+    }
+    if (tt == 0) s_cnt[team] = ngroups;
+    __syncthreads();
+    int gmax = 0;
+#pragma unroll
+    for (int j = 0; j < TEAMS; ++j) gmax = max(gmax, s_cnt[j]);
+
+    // state of the team's current matrix (uniform across the team)
+    int mi = mfirst, r0 = 0, r1 = 0, nr = 0, k = 0, part = 0, m = 1;
+    PsMat M{};
+    bool act = false;
+    float q[4][4], qt[4][4];
+    double g = 0.0;
+    __amdgpu_buffer_rsrc_t rm = rows_rsrc(nullptr, 0, 4, 0), rg = rows_rsrc(nullptr, 0, 4, 0);
+    unsigned colm = OOB_OFFSET, colg = OOB_OFFSET, rowm = 0, rowg = 0;
+    RawChunk<BF16> raw[RG];
+    auto load_group = [&](int kk) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const unsigned kr = static_cast<unsigned>(kk + r);
+            raw[r].m = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, colm + kr * rowm, 0, 0));
+            if constexpr (BF16)
+                raw[r].g = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, colg + kr * rowg, 0, 0));
+            else
+                raw[r].g = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, colg + kr * rowg, 0, 0));
+        }
+    };
+    // moves to the first matrix at or after mi with rows in the share and
+    // loads its Q_in and first row group; false when there is none
+    auto open_matrix = [&]() -> bool {
+        for (; mi < i1; ++mi) {
+            if (T[mi].poff >= s_hi) {
+                mi = i1;
+                break;
+            }
+            M = mat_at(B, mi);
+            rows_in_part(M, s_lo, s_hi, r0, r1);
+            if (r1 > r0) break;
+        }
+        if (mi >= i1) return false;
+        nr = r1 - r0;
+        k = 0;
+        part = vb - owner_of(M.poff - base, E, G);
+        m = M.m;
+        act = tt < m / 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (act && j < M.rank) qv = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m)[tt];
+            q[0][j] = qv.x; q[1][j] = qv.y; q[2][j] = qv.z; q[3][j] = qv.w;
+        }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qt[cc][j] = 0.0f;
+        g = 0.0;
+        const long long e0 = static_cast<long long>(r0) * m, ne = static_cast<long long>(nr) * m;
+        rm = rows_rsrc(M.mem, e0, 4, ne);
+        rg = rows_rsrc(M.grad, e0, BF16 ? 2 : 4, ne);
+        colm = act ? static_cast<unsigned>(tt) * 16u : OOB_OFFSET;
+        colg = act ? static_cast<unsigned>(tt) * (BF16 ? 8u : 16u) : OOB_OFFSET;
+        rowm = static_cast<unsigned>(m) * 4u;
+        rowg = static_cast<unsigned>(m) * (BF16 ? 2u : 4u);
+        load_group(0);
+        return true;
+    };
+
+    const int li = lane & 15, lr = lane >> 4;
+    const int vi = lane % V, lg = lane / V;
+    const int ga = (lane >> 2) & 3, gb = lane & 3;
+    bool live = valid && open_matrix();
+    int par = 0;
+    for (int it = 0; it < gmax; ++it) {
+        float v[RG][4];
+        if (live) {
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const float4 x = raw_to_M<BF16>(raw[r], B.eta);
+                v[r][0] = x.x; v[r][1] = x.y; v[r][2] = x.z; v[r][3] = x.w;
+            }
+            load_group(k + RG);
+            float xs[V];
+#pragma unroll
+            for (int r = 0; r < RG; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float a = v[r][0] * q[0][j];
+                    a = fmaf(v[r][1], q[1][j], a);
+                    a = fmaf(v[r][2], q[2][j], a);
+                    xs[4 * r + j] = fmaf(v[r][3], q[3][j], a);
+                }
+            float x8[V / 2], x4[V / 4], x2[V / 8], x1[V / 16];
+            scatter_step<DPP_XOR1, 1>(xs, x8, lane);
+            scatter_step<DPP_XOR2, 2>(x8, x4, lane);
+            scatter_step<DPP_ROR4, 4>(x4, x2, lane);
+            scatter_step<DPP_ROR8, 8>(x2, x1, lane);
+            // lane li of a 16-lane row now holds entry rev4(li)
+            s_part[par][team * NPT + wt * 4 + lr][rev4(li)] = x1[0];
+        }
+        __syncthreads();
+        if (live) {
+            float pv = 0.0f;
+#pragma unroll
+            for (int u = 0; u < NPT / L; ++u) pv += s_part[par][team * NPT + lg * (NPT / L) + u][vi];
+#pragma unroll
+            for (int sh = V; sh < 64; sh <<= 1) pv += __shfl_xor(pv, sh, WAVE);
+            float p[RG][4];
+#pragma unroll
+            for (int r = 0; r < RG; ++r)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    p[r][j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pv), 4 * r + j));
+#pragma unroll
+            for (int r = 0; r < RG; ++r)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) qt[cc][j] = fmaf(v[r][cc], p[r][j], qt[cc][j]);
+            if (wt == 0) {
+                if (lane < V && k + vi / 4 < nr) M.praw[static_cast<long long>(r0 + k) * 4 + vi] = pv;
+                if (lane < 16) {
+#pragma unroll
+                    for (int r = 0; r < RG; ++r) {
+                        float pa = p[r][0], pb = p[r][0];
+#pragma unroll
+                        for (int j = 1; j < 4; ++j) {
+                            pa = (ga == j) ? p[r][j] : pa;
+                            pb = (gb == j) ? p[r][j] : pb;
+                        }
+                        g = fma(static_cast<double>(pa), static_cast<double>(pb), g);
+                    }
+                }
+            }
+            k += RG;
+            if (k >= nr) {
+                if (act) {
+                    float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(part) * m + 4 * tt;
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) dst[cc] = make_float4(qt[cc][0], qt[cc][1], qt[cc][2], qt[cc][3]);
+                }
+                if (wt == 0 && lane < 16) M.gpart[static_cast<long long>(part) * 16 + lane] = g;
+                ++mi;
+                live = open_matrix();
+            }
+        }
+        par ^= 1;
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(TEAM_NT) void psgd_pq_teams(const PsBatch B) {
+    __shared__ float s_part[2][TEAM_NT / 16][4 * TEAM_RG];
+    __shared__ int s_cnt[TEAM_NT / 256];
+    int w = blockIdx.x, cls = 0;
+    for (; cls < TEAM_CLASSES; ++cls) {
+        const int n = team_wgs(B.cgrid[cls], cls);
+        if (w < n) break;
+        w -= n;
+    }
+    if (cls == 0) pq_teams<BF16, 256>(B, 0, w, s_part, s_cnt);
+    else if (cls == 1) pq_teams<BF16, 512>(B, 1, w, s_part, s_cnt);
+    else if (cls == 2) pq_teams<BF16, 1024>(B, 2, w, s_part, s_cnt);
 }
 
 // ------------------------------------------------------------------ psgd_qreduce
@@ -826,6 +1065,7 @@ int shape_class(int m) {
 struct PlanMat {
     int idx;            // index in the caller's array
     long long off;      // first entry within the batch
+    long long poff;     // fused classes: first partition unit within the batch
     int nq, ng;         // partial counts
     int begin_p, begin_q, begin_r;
     int qs;             // psgd_qreduce threads per column
@@ -884,8 +1124,8 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             const int c = shape_class(mats[a].m);
             ++ccount[c];
             if (c < PQ_CLASSES) {
-                pb.cent[c] += static_cast<long long>(mats[a].n) * mats[a].m;
-                cmax[c] = std::max(cmax[c], mats[a].m);
+                pb.cent[c] += static_cast<long long>(mats[a].n) * (mats[a].m + PQ_ROW_COST);
+                cmax[c] = std::max(cmax[c], mats[a].m + PQ_ROW_COST);
             }
         }
         pb.cbeg[0] = 0;
@@ -899,14 +1139,15 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             // psgd_pq addresses a workgroup's share with 32-bit buffer offsets
             // (plus the row group it loads ahead, past the share's last row,
             // and the 2^31 idle-lane offset): keep every share below
-            // PQ_SHARE_MAX_ENTRIES, running extra workgroups in further rounds
-            // if a class is that large
+            // PQ_SHARE_MAX_ENTRIES units (a share holds fewer entries than
+            // units), running extra workgroups in further rounds if a class
+            // is that large
             if (pb.cent[c] > 0) {
                 const long long need = (pb.cent[c] + PQ_SHARE_MAX_ENTRIES - 1) / PQ_SHARE_MAX_ENTRIES;
                 pb.cgrid[c] = static_cast<int>(std::max<long long>(pb.cgrid[c], need));
             }
         }
-        long long eall = 0;
+        long long eall = 0, pall = 0;
         for (int a : idx) {
             PlanMat pm{};
             pm.idx = a;
@@ -914,9 +1155,12 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             const int n = mats[a].n, m = mats[a].m;
             const int c = shape_class(m);
             if (c < PQ_CLASSES) {
-                const long long E = pb.cent[c], rel = pm.off - pb.cbase[c];
+                pm.poff = pall;
+                pall += static_cast<long long>(n) * (m + PQ_ROW_COST);
+                const long long E = pb.cent[c], rel = pm.poff - pb.cbase[c];
                 const int G = pb.cgrid[c];
-                pm.nq = pm.ng = owner_of(rel + static_cast<long long>(n - 1) * m, E, G) - owner_of(rel, E, G) + 1;
+                pm.nq = pm.ng = owner_of(rel + static_cast<long long>(n - 1) * (m + PQ_ROW_COST), E, G) -
+                                owner_of(rel, E, G) + 1;
             } else {
                 pm.nq = (n + Q_ROWS - 1) / Q_ROWS;
                 pm.ng = (n + P_ROWS_WG - 1) / P_ROWS_WG;
@@ -980,13 +1224,25 @@ int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& t
                                         hipMemcpyHostToDevice, s);
     if (e != hipSuccess)
         return fail(GC_ERR_HIP, std::string("gc_powersgd_ef_step: matrix table copy: ") + hipGetErrorString(e));
+    int fused = 0, team_grid = 0;
     for (int c = 0; c < PQ_CLASSES; ++c) {
-        if (B.cbeg[c + 1] == B.cbeg[c]) continue;
+        fused += B.cbeg[c + 1] > B.cbeg[c] ? 1 : 0;
+        team_grid += team_wgs(B.cgrid[c], c);
+    }
+    if (fused >= 2 && B.eall <= TEAM_MAX_ENTRIES) {
+        // small group, several classes: one launch (the classes' passes side by side)
         TimedLaunch tl("psgd_pq", s);
-        if (c == 0) psgd_pq<BF16, 256, 8><<<B.cgrid[c], 256, 0, s>>>(B, c);
-        else if (c == 1) psgd_pq<BF16, 512, 4><<<B.cgrid[c], 512, 0, s>>>(B, c);
-        else psgd_pq<BF16, 1024, 4><<<B.cgrid[c], 1024, 0, s>>>(B, c);
+        psgd_pq_teams<BF16><<<team_grid, TEAM_NT, 0, s>>>(B);
         if ((rc = check_launch("psgd_pq")) != GC_OK) return rc;
+    } else {
+        for (int c = 0; c < PQ_CLASSES; ++c) {
+            if (B.cbeg[c + 1] == B.cbeg[c]) continue;
+            TimedLaunch tl("psgd_pq", s);
+            if (c == 0) psgd_pq<BF16, 256, 8><<<B.cgrid[c], 256, 0, s>>>(B, c);
+            else if (c == 1) psgd_pq<BF16, 512, 4><<<B.cgrid[c], 512, 0, s>>>(B, c);
+            else psgd_pq<BF16, 1024, 4><<<B.cgrid[c], 1024, 0, s>>>(B, c);
+            if ((rc = check_launch("psgd_pq")) != GC_OK) return rc;
+        }
     }
     const int s0 = B.cbeg[SPLIT_CLASS];
     if (s0 < B.count) {
@@ -1083,6 +1339,8 @@ int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta
             base += ws_round(static_cast<size_t>(pm.nq) * a.m * 16);
             M.tmat = reinterpret_cast<double*>(base);
             M.off = pm.off;
+            M.poff = pm.poff;
+            M.rcost = a.m + PQ_ROW_COST;
             M.n = a.n;
             M.m = a.m;
             M.rank = a.rank;
