@@ -57,6 +57,8 @@ _sig("gc_topk_decode", _i32, _vp, _vp, _i64, _vp, _i64, _i32, _vp)
 _sig("gc_randk_ef_encode", _i32, _vp, _i32, _vp, _i64, _f32, _vp, _i64, _vp, _vp)
 _sig("gc_powersgd_workspace_bytes", _sz, C.POINTER(gc_mat), _i32)
 _sig("gc_powersgd_ef_step", _i32, C.POINTER(gc_mat), _i32, _i32, _f32, _vp, _sz, _vp)
+_sig("gc_powersgd_ef_step_deferred", _i32, C.POINTER(gc_mat), C.POINTER(C.c_int32), _i32, _i32, _f32, _vp, _sz, _vp)
+_sig("gc_powersgd_materialize", _i32, C.POINTER(gc_mat), C.POINTER(C.c_int32), _i32, _vp, _sz, _vp)
 _sig("gc_grad_norm_workspace_bytes", _sz, C.POINTER(gc_span), _i32)
 _sig("gc_grad_norm", _i32, C.POINTER(gc_span), _i32, _i32, _vp, _vp, _sz, _vp)
 _sig("gc_accordion_select", _i32, C.POINTER(C.c_float), C.POINTER(C.c_float), _i32, _f32, _i32,
@@ -67,6 +69,7 @@ _sig("gc_kernel_names", C.c_char_p)
 
 EXPORTED = ["gc_status_str", "gc_last_error", "gc_topk_workspace_bytes", "gc_topk_ef_encode",
             "gc_topk_decode", "gc_randk_ef_encode", "gc_powersgd_workspace_bytes", "gc_powersgd_ef_step",
+            "gc_powersgd_ef_step_deferred", "gc_powersgd_materialize",
             "gc_grad_norm_workspace_bytes", "gc_grad_norm", "gc_accordion_select",
             "gc_timing_enable", "gc_timing_read", "gc_kernel_names"]
 
@@ -194,18 +197,24 @@ class Mat:
     out: object = None
 
 
-def _mats(mats: Sequence[Mat]):
+def _mats(mats: Sequence[Mat], prev=None, need_grad: bool = True):
+    """ctypes array of the matrices; prev: the previous ranks of a deferred
+    or materialize call (q and p must then hold max(rank, prev) columns)."""
     import torch
     _need(len(mats) >= 1, "need at least one matrix")
+    g0 = next((a.grad for a in mats if a.grad is not None), None)
     arr = (gc_mat * len(mats))()
     for i, a in enumerate(mats):
         _need(a.mem.dim() == 2, f"mats[{i}].mem must be 2-D (n, m)")
         n, m = a.mem.shape
-        r = int(a.rank)
+        r = max(int(a.rank), int(prev[i])) if prev is not None else int(a.rank)
         _dtype_is(a.mem, torch.float32, f"mats[{i}].mem")
         _dtype_is(a.q, torch.float32, f"mats[{i}].q")
-        _need(a.grad.dtype == mats[0].grad.dtype, "every gradient must have the first one's dtype")
-        _need(a.grad.numel() == n * m, f"mats[{i}].grad must have n*m entries")
+        if a.grad is None:
+            _need(not need_grad, f"mats[{i}].grad is required")
+        else:
+            _need(a.grad.dtype == g0.dtype, "every gradient must have the first one's dtype")
+            _need(a.grad.numel() == n * m, f"mats[{i}].grad must have n*m entries")
         _need(a.q.numel() >= r * m, f"mats[{i}].q needs rank*m entries")
         if a.p is not None:
             _dtype_is(a.p, torch.float32, f"mats[{i}].p")
@@ -220,13 +229,40 @@ def _mats(mats: Sequence[Mat]):
 
 
 def gc_powersgd_workspace_bytes(mats: Sequence[Mat]) -> int:
-    return int(lib.gc_powersgd_workspace_bytes(_mats(mats), len(mats)))
+    # the query reads the shapes only
+    return int(lib.gc_powersgd_workspace_bytes(_mats(mats, need_grad=False), len(mats)))
 
 
 def gc_powersgd_ef_step(mats: Sequence[Mat], eta: float, ws, stream=None) -> None:
     arr = _mats(mats)
     _check(lib.gc_powersgd_ef_step(arr, len(mats), _dtype_code(mats[0].grad), float(eta), _ptr(ws), _nbytes(ws),
                                    _stream(stream)), "gc_powersgd_ef_step")
+
+
+def _prev_ranks(mats, prev_rank):
+    prev = np.ascontiguousarray(prev_rank, np.int32)
+    _need(prev.ndim == 1 and prev.size == len(mats), "prev_rank needs one entry per matrix")
+    for i, a in enumerate(mats):
+        _need(a.p is not None, f"mats[{i}].p is required: it keeps P^ for the deferred memory")
+    return prev
+
+
+def gc_powersgd_ef_step_deferred(mats: Sequence[Mat], prev_rank, eta: float, ws, stream=None) -> None:
+    """PowerSGD step with the memory kept as (M, P^, Q); prev_rank[i] = 0 when
+    mem holds the memory itself, else the rank of the previous deferred call."""
+    prev = _prev_ranks(mats, prev_rank)
+    arr = _mats(mats, prev)
+    _check(lib.gc_powersgd_ef_step_deferred(arr, prev.ctypes.data_as(C.POINTER(C.c_int32)), len(mats),
+                                            _dtype_code(mats[0].grad), float(eta), _ptr(ws), _nbytes(ws),
+                                            _stream(stream)), "gc_powersgd_ef_step_deferred")
+
+
+def gc_powersgd_materialize(mats: Sequence[Mat], prev_rank, ws, stream=None) -> None:
+    """Writes the deferred memory out: mem = M - P^ Q^T where prev_rank[i] > 0."""
+    prev = _prev_ranks(mats, prev_rank)
+    arr = _mats([Mat(grad=None, mem=a.mem, q=a.q, rank=a.rank, p=a.p) for a in mats], prev, need_grad=False)
+    _check(lib.gc_powersgd_materialize(arr, prev.ctypes.data_as(C.POINTER(C.c_int32)), len(mats), _ptr(ws),
+                                       _nbytes(ws), _stream(stream)), "gc_powersgd_materialize")
 
 
 # ------------------------------------------------------------------ norms / Accordion

@@ -87,8 +87,11 @@ struct PsMat {
     int begin_r;     // first workgroup in psgd_qreduce
     int qs;          // psgd_qreduce threads per column
     int rcost;       // fused classes: partition units per row (m + PQ_ROW_COST)
+    int prank;       // deferred memory: rank of the previous step's P^, Q (0: mem holds the memory itself)
+    int pad_;
 };
 static_assert(sizeof(PsMat) % 8 == 0, "table entries are copied as words");
+static_assert(sizeof(PsMat) == 136, "table entry size stated in gc.h");
 
 // Fused-pass classes by row length: m <= 1024, m <= 2048, m <= 4096 (m % 4 == 0),
 // each with its own workgroup width; the rest take the split path.
@@ -188,6 +191,26 @@ __device__ __forceinline__ void rows_in_part(const PsMat& M, long long s_lo, lon
     rows_in_range(M.poff, M.n, M.rcost, s_lo, s_hi, r0, r1);
 }
 
+// One entry of the residual m' = M - P^ Q^T of a row: ph = the row of P^,
+// qr = Q of the column (both zero past the rank).  The explicit step's output
+// pass and the deferred step's first pass both form it with these float32
+// operations in this order, so the deferred memory has the explicit bits.
+__device__ __forceinline__ float residual1(float mv, const float (&ph)[4], const float (&qr)[4]) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s = fmaf(ph[j], qr[j], s);
+    return mv - s;
+}
+
+// Row `row` of P^_prev (zero past the previous rank), through scalar loads:
+// p was written by an earlier kernel and is only read in this one.
+__device__ __forceinline__ void prev_phat_row(const PsMat& M, int row, float (&ph)[4]) {
+    typedef const __attribute__((address_space(4))) float* ConstF;
+    const ConstF pc = (ConstF)(M.p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ph[j] = j < M.prank ? pc[static_cast<long long>(j) * M.n + row] : 0.0f;
+}
+
 __device__ __forceinline__ int nstrips_of(int m) {
     const int w = (m % 4 == 0) ? PS_THREADS * 4 : PS_THREADS;
     return (m + w - 1) / w;
@@ -223,33 +246,68 @@ __device__ __forceinline__ void load_Mv(const PsMat& M, float eta, long long e, 
 
 // Each wave owns P_ROWS_WAVE rows; lanes stride over the row in VEC-wide
 // chunks.  The row loads of one chunk are issued before any use.
-template <bool BF16, int VEC>
+template <bool BF16, int VEC, bool DEF>
 __device__ __forceinline__ void p_rows(const PsMat& M, float eta, int row0, float (&acc)[P_ROWS_WAVE][4]) {
     const int lane = threadIdx.x & 63;
     const int n = M.n, m = M.m, r = M.rank;
     const int nch = m / VEC;
+    const int qn = DEF ? max(r, M.prank) : r;
     int rowc[P_ROWS_WAVE];
+    float ph[P_ROWS_WAVE][4];
 #pragma unroll
-    for (int rr = 0; rr < P_ROWS_WAVE; ++rr) rowc[rr] = min(row0 + rr, n - 1);
+    for (int rr = 0; rr < P_ROWS_WAVE; ++rr) {
+        rowc[rr] = min(row0 + rr, n - 1);
+        if constexpr (DEF) prev_phat_row(M, rowc[rr], ph[rr]);
+    }
 #pragma unroll 2
     for (int c = lane; c < nch; c += 64) {
-        float mv[P_ROWS_WAVE][VEC];
-#pragma unroll
-        for (int rr = 0; rr < P_ROWS_WAVE; ++rr)
-            load_Mv<BF16, VEC>(M, eta, static_cast<long long>(rowc[rr]) * m + static_cast<long long>(c) * VEC, mv[rr]);
-        float qv[VEC][4];
+        float qa[VEC][4], qv[VEC][4], qp[VEC][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (j < r) {
+            if (j < qn) {
                 if constexpr (VEC == 4) {
                     const float4 t = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m)[c];
-                    qv[0][j] = t.x; qv[1][j] = t.y; qv[2][j] = t.z; qv[3][j] = t.w;
+                    qa[0][j] = t.x; qa[1][j] = t.y; qa[2][j] = t.z; qa[3][j] = t.w;
                 } else {
-                    qv[0][j] = M.q[static_cast<long long>(j) * m + c];
+                    qa[0][j] = M.q[static_cast<long long>(j) * m + c];
                 }
             } else {
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) qv[v][j] = 0.0f;
+                for (int v = 0; v < VEC; ++v) qa[v][j] = 0.0f;
+            }
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                qv[v][j] = j < r ? qa[v][j] : 0.0f;
+                qp[v][j] = j < M.prank ? qa[v][j] : 0.0f;
+            }
+        }
+        float mv[P_ROWS_WAVE][VEC];
+#pragma unroll
+        for (int rr = 0; rr < P_ROWS_WAVE; ++rr) {
+            const long long e = static_cast<long long>(rowc[rr]) * m + static_cast<long long>(c) * VEC;
+            if constexpr (DEF) {
+                // rebuild m' from M_prev, form M and store it over M_prev (the
+                // clamped copy of the last row stores nothing)
+                float mp[VEC], gv[VEC];
+                if constexpr (VEC == 4) {
+                    const float4 a = reinterpret_cast<const float4*>(M.mem)[e / 4];
+                    const float4 b = load_grad4<BF16>(M.grad, e / 4);
+                    mp[0] = a.x; mp[1] = a.y; mp[2] = a.z; mp[3] = a.w;
+                    gv[0] = b.x; gv[1] = b.y; gv[2] = b.z; gv[3] = b.w;
+                } else {
+                    mp[0] = M.mem[e];
+                    gv[0] = load_grad1<BF16>(M.grad, e);
+                }
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) mv[rr][v] = ef_acc(residual1(mp[v], ph[rr], qp[v]), eta, gv[v]);
+                if (row0 + rr < n) {
+                    if constexpr (VEC == 4)
+                        reinterpret_cast<float4*>(M.mem)[e / 4] = make_float4(mv[rr][0], mv[rr][1], mv[rr][2], mv[rr][3]);
+                    else
+                        M.mem[e] = mv[rr][0];
+                }
+            } else {
+                load_Mv<BF16, VEC>(M, eta, e, mv[rr]);
             }
         }
 #pragma unroll
@@ -264,7 +322,7 @@ __device__ __forceinline__ void p_rows(const PsMat& M, float eta, int row0, floa
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool DEF>
 __global__ __launch_bounds__(PS_THREADS) void psgd_p(const PsBatch B, int i0, int i1) {
     __shared__ double s_g[4][16];
     const PsMat M = mat_at(B, mat_of_block<MAP_P>(B, i0, i1, blockIdx.x));
@@ -277,9 +335,9 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_p(const PsBatch B, int i0, in
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[rr][j] = 0.0f;
     if (M.m % 4 == 0)
-        p_rows<BF16, 4>(M, B.eta, row0, acc);
+        p_rows<BF16, 4, DEF>(M, B.eta, row0, acc);
     else
-        p_rows<BF16, 1>(M, B.eta, row0, acc);
+        p_rows<BF16, 1, DEF>(M, B.eta, row0, acc);
 #pragma unroll
     for (int rr = 0; rr < P_ROWS_WAVE; ++rr)
 #pragma unroll
@@ -313,7 +371,7 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_p(const PsBatch B, int i0, in
 
 // ------------------------------------------------------------------ psgd_q
 
-template <bool BF16, int VEC>
+template <bool BF16, int VEC, bool DEF>
 __device__ __forceinline__ void q_chunk(const PsMat& M, float eta, int strip, int chunk) {
     const int n = M.n, m = M.m;
     const int col0 = strip * (PS_THREADS * VEC) + threadIdx.x * VEC;
@@ -331,7 +389,18 @@ __device__ __forceinline__ void q_chunk(const PsMat& M, float eta, int strip, in
 #pragma unroll
         for (int u = 0; u < ROW_GROUP; ++u) {
             const int row = min(i0 + u, r1 - 1);
-            load_Mv<BF16, VEC>(M, eta, static_cast<long long>(row) * m + col0, mv[u]);
+            const long long e = static_cast<long long>(row) * m + col0;
+            if constexpr (DEF) {
+                // psgd_p stored M in mem
+                if constexpr (VEC == 4) {
+                    const float4 a = reinterpret_cast<const float4*>(M.mem)[e / 4];
+                    mv[u][0] = a.x; mv[u][1] = a.y; mv[u][2] = a.z; mv[u][3] = a.w;
+                } else {
+                    mv[u][0] = M.mem[e];
+                }
+            } else {
+                load_Mv<BF16, VEC>(M, eta, e, mv[u]);
+            }
         }
 #pragma unroll
         for (int u = 0; u < ROW_GROUP; ++u) {
@@ -352,16 +421,16 @@ __device__ __forceinline__ void q_chunk(const PsMat& M, float eta, int strip, in
     for (int v = 0; v < VEC; ++v) dst[v] = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
 }
 
-template <bool BF16>
+template <bool BF16, bool DEF>
 __global__ __launch_bounds__(PS_THREADS) void psgd_q(const PsBatch B, int i0, int i1) {
     const PsMat M = mat_at(B, mat_of_block<MAP_Q>(B, i0, i1, blockIdx.x));
     const int lwg = blockIdx.x - M.begin_q;
     const int ns = nstrips_of(M.m);
     const int strip = lwg % ns, chunk = lwg / ns;
     if (M.m % 4 == 0)
-        q_chunk<BF16, 4>(M, B.eta, strip, chunk);
+        q_chunk<BF16, 4, DEF>(M, B.eta, strip, chunk);
     else
-        q_chunk<BF16, 1>(M, B.eta, strip, chunk);
+        q_chunk<BF16, 1, DEF>(M, B.eta, strip, chunk);
 }
 
 // ------------------------------------------------------------------ psgd_pq
@@ -382,17 +451,34 @@ struct RawChunk<false> {
 };
 
 template <bool BF16>
-__device__ __forceinline__ float4 raw_to_M(const RawChunk<BF16>& r, float eta) {
-    float4 g;
+__device__ __forceinline__ float4 raw_grad(const RawChunk<BF16>& r) {
     if constexpr (BF16) {
-        g = make_float4(__uint_as_float(r.g.x << 16), __uint_as_float(r.g.x & 0xFFFF0000u),
-                        __uint_as_float(r.g.y << 16), __uint_as_float(r.g.y & 0xFFFF0000u));
+        return make_float4(__uint_as_float(r.g.x << 16), __uint_as_float(r.g.x & 0xFFFF0000u),
+                           __uint_as_float(r.g.y << 16), __uint_as_float(r.g.y & 0xFFFF0000u));
     } else {
-        g = r.g;
+        return r.g;
     }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float4 raw_to_M(const RawChunk<BF16>& r, float eta) {
+    const float4 g = raw_grad<BF16>(r);
     return make_float4(ef_acc(r.m.x, eta, g.x), ef_acc(r.m.y, eta, g.y), ef_acc(r.m.z, eta, g.z),
                        ef_acc(r.m.w, eta, g.w));
 }
+
+// Deferred memory: M = m' + eta*grad with m' = M_prev - P^_prev Q_prev^T
+// rebuilt here from the stored M_prev (4 columns of one row), ph = that row
+// of P^_prev, qr[c] = Q_prev of column c (both zero past the previous rank).
+template <bool BF16>
+__device__ __forceinline__ float4 raw_to_M_def(const RawChunk<BF16>& r, float eta, const float (&ph)[4],
+                                               const float (&qr)[4][4]) {
+    const float4 g = raw_grad<BF16>(r);
+    return make_float4(ef_acc(residual1(r.m.x, ph, qr[0]), eta, g.x), ef_acc(residual1(r.m.y, ph, qr[1]), eta, g.y),
+                       ef_acc(residual1(r.m.z, ph, qr[2]), eta, g.z), ef_acc(residual1(r.m.w, ph, qr[3]), eta, g.w));
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer resources over rows [r0, r1) of a matrix.  The whole byte offset of
 // a load goes into the vector operand, which the hardware checks against the
@@ -440,7 +526,7 @@ __device__ __forceinline__ int rev4(int x) {
 //   5. M^T P accumulators += M[i, cols] P[i, :]; wave 0 stores the P rows and
 //      accumulates the Gram matrix (float64).
 // The accumulators and Gram entries of the workgroup are partial `part`.
-template <bool BF16, int NT, int RG>
+template <bool BF16, int NT, int RG, bool DEF>
 __device__ __forceinline__ void pq_rows(const PsMat& M, float eta, int r0, int r1, int part,
                                         float (*s_part)[NT / 16][4 * RG], int& par) {
     constexpr int V = 4 * RG;          // P entries per row group
@@ -451,12 +537,15 @@ __device__ __forceinline__ void pq_rows(const PsMat& M, float eta, int r0, int r
     const int m = M.m, c4 = m / 4, nr = r1 - r0;
     const bool act = t < c4;
 
-    float q[4][4], qt[4][4];
+    float q[4][4], qt[4][4], qr[4][4];
+    const int qn = DEF ? max(M.rank, M.prank) : M.rank;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (act && j < M.rank) v = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m)[t];
-        q[0][j] = v.x; q[1][j] = v.y; q[2][j] = v.z; q[3][j] = v.w;
+        if (act && j < qn) v = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m)[t];
+        const bool in = j < M.rank, ip = j < M.prank;
+        q[0][j] = in ? v.x : 0.f; q[1][j] = in ? v.y : 0.f; q[2][j] = in ? v.z : 0.f; q[3][j] = in ? v.w : 0.f;
+        qr[0][j] = ip ? v.x : 0.f; qr[1][j] = ip ? v.y : 0.f; qr[2][j] = ip ? v.z : 0.f; qr[3][j] = ip ? v.w : 0.f;
     }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
@@ -492,7 +581,19 @@ __device__ __forceinline__ void pq_rows(const PsMat& M, float eta, int r0, int r
         float v[RG][4];
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
-            const float4 x = raw_to_M<BF16>(raw[r], eta);
+            float4 x;
+            if constexpr (DEF) {
+                // M replaces M_prev in mem; rows past r1 and idle lanes store
+                // nothing.  Rows past r1 read as zero and take a zero P^ row,
+                // so their M stays zero (no P, Gram or M^T P terms)
+                float ph[4] = {0.f, 0.f, 0.f, 0.f};
+                if (k + r < nr) prev_phat_row(M, r0 + k + r, ph);
+                x = raw_to_M_def<BF16>(raw[r], eta, ph, qr);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rm,
+                                                       colm + static_cast<unsigned>(k + r) * rowm, 0, 0);
+            } else {
+                x = raw_to_M<BF16>(raw[r], eta);
+            }
             v[r][0] = x.x; v[r][1] = x.y; v[r][2] = x.z; v[r][3] = x.w;
         }
         load_group(k + RG);
@@ -564,7 +665,7 @@ constexpr int pq_min_waves() { return NT == 256 ? 3 : NT == 512 ? 4 : 4; }
 
 // One pass over the matrices of fused class CLS (m % 4 == 0, m <= 4 NT):
 // workgroup b takes its balanced share of their rows, matrix by matrix.
-template <bool BF16, int NT, int RG>
+template <bool BF16, int NT, int RG, bool DEF>
 __global__ __launch_bounds__(NT, pq_min_waves<NT>()) void psgd_pq(const PsBatch B, int cls) {
     __shared__ float s_part[2][NT / 16][4 * RG];
     const int b = blockIdx.x, G = B.cgrid[cls];
@@ -578,7 +679,7 @@ __global__ __launch_bounds__(NT, pq_min_waves<NT>()) void psgd_pq(const PsBatch 
         int r0, r1;
         rows_in_part(M, s_lo, s_hi, r0, r1);
         if (r0 >= r1) continue;
-        pq_rows<BF16, NT, RG>(M, B.eta, r0, r1, b - owner_of(M.poff - base, E, G), s_part, par);
+        pq_rows<BF16, NT, RG, DEF>(M, B.eta, r0, r1, b - owner_of(M.poff - base, E, G), s_part, par);
     }
 }
 
@@ -606,7 +707,7 @@ __host__ __device__ inline int team_wgs(int vblocks, int cls) {
     return (vblocks + per - 1) / per;
 }
 
-template <bool BF16, int TW>
+template <bool BF16, int TW, bool DEF>
 __device__ __forceinline__ void pq_teams(const PsBatch& B, int cls, int wg_in_class,
                                          float (*s_part)[TEAM_NT / 16][4 * TEAM_RG], int* s_cnt) {
     constexpr int RG = TEAM_RG, V = 4 * RG, NPT = TW / 16, L = 64 / V, TEAMS = TEAM_NT / TW;
@@ -648,7 +749,7 @@ __device__ __forceinline__ void pq_teams(const PsBatch& B, int cls, int wg_in_cl
     int mi = mfirst, r0 = 0, r1 = 0, nr = 0, k = 0, part = 0, m = 1;
     PsMat M{};
     bool act = false;
-    float q[4][4], qt[4][4];
+    float q[4][4], qt[4][4], qr[4][4];
     double g = 0.0;
     __amdgpu_buffer_rsrc_t rm = rows_rsrc(nullptr, 0, 4, 0), rg = rows_rsrc(nullptr, 0, 4, 0);
     unsigned colm = OOB_OFFSET, colg = OOB_OFFSET, rowm = 0, rowg = 0;
@@ -682,11 +783,15 @@ __device__ __forceinline__ void pq_teams(const PsBatch& B, int cls, int wg_in_cl
         part = vb - owner_of(M.poff - base, E, G);
         m = M.m;
         act = tt < m / 4;
+        const int qn = DEF ? max(M.rank, M.prank) : M.rank;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (act && j < M.rank) qv = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m)[tt];
-            q[0][j] = qv.x; q[1][j] = qv.y; q[2][j] = qv.z; q[3][j] = qv.w;
+            if (act && j < qn) qv = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m)[tt];
+            const bool in = j < M.rank, ip = j < M.prank;
+            q[0][j] = in ? qv.x : 0.f; q[1][j] = in ? qv.y : 0.f; q[2][j] = in ? qv.z : 0.f; q[3][j] = in ? qv.w : 0.f;
+            qr[0][j] = ip ? qv.x : 0.f; qr[1][j] = ip ? qv.y : 0.f; qr[2][j] = ip ? qv.z : 0.f;
+            qr[3][j] = ip ? qv.w : 0.f;
         }
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
@@ -714,7 +819,17 @@ __device__ __forceinline__ void pq_teams(const PsBatch& B, int cls, int wg_in_cl
         if (live) {
 #pragma unroll
             for (int r = 0; r < RG; ++r) {
-                const float4 x = raw_to_M<BF16>(raw[r], B.eta);
+                float4 x;
+                if constexpr (DEF) {
+                    // rows past r1: zero data and a zero P^ row give M = 0
+                    float ph[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (k + r < nr) prev_phat_row(M, r0 + k + r, ph);
+                    x = raw_to_M_def<BF16>(raw[r], B.eta, ph, qr);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rm,
+                                                           colm + static_cast<unsigned>(k + r) * rowm, 0, 0);
+                } else {
+                    x = raw_to_M<BF16>(raw[r], B.eta);
+                }
                 v[r][0] = x.x; v[r][1] = x.y; v[r][2] = x.z; v[r][3] = x.w;
             }
             load_group(k + RG);
@@ -786,7 +901,7 @@ __device__ __forceinline__ void pq_teams(const PsBatch& B, int cls, int wg_in_cl
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool DEF>
 __global__ __launch_bounds__(TEAM_NT) void psgd_pq_teams(const PsBatch B) {
     __shared__ float s_part[2][TEAM_NT / 16][4 * TEAM_RG];
     __shared__ int s_cnt[TEAM_NT / 256];
@@ -796,9 +911,9 @@ __global__ __launch_bounds__(TEAM_NT) void psgd_pq_teams(const PsBatch B) {
         if (w < n) break;
         w -= n;
     }
-    if (cls == 0) pq_teams<BF16, 256>(B, 0, w, s_part, s_cnt);
-    else if (cls == 1) pq_teams<BF16, 512>(B, 1, w, s_part, s_cnt);
-    else if (cls == 2) pq_teams<BF16, 1024>(B, 2, w, s_part, s_cnt);
+    if (cls == 0) pq_teams<BF16, 256, DEF>(B, 0, w, s_part, s_cnt);
+    else if (cls == 1) pq_teams<BF16, 512, DEF>(B, 1, w, s_part, s_cnt);
+    else if (cls == 2) pq_teams<BF16, 1024, DEF>(B, 2, w, s_part, s_cnt);
 }
 
 // ------------------------------------------------------------------ psgd_qreduce
@@ -925,13 +1040,22 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
 
 // ------------------------------------------------------------------ psgd_out
 
+// What the output pass does with a row:
+//   OUT_EXPLICIT     M from (mem, grad); out = P^ Q'^T, mem = M - out, P^ into p
+//   OUT_DEFERRED     out = P^ Q'^T and P^ into p only: mem already holds M (the
+//                    first pass stored it) and keeps it as the deferred memory
+//   OUT_MATERIALIZE  mem = M_prev - P^_prev Q_prev^T with P^_prev read from p
+//                    (rank prank): the deferred memory written out
+enum OutMode { OUT_EXPLICIT, OUT_DEFERRED, OUT_MATERIALIZE };
+
 // Rows [r0, r1) of one matrix, one column strip at a time (Q of the strip in
 // registers); loads of ROW_GROUP rows are issued together.  STREAM marks the
 // last reads of mem/grad and the writes of mem/out non-temporal, for batches
 // far larger than the last-level cache.
-template <bool BF16, int VEC, bool STREAM>
+template <bool BF16, int VEC, bool STREAM, int MODE>
 __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int r1) {
-    const int n = M.n, m = M.m, r = M.rank;
+    constexpr bool LOAD = MODE != OUT_DEFERRED;   // reads mem
+    const int n = M.n, m = M.m, r = MODE == OUT_MATERIALIZE ? M.prank : M.rank;
     // P and T were written by earlier kernels and are only read here: the
     // constant address space gives scalar loads that no store has to wait for
     typedef const __attribute__((address_space(4))) double* ConstD;
@@ -963,27 +1087,44 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
                 }
             }
         }
-        const bool write_p = M.p != nullptr && strip == 0 && threadIdx.x < static_cast<unsigned>(r);
+        const bool write_p = MODE != OUT_MATERIALIZE && M.p != nullptr && strip == 0 &&
+                             threadIdx.x < static_cast<unsigned>(r);
         const int colc = active ? col0 : 0;
         for (int i0 = r0; i0 < r1; i0 += ROW_GROUP) {
             float mv[ROW_GROUP][VEC];
+            if constexpr (LOAD) {
 #pragma unroll
-            for (int u = 0; u < ROW_GROUP; ++u) {
-                const int row = min(i0 + u, r1 - 1);
-                load_Mv<BF16, VEC, STREAM>(M, eta, static_cast<long long>(row) * m + colc, mv[u]);
+                for (int u = 0; u < ROW_GROUP; ++u) {
+                    const int row = min(i0 + u, r1 - 1);
+                    const long long e = static_cast<long long>(row) * m + colc;
+                    if constexpr (MODE == OUT_MATERIALIZE) {
+                        if constexpr (VEC == 4) {
+                            const float4 a = reinterpret_cast<const float4*>(M.mem)[e / 4];
+                            mv[u][0] = a.x; mv[u][1] = a.y; mv[u][2] = a.z; mv[u][3] = a.w;
+                        } else {
+                            mv[u][0] = M.mem[e];
+                        }
+                    } else {
+                        load_Mv<BF16, VEC, STREAM>(M, eta, e, mv[u]);
+                    }
+                }
             }
 #pragma unroll
             for (int u = 0; u < ROW_GROUP; ++u) {
                 const int i = i0 + u;
                 if (i >= r1) break;
-                const float prv[4] = {pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
                 float ph[4];
+                if constexpr (MODE == OUT_MATERIALIZE) {
+                    prev_phat_row(M, i, ph);
+                } else {
+                    const float prv[4] = {pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    double v = 0.0;
+                    for (int j = 0; j < 4; ++j) {
+                        double v = 0.0;
 #pragma unroll
-                    for (int a = 0; a <= j; ++a) v = fma(static_cast<double>(prv[a]), T[j * (j + 1) / 2 + a], v);
-                    ph[j] = static_cast<float>(v);
+                        for (int a = 0; a <= j; ++a) v = fma(static_cast<double>(prv[a]), T[j * (j + 1) / 2 + a], v);
+                        ph[j] = static_cast<float>(v);
+                    }
                 }
                 if (write_p) {
                     float mine = ph[0];
@@ -996,35 +1137,37 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
                 float o[VEC], nm[VEC];
 #pragma unroll
                 for (int v = 0; v < VEC; ++v) {
+                    // the sum that residual1 forms, kept for the decoded output
                     float sacc = 0.0f;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) sacc = fmaf(ph[j], qv[v][j], sacc);
                     o[v] = sacc;
-                    nm[v] = mv[u][v] - sacc;
+                    nm[v] = LOAD ? mv[u][v] - sacc : 0.0f;
                 }
+                constexpr bool WRITE_OUT = MODE != OUT_MATERIALIZE, WRITE_MEM = MODE != OUT_DEFERRED;
                 if constexpr (VEC == 4) {
                     const float4 ov = make_float4(o[0], o[1], o[2], o[3]), mv4 = make_float4(nm[0], nm[1], nm[2], nm[3]);
                     float4* const op = reinterpret_cast<float4*>(M.out) + e / 4;
                     float4* const mp = reinterpret_cast<float4*>(M.mem) + e / 4;
                     if constexpr (STREAM) {
-                        if (M.out) store_stream(op, ov);
-                        store_stream(mp, mv4);
+                        if (WRITE_OUT && M.out) store_stream(op, ov);
+                        if (WRITE_MEM) store_stream(mp, mv4);
                     } else {
-                        if (M.out) *op = ov;
-                        *mp = mv4;
+                        if (WRITE_OUT && M.out) *op = ov;
+                        if (WRITE_MEM) *mp = mv4;
                     }
                 } else {
-                    if (M.out) M.out[e] = o[0];
-                    M.mem[e] = nm[0];
+                    if (WRITE_OUT && M.out) M.out[e] = o[0];
+                    if (WRITE_MEM) M.mem[e] = nm[0];
                 }
             }
         }
     }
 }
 
-// Decode + residual for every matrix of the table: workgroup b takes its
-// balanced share of rows.
-template <bool BF16, bool STREAM>
+// Decode + residual for every matrix of the table (MODE: OutMode): workgroup
+// b takes its balanced share of rows.
+template <bool BF16, bool STREAM, int MODE>
 __global__ __launch_bounds__(PS_THREADS) void psgd_out(const PsBatch B) {
     const int b = blockIdx.x, G = B.gout;
     const long long E = B.eall;
@@ -1032,13 +1175,14 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_out(const PsBatch B) {
     for (int i = mat_of_entry(B, 0, B.count, s_lo); i < B.count; ++i) {
         const PsMat M = mat_at(B, i);
         if (M.off >= s_hi) break;
+        if (MODE == OUT_MATERIALIZE && M.prank == 0) continue;   // mem holds the memory already
         int r0, r1;
         rows_in_share(M, s_lo, s_hi, r0, r1);
         if (r0 >= r1) continue;
         if (M.m % 4 == 0)
-            out_rows<BF16, 4, STREAM>(M, B.eta, r0, r1);
+            out_rows<BF16, 4, STREAM, MODE>(M, B.eta, r0, r1);
         else
-            out_rows<BF16, 1, STREAM>(M, B.eta, r0, r1);
+            out_rows<BF16, 1, STREAM, MODE>(M, B.eta, r0, r1);
     }
 }
 
@@ -1191,13 +1335,24 @@ Plan make_plan(const gc_mat* mats, int nmats) {
     return P;
 }
 
-int validate_mat(const gc_mat& a, int i, int dtype) {
-    const std::string pre = "gc_powersgd_ef_step: mats[" + std::to_string(i) + "]: ";
-    if (!a.grad || !a.mem || !a.q) return fail(GC_ERR_ARG, pre + "null grad/mem/q");
+// no_grad: the materialize call, which reads neither grad nor rank.
+int validate_mat(const gc_mat& a, int i, int dtype, const std::string& fn, bool no_grad) {
+    const std::string pre = fn + ": mats[" + std::to_string(i) + "]: ";
+    if ((!no_grad && !a.grad) || !a.mem || !a.q) return fail(GC_ERR_ARG, pre + "null grad/mem/q");
     if (a.n < 1 || a.m < 1) return fail(GC_ERR_ARG, pre + "n and m must be >= 1");
     if (static_cast<long long>(a.n) * a.m > INT32_MAX) return fail(GC_ERR_ARG, pre + "n*m exceeds INT32_MAX");
-    if (a.rank < 1 || a.rank > 4 || a.rank > a.n || a.rank > a.m)
+    if (!no_grad && (a.rank < 1 || a.rank > 4 || a.rank > a.n || a.rank > a.m))
         return fail(GC_ERR_ARG, pre + "rank must be in [1, min(4, n, m)]");
+    if (no_grad) {
+        // only mem, q and p are touched (q and p read, first prev_rank columns)
+        if (!aligned16(a.mem) || !aligned16(a.q) || (a.p && !aligned16(a.p)))
+            return fail(GC_ERR_ARG, pre + "device pointers must be 16-byte aligned");
+        const size_t mb = static_cast<size_t>(a.n) * a.m * 4;
+        const size_t qb = static_cast<size_t>(a.m) * 16, pb = static_cast<size_t>(a.n) * 16;
+        if (overlaps(a.q, qb, a.mem, mb) || (a.p && overlaps(a.p, pb, a.mem, mb)))
+            return fail(GC_ERR_ARG, pre + "buffers overlap");
+        return GC_OK;
+    }
     if (!aligned16(a.grad) || !aligned16(a.mem) || !aligned16(a.q) || (a.p && !aligned16(a.p)) ||
         (a.out && !aligned16(a.out)))
         return fail(GC_ERR_ARG, pre + "device pointers must be 16-byte aligned");
@@ -1213,17 +1368,24 @@ int validate_mat(const gc_mat& a, int i, int dtype) {
     return GC_OK;
 }
 
-// Launches all kernels of one batch: the table copy, the fused classes,
-// the split path, the Q reduction and the output pass.
-template <bool BF16>
-int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& tbl, hipStream_t s) {
-    int rc;
-    // The table goes to the device in stream order.  From pageable memory the
-    // runtime stages the bytes before returning, so `tbl` may go out of scope.
+// The table goes to the device in stream order.  From pageable memory the
+// runtime stages the bytes before returning, so `tbl` may go out of scope.
+int copy_table(const PsBatch& B, const std::vector<PsMat>& tbl, hipStream_t s) {
     const hipError_t e = hipMemcpyAsync(const_cast<PsMat*>(B.tbl), tbl.data(), tbl.size() * sizeof(PsMat),
                                         hipMemcpyHostToDevice, s);
     if (e != hipSuccess)
-        return fail(GC_ERR_HIP, std::string("gc_powersgd_ef_step: matrix table copy: ") + hipGetErrorString(e));
+        return fail(GC_ERR_HIP, std::string("PowerSGD matrix table copy: ") + hipGetErrorString(e));
+    return GC_OK;
+}
+
+// Launches all kernels of one batch: the table copy, the fused classes,
+// the split path, the Q reduction and the output pass.  DEF: the deferred
+// step (the first passes rebuild the previous residual and store M in mem;
+// the output pass writes out and P^ only).
+template <bool BF16, bool DEF>
+int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& tbl, hipStream_t s) {
+    int rc;
+    if ((rc = copy_table(B, tbl, s)) != GC_OK) return rc;
     int fused = 0, team_grid = 0;
     for (int c = 0; c < PQ_CLASSES; ++c) {
         fused += B.cbeg[c + 1] > B.cbeg[c] ? 1 : 0;
@@ -1232,15 +1394,15 @@ int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& t
     if (fused >= 2 && B.eall <= TEAM_MAX_ENTRIES) {
         // small group, several classes: one launch (the classes' passes side by side)
         TimedLaunch tl("psgd_pq", s);
-        psgd_pq_teams<BF16><<<team_grid, TEAM_NT, 0, s>>>(B);
+        psgd_pq_teams<BF16, DEF><<<team_grid, TEAM_NT, 0, s>>>(B);
         if ((rc = check_launch("psgd_pq")) != GC_OK) return rc;
     } else {
         for (int c = 0; c < PQ_CLASSES; ++c) {
             if (B.cbeg[c + 1] == B.cbeg[c]) continue;
             TimedLaunch tl("psgd_pq", s);
-            if (c == 0) psgd_pq<BF16, 256, 8><<<B.cgrid[c], 256, 0, s>>>(B, c);
-            else if (c == 1) psgd_pq<BF16, 512, 4><<<B.cgrid[c], 512, 0, s>>>(B, c);
-            else psgd_pq<BF16, 1024, 4><<<B.cgrid[c], 1024, 0, s>>>(B, c);
+            if (c == 0) psgd_pq<BF16, 256, 8, DEF><<<B.cgrid[c], 256, 0, s>>>(B, c);
+            else if (c == 1) psgd_pq<BF16, 512, 4, DEF><<<B.cgrid[c], 512, 0, s>>>(B, c);
+            else psgd_pq<BF16, 1024, 4, DEF><<<B.cgrid[c], 1024, 0, s>>>(B, c);
             if ((rc = check_launch("psgd_pq")) != GC_OK) return rc;
         }
     }
@@ -1248,12 +1410,12 @@ int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& t
     if (s0 < B.count) {
         {
             TimedLaunch tl("psgd_p", s);
-            psgd_p<BF16><<<pb.np, PS_THREADS, 0, s>>>(B, s0, B.count);
+            psgd_p<BF16, DEF><<<pb.np, PS_THREADS, 0, s>>>(B, s0, B.count);
             if ((rc = check_launch("psgd_p")) != GC_OK) return rc;
         }
         {
             TimedLaunch tl("psgd_q", s);
-            psgd_q<BF16><<<pb.nq, PS_THREADS, 0, s>>>(B, s0, B.count);
+            psgd_q<BF16, DEF><<<pb.nq, PS_THREADS, 0, s>>>(B, s0, B.count);
             if ((rc = check_launch("psgd_q")) != GC_OK) return rc;
         }
     }
@@ -1266,46 +1428,53 @@ int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& t
         TimedLaunch tl("psgd_out", s);
         // streaming accesses only pay when the pass moves far more than the
         // 256 MB last-level cache holds
-        const bool stream = static_cast<double>(B.eall) * (BF16 ? 14.0 : 16.0) > STREAM_MIN_BYTES;
-        if (stream) psgd_out<BF16, true><<<B.gout, PS_THREADS, 0, s>>>(B);
-        else psgd_out<BF16, false><<<B.gout, PS_THREADS, 0, s>>>(B);
+        const double bytes_per_entry = DEF ? 4.0 : (BF16 ? 14.0 : 16.0);
+        const bool stream = static_cast<double>(B.eall) * bytes_per_entry > STREAM_MIN_BYTES;
+        constexpr int MODE = DEF ? OUT_DEFERRED : OUT_EXPLICIT;
+        if (stream) psgd_out<BF16, true, MODE><<<B.gout, PS_THREADS, 0, s>>>(B);
+        else psgd_out<BF16, false, MODE><<<B.gout, PS_THREADS, 0, s>>>(B);
         if ((rc = check_launch("psgd_out")) != GC_OK) return rc;
     }
     return GC_OK;
 }
 
-}  // namespace
-}  // namespace gc
-
-using namespace gc;
-
-extern "C" {
-
-size_t gc_powersgd_workspace_bytes(const gc_mat* mats, int nmats) {
-    if (!mats || nmats < 1) return 0;
-    for (int i = 0; i < nmats; ++i) {
-        const gc_mat& a = mats[i];
-        if (a.n < 1 || a.m < 1 || static_cast<long long>(a.n) * a.m > INT32_MAX) return 0;
-    }
-    return make_plan(mats, nmats).ws_bytes;
+// mem = M_prev - P^_prev Q_prev^T for the matrices with prank > 0.
+int run_materialize(const PsBatch& B, const std::vector<PsMat>& tbl, hipStream_t s) {
+    int rc;
+    if ((rc = copy_table(B, tbl, s)) != GC_OK) return rc;
+    TimedLaunch tl("psgd_materialize", s);
+    psgd_out<false, false, OUT_MATERIALIZE><<<B.gout, PS_THREADS, 0, s>>>(B);
+    return check_launch("psgd_materialize");
 }
 
-int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta,
-                        void* ws, size_t ws_bytes, void* stream) {
-    if (!mats || nmats < 1) return fail(GC_ERR_ARG, "gc_powersgd_ef_step: need mats and nmats >= 1");
+enum StepKind { STEP_EXPLICIT, STEP_DEFERRED, STEP_MATERIALIZE };
+
+// Validation, plan, table and launches shared by the three PowerSGD calls.
+// prank: [host] previous ranks (deferred and materialize calls), else NULL.
+int powersgd_call(const char* fn, StepKind kind, const gc_mat* mats, const int32_t* prank, int nmats,
+                  int grad_dtype, float eta, void* ws, size_t ws_bytes, hipStream_t s) {
+    const std::string f(fn);
+    if (!mats || nmats < 1) return fail(GC_ERR_ARG, f + ": need mats and nmats >= 1");
+    if (kind != STEP_EXPLICIT && !prank) return fail(GC_ERR_ARG, f + ": null prev_rank");
     if (grad_dtype != GC_F32 && grad_dtype != GC_BF16)
-        return fail(GC_ERR_DTYPE, "gc_powersgd_ef_step: grad_dtype must be GC_F32 or GC_BF16");
-    if (!ws) return fail(GC_ERR_ARG, "gc_powersgd_ef_step: null workspace");
-    if (!aligned16(ws)) return fail(GC_ERR_ARG, "gc_powersgd_ef_step: workspace must be 16-byte aligned");
+        return fail(GC_ERR_DTYPE, f + ": grad_dtype must be GC_F32 or GC_BF16");
+    if (!ws) return fail(GC_ERR_ARG, f + ": null workspace");
+    if (!aligned16(ws)) return fail(GC_ERR_ARG, f + ": workspace must be 16-byte aligned");
     for (int i = 0; i < nmats; ++i) {
-        const int rc = validate_mat(mats[i], i, grad_dtype);
+        const int rc = validate_mat(mats[i], i, grad_dtype, f, kind == STEP_MATERIALIZE);
         if (rc != GC_OK) return rc;
+        if (kind != STEP_EXPLICIT) {
+            const gc_mat& a = mats[i];
+            const std::string pre = f + ": mats[" + std::to_string(i) + "]: ";
+            if (!a.p) return fail(GC_ERR_ARG, pre + "p is required (it keeps P^ for the deferred memory)");
+            if (prank[i] < 0 || prank[i] > 4 || prank[i] > a.n || prank[i] > a.m)
+                return fail(GC_ERR_ARG, pre + "prev_rank must be in [0, min(4, n, m)]");
+        }
     }
     const Plan P = make_plan(mats, nmats);
     if (ws_bytes < P.ws_bytes)
-        return fail(GC_ERR_WORKSPACE, "gc_powersgd_ef_step: workspace smaller than gc_powersgd_workspace_bytes");
+        return fail(GC_ERR_WORKSPACE, f + ": workspace smaller than gc_powersgd_workspace_bytes");
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
     char* wp = static_cast<char*>(ws);
     for (const PlanBatch& pb : P.batches) {
         PsBatch B{};
@@ -1343,18 +1512,58 @@ int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta
             M.rcost = a.m + PQ_ROW_COST;
             M.n = a.n;
             M.m = a.m;
-            M.rank = a.rank;
+            M.rank = kind == STEP_MATERIALIZE ? 1 : a.rank;
             M.nq = pm.nq;
             M.ng = pm.ng;
             M.begin_p = pm.begin_p;
             M.begin_q = pm.begin_q;
             M.begin_r = pm.begin_r;
             M.qs = pm.qs;
+            M.prank = kind == STEP_EXPLICIT ? 0 : prank[pm.idx];
         }
-        const int rc = grad_dtype == GC_BF16 ? run_batch<true>(B, pb, tbl, s) : run_batch<false>(B, pb, tbl, s);
+        int rc;
+        if (kind == STEP_MATERIALIZE) rc = run_materialize(B, tbl, s);
+        else if (kind == STEP_DEFERRED)
+            rc = grad_dtype == GC_BF16 ? run_batch<true, true>(B, pb, tbl, s) : run_batch<false, true>(B, pb, tbl, s);
+        else
+            rc = grad_dtype == GC_BF16 ? run_batch<true, false>(B, pb, tbl, s) : run_batch<false, false>(B, pb, tbl, s);
         if (rc != GC_OK) return rc;
     }
     return GC_OK;
+}
+
+}  // namespace
+}  // namespace gc
+
+using namespace gc;
+
+extern "C" {
+
+size_t gc_powersgd_workspace_bytes(const gc_mat* mats, int nmats) {
+    if (!mats || nmats < 1) return 0;
+    for (int i = 0; i < nmats; ++i) {
+        const gc_mat& a = mats[i];
+        if (a.n < 1 || a.m < 1 || static_cast<long long>(a.n) * a.m > INT32_MAX) return 0;
+    }
+    return make_plan(mats, nmats).ws_bytes;
+}
+
+int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta,
+                        void* ws, size_t ws_bytes, void* stream) {
+    return powersgd_call("gc_powersgd_ef_step", STEP_EXPLICIT, mats, nullptr, nmats, grad_dtype, eta, ws, ws_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
+int gc_powersgd_ef_step_deferred(const gc_mat* mats, const int32_t* prev_rank, int nmats, int grad_dtype,
+                                 float eta, void* ws, size_t ws_bytes, void* stream) {
+    return powersgd_call("gc_powersgd_ef_step_deferred", STEP_DEFERRED, mats, prev_rank, nmats, grad_dtype, eta, ws,
+                         ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int gc_powersgd_materialize(const gc_mat* mats, const int32_t* prev_rank, int nmats, void* ws, size_t ws_bytes,
+                            void* stream) {
+    return powersgd_call("gc_powersgd_materialize", STEP_MATERIALIZE, mats, prev_rank, nmats, GC_F32, 1.0f, ws,
+                         ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

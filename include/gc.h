@@ -153,13 +153,59 @@ size_t gc_powersgd_workspace_bytes(const gc_mat* mats, int nmats);
  *     out = P^ Q^T;  mem = M - out
  * float32 storage; the Gram matrix and the orthonormalisation are in float64.
  * Buffers of different matrices must not overlap.
- * The call copies a small matrix table (120 bytes per matrix) from host memory
+ * The call copies a small matrix table (136 bytes per matrix) from host memory
  * into ws with one hipMemcpyAsync on `stream`, then enqueues the kernels; the
  * host array may be reused as soon as the call returns.  Because of that copy
  * the call is not for graph capture (a replay would read freed host memory).
  * Errors: GC_ERR_ARG, GC_ERR_DTYPE, GC_ERR_WORKSPACE, GC_ERR_HIP. */
 int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* The same PowerSGD step with the error-feedback memory kept in deferred form.
+ * The memory the method carries to the next step, m' = M - P^ Q^T, is not
+ * written out.  It is held as three parts instead: mem keeps M, p keeps P^
+ * (the first `rank` columns) and q keeps Q.  The next deferred call rebuilds
+ * m' from them in its first pass over mem, then forms M = m' + eta*grad and
+ * stores M over mem.  The output pass writes only out and p.
+ *
+ * This is the memory convention of Mem-SGD (Sparsified SGD with Memory,
+ * method section: the memory keeps what the compressed update left out),
+ * held as the factors that define it.
+ * Each entry moves (grad bytes + 12) bytes per step instead of
+ * (grad bytes + 12) + (grad bytes + 4): M is read once, not twice.
+ * out, q and p get the bits of gc_powersgd_ef_step.  After
+ * gc_powersgd_materialize, mem holds that call's bits too (the residual is
+ * formed with the same float32 operations in the same order).
+ *
+ * prev_rank ([host], nmats entries) says what mem holds on entry:
+ *   0      mem holds the memory itself (the first call, or after
+ *          gc_powersgd_materialize);
+ *   r' > 0 mem holds M of the previous deferred call, and its P^ and Q are
+ *          still in the first r' columns of p and q.  r' is that call's rank.
+ * On return mem holds M of this call: pass prev_rank[i] = mats[i].rank next
+ * time.
+ * On a rank change, columns past r' of q may be refilled (a warm start for a
+ * higher rank) before the call.  The first min(r', rank) columns must be
+ * left as the previous call wrote them.
+ * p is required (non-NULL), since it carries P^ to the next call.
+ * Workspace: gc_powersgd_workspace_bytes on the same array.
+ * Errors: those of gc_powersgd_ef_step, and GC_ERR_ARG for a NULL prev_rank,
+ * a NULL p, or prev_rank[i] outside [0, min(4, n, m)]. */
+int gc_powersgd_ef_step_deferred(const gc_mat* mats, const int32_t* prev_rank, int nmats, int grad_dtype,
+                                 float eta, void* ws, size_t ws_bytes, void* stream);
+
+/* Writes the deferred memory out: for every matrix with prev_rank[i] > 0,
+ * mem = mem - P^ Q^T over the first prev_rank[i] columns of p and q.
+ * Afterwards mem holds m', bit for bit what gc_powersgd_ef_step would have
+ * left there, and the next step takes prev_rank 0.
+ * Reads mem, p and q; grad, rank and out are not used (grad may be NULL).
+ * Matrices with prev_rank[i] == 0 are left alone.
+ * Workspace: gc_powersgd_workspace_bytes on the same array.
+ * Errors: GC_ERR_ARG (NULL mats, prev_rank, mem, q or p where
+ * prev_rank[i] > 0; prev_rank out of range; misaligned or overlapping
+ * buffers), GC_ERR_WORKSPACE, GC_ERR_HIP. */
+int gc_powersgd_materialize(const gc_mat* mats, const int32_t* prev_rank, int nmats, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Accordion: per-layer norms and the l_low / l_high switch                 */

@@ -164,6 +164,32 @@ def test_powersgd_validation(gcl):
     assert step(mats(), wsb=need - 1) == gcl.GC_ERR_WORKSPACE
     assert L.gc_powersgd_ef_step(mats(), 0, 0, 1.0, 0x900000, big, None) == gcl.GC_ERR_ARG
 
+    # the deferred step and the materialize call: every case fails validation
+    def prev(*r):
+        return (C.c_int32 * len(r))(*r)
+
+    def dstep(arr, pr, dt=gcl.GC_F32, wsb=big):
+        return L.gc_powersgd_ef_step_deferred(arr, pr, 1, dt, 1.0, 0x900000, wsb, None)
+
+    def mat(arr, pr, wsb=big):
+        return L.gc_powersgd_materialize(arr, pr, 1, 0x900000, wsb, None)
+
+    assert dstep(mats(), None) == gcl.GC_ERR_ARG                      # NULL prev_rank
+    assert dstep(mats(p=None), prev(0)) == gcl.GC_ERR_ARG             # p is required
+    assert dstep(mats(), prev(5)) == gcl.GC_ERR_ARG                   # prev_rank > 4
+    assert dstep(mats(), prev(-1)) == gcl.GC_ERR_ARG
+    assert dstep(mats(n=3, rank=2), prev(4)) == gcl.GC_ERR_ARG        # prev_rank > min(n, m)
+    assert dstep(mats(rank=0), prev(0)) == gcl.GC_ERR_ARG
+    assert dstep(mats(grad=None), prev(0)) == gcl.GC_ERR_ARG
+    assert dstep(mats(), prev(2), dt=3) == gcl.GC_ERR_DTYPE
+    assert dstep(mats(), prev(2), wsb=need - 1) == gcl.GC_ERR_WORKSPACE
+    assert mat(mats(), None) == gcl.GC_ERR_ARG
+    assert mat(mats(p=None), prev(2)) == gcl.GC_ERR_ARG
+    assert mat(mats(mem=None), prev(2)) == gcl.GC_ERR_ARG
+    assert mat(mats(grad=None), prev(7)) == gcl.GC_ERR_ARG            # grad may be NULL, prev_rank may not be 7
+    assert mat(mats(grad=None), prev(2), wsb=need - 1) == gcl.GC_ERR_WORKSPACE
+    assert mat(mats(grad=None, p=0x200000 + 64), prev(2)) == gcl.GC_ERR_ARG   # p inside mem
+
 
 @no_gpu
 def test_norm_validation(gcl):
