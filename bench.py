@@ -39,6 +39,8 @@ import gen  # noqa: E402
 METRIC = "gradient GB/s through encode+decode+EF (µs/step) at 1 GPU; % of HBM peak"
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
+# PowerSGD memory form: deferred (gc_powersgd_ef_step_deferred) unless --explicit
+PSGD_DEFERRED = True
 
 
 def parse():
@@ -48,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c3acc", "c3randk", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--explicit", action="store_true",
+                    help="PowerSGD workloads: write the memory out every step (gc_powersgd_ef_step) instead of "
+                         "keeping it in deferred form (gc_powersgd_ef_step_deferred)")
     ap.add_argument("--flush", action="store_true",
                     help="between timed steps write 1 GiB, then read 1 GiB (cold last-level cache, no dirty lines)")
     ap.add_argument("--copy-calib", action="store_true", help="only run a 1 GiB device copy (counter calibration)")
@@ -85,8 +90,13 @@ def _upload_bf16(torch, dst, bits):
 class PowersgdPart:
     """Device buffers + ctypes table for a list of matrices sharing one flat memory buffer."""
 
-    def __init__(self, torch, gc, shapes, ranks, grad_views_per_set, mem_views, dev, qcfg):
+    def __init__(self, torch, gc, shapes, ranks, grad_views_per_set, mem_views, dev, qcfg, deferred=None):
         self.gc = gc
+        # deferred: the memory is kept as (M, P^, Q) and rebuilt in the next
+        # step's first pass (gc_powersgd_ef_step_deferred); prev = the ranks
+        # of the previous call (0: mem holds the memory itself)
+        self.deferred = PSGD_DEFERRED if deferred is None else deferred
+        self.prev = [0] * len(shapes)
         self.shapes = shapes
         self.ranks = list(ranks)
         self.q = [torch.from_numpy(gen.q_init(qcfg, l, m)).to(dev) for l, (n, m) in enumerate(shapes)]
@@ -96,19 +106,23 @@ class PowersgdPart:
         self.mem = [mv.view(n, m) for mv, (n, m) in zip(mem_views, shapes)]
         self.grads = [[g.view(n, m) for g, (n, m) in zip(gs, shapes)] for gs in grad_views_per_set]
         self.tables = [self._mats(s) for s in range(len(self.grads))]
-        self.ws = torch.empty(gc.gc_powersgd_workspace_bytes(self._mats(0)), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(gc.gc_powersgd_workspace_bytes(self._mats(0).mats), dtype=torch.uint8, device=dev)
 
     def _mats(self, s):
         gc = self.gc
-        return [gc.Mat(grad=self.grads[s][i], mem=self.mem[i], q=self.q[i], rank=self.ranks[i], p=self.p[i],
-                       out=self.out[i]) for i in range(len(self.shapes))]
+        return gc.MatArray([gc.Mat(grad=self.grads[s][i], mem=self.mem[i], q=self.q[i], rank=self.ranks[i],
+                                   p=self.p[i], out=self.out[i]) for i in range(len(self.shapes))])
 
     def set_ranks(self, ranks):
         self.ranks = list(ranks)
         self.tables = [self._mats(s) for s in range(len(self.grads))]
 
     def step(self, s, eta=1.0):
-        self.gc.gc_powersgd_ef_step(self.tables[s], eta, self.ws)
+        if self.deferred:
+            self.gc.gc_powersgd_ef_step_deferred(self.tables[s], self.prev, eta, self.ws)
+            self.prev = self.ranks
+        else:
+            self.gc.gc_powersgd_ef_step(self.tables[s], eta, self.ws)
 
 
 def psgd_bytes(shapes, ranks, sg):
@@ -122,17 +136,38 @@ def fused_split_elems(shapes):
     return fused, sum(n * m for n, m in shapes) - fused
 
 
-def psgd_kernel_bytes(shapes, ranks, sg):
-    """Algorithmic bytes of each PowerSGD kernel per step: the first pass reads
-    M's inputs (grad + memory) once, psgd_out reads them again and writes
-    memory and the decoded output."""
+def psgd_kernel_bytes(shapes, ranks, sg, deferred=None):
+    """Bytes each PowerSGD kernel must move per step.
+
+    deferred (gc_powersgd_ef_step_deferred): the first pass reads the stored M
+    of the last step and the gradient, writes the new M and reads Q_in
+    ((sg + 8) n m + 4 r m); psgd_out writes the decoded output and P^ and reads
+    Q' (4 n m + 4 r (n + m)).  These add up to the step's algorithmic bytes
+    (sg + 12) n m + 4 r (n + 2 m).  The split path's psgd_q reads M again
+    (4 n m).
+    explicit (gc_powersgd_ef_step): the first pass reads grad + memory; psgd_out
+    reads them again and writes memory and output (it is charged the step's
+    whole algorithmic bytes)."""
     fused, split = fused_split_elems(shapes)
-    kb = {"psgd_out": psgd_bytes(shapes, ranks, sg)}
+    if deferred is None:
+        deferred = PSGD_DEFERRED
+    if not deferred:
+        kb = {"psgd_out": psgd_bytes(shapes, ranks, sg)}
+        if fused:
+            kb["psgd_pq"] = (sg + 4) * fused
+        if split:
+            kb["psgd_p"] = (sg + 4) * split
+            kb["psgd_q"] = (sg + 4) * split
+        return kb
+    kb = {"psgd_decode": sum(4 * n * m + 4 * r * (n + m) for (n, m), r in zip(shapes, ranks))}
+    qin = {True: 0, False: 0}
+    for (n, m), r in zip(shapes, ranks):
+        qin[m % 4 == 0 and m <= 4096] += 4 * r * m
     if fused:
-        kb["psgd_pq"] = (sg + 4) * fused
+        kb["psgd_pq"] = (sg + 8) * fused + qin[True]
     if split:
-        kb["psgd_p"] = (sg + 4) * split
-        kb["psgd_q"] = (sg + 4) * split
+        kb["psgd_p"] = (sg + 8) * split + qin[False]
+        kb["psgd_q"] = 4 * split
     return kb
 
 
@@ -183,6 +218,8 @@ class C5(Workload):
         self.config = {"workload": "bert-large gradient set", "params": total, "matrices": len(shapes),
                        "powersgd_rank": 4, "embedding": list(gen.BERT_EMB), "topk_k": self.k,
                        "grad_dtype": "bf16", "memory_dtype": "f32", "eta": 1.0, "accordion_check_every": 10}
+        self.config["powersgd_memory"] = "deferred: (M, P^, Q) kept, residual rebuilt in the next step's first pass" \
+            if self.ps.deferred else "explicit: written out every step"
 
     def step(self, t):
         gc, s = self.gc, t % 2
@@ -226,6 +263,8 @@ class C2(Workload):
         self.description = gen.WORKLOADS["c2"].description + f" (rank {rank})"
         self.config = {"workload": "resnet18 gradient set", "params": me, "powersgd_rank": rank,
                        "grad_dtype": "f32", "memory_dtype": "f32"}
+        self.config["powersgd_memory"] = "deferred: (M, P^, Q) kept, residual rebuilt in the next step's first pass" \
+            if self.ps.deferred else "explicit: written out every step"
 
     def step(self, t):
         self.ps.step(t % 2)
@@ -365,6 +404,8 @@ class C4(Workload):
         self.description = gen.WORKLOADS["c4"].description
         self.config = {"workload": "vgg19 gradient set", "params": me, "levels": "l_low=rank4, l_high=rank2",
                        "grad_dtype": "f32", "memory_dtype": "f32", "accordion_check_every": 10}
+        self.config["powersgd_memory"] = "deferred: (M, P^, Q) kept, residual rebuilt in the next step's first pass" \
+            if self.ps.deferred else "explicit: written out every step"
 
     def step(self, t):
         gc, s = self.gc, t % 2
@@ -540,6 +581,8 @@ def main():
         return
 
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
+    global PSGD_DEFERRED
+    PSGD_DEFERRED = not args.explicit
     W = {"c5": C5, "c2": C2, "c3": C3, "c3acc": C3Acc, "c3randk": C3Randk, "c4": C4}[args.workload](torch, gc, dev)
     if hasattr(W, "prepare"):
         W.prepare(args.warmup + args.steps + 2)

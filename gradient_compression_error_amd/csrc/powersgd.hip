@@ -88,7 +88,7 @@ struct PsMat {
     int qs;          // psgd_qreduce threads per column
     int rcost;       // fused classes: partition units per row (m + PQ_ROW_COST)
     int prank;       // deferred memory: rank of the previous step's P^, Q (0: mem holds the memory itself)
-    int pad_;
+    int begin_d;     // deferred step: first workgroup of the matrix in psgd_decode
 };
 static_assert(sizeof(PsMat) % 8 == 0, "table entries are copied as words");
 static_assert(sizeof(PsMat) == 136, "table entry size stated in gc.h");
@@ -152,13 +152,14 @@ __device__ __forceinline__ int mat_of_entry(const PsBatch& B, int i0, int i1, lo
     return lo;
 }
 
-enum BlockMap { MAP_P, MAP_Q, MAP_R };
+enum BlockMap { MAP_P, MAP_Q, MAP_R, MAP_D };
 
 template <BlockMap K>
 __device__ __forceinline__ int first_block(MatTable T, int i) {
     if constexpr (K == MAP_P) return T[i].begin_p;
     else if constexpr (K == MAP_Q) return T[i].begin_q;
-    else return T[i].begin_r;
+    else if constexpr (K == MAP_R) return T[i].begin_r;
+    else return T[i].begin_d;
 }
 
 // Matrix of workgroup blk among matrices [i0, i1) (last i with first block <= blk).
@@ -1053,7 +1054,7 @@ enum OutMode { OUT_EXPLICIT, OUT_DEFERRED, OUT_MATERIALIZE };
 // last reads of mem/grad and the writes of mem/out non-temporal, for batches
 // far larger than the last-level cache.
 template <bool BF16, int VEC, bool STREAM, int MODE>
-__device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int r1) {
+__device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int r1, int s0 = 0, int s1 = 1 << 30) {
     constexpr bool LOAD = MODE != OUT_DEFERRED;   // reads mem
     const int n = M.n, m = M.m, r = MODE == OUT_MATERIALIZE ? M.prank : M.rank;
     // P and T were written by earlier kernels and are only read here: the
@@ -1069,8 +1070,8 @@ __device__ __forceinline__ void out_rows(const PsMat& M, float eta, int r0, int 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int a = 0; a <= j; ++a) T[j * (j + 1) / 2 + a] = tm[a * 4 + j];
-    const int ns = nstrips_of(m);
-    for (int strip = 0; strip < ns; ++strip) {
+    const int ns = min(s1, nstrips_of(m));
+    for (int strip = s0; strip < ns; ++strip) {
         const int col0 = strip * (PS_THREADS * VEC) + threadIdx.x * VEC;
         const bool active = col0 < m;
         float qv[VEC][4];
@@ -1186,6 +1187,29 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_out(const PsBatch B) {
     }
 }
 
+// Output pass of the deferred step: out = P^ Q'^T and P^ into p, nothing
+// read but P, T and Q'.  A write-only pass runs fastest as many short
+// workgroups dispatched in address order (the writes sweep memory front to
+// back) rather than as a persistent grid of long contiguous shares: one
+// workgroup per DEC_ROWS rows x one column strip of a matrix.
+constexpr int DEC_ROWS = ROW_GROUP;
+// launch groups whose psgd_decode grid would exceed this take the persistent
+// psgd_out pass instead (the grid is an int)
+constexpr long long DEC_GRID_MAX = 1LL << 30;
+
+template <bool STREAM>
+__global__ __launch_bounds__(PS_THREADS) void psgd_decode(const PsBatch B) {
+    const PsMat M = mat_at(B, mat_of_block<MAP_D>(B, 0, B.count, blockIdx.x));
+    const int lwg = blockIdx.x - M.begin_d;
+    const int ns = nstrips_of(M.m);
+    const int strip = lwg % ns, r0 = (lwg / ns) * DEC_ROWS;
+    const int r1 = min(M.n, r0 + DEC_ROWS);
+    if (M.m % 4 == 0)
+        out_rows<false, 4, STREAM, OUT_DEFERRED>(M, B.eta, r0, r1, strip, strip + 1);
+    else
+        out_rows<false, 1, STREAM, OUT_DEFERRED>(M, B.eta, r0, r1, strip, strip + 1);
+}
+
 // ------------------------------------------------------------------ host side
 
 int nstrips_host(int m) {
@@ -1211,7 +1235,7 @@ struct PlanMat {
     long long off;      // first entry within the batch
     long long poff;     // fused classes: first partition unit within the batch
     int nq, ng;         // partial counts
-    int begin_p, begin_q, begin_r;
+    int begin_p, begin_q, begin_r, begin_d;
     int qs;             // psgd_qreduce threads per column
     size_t ws_off;      // workspace offset of this matrix's scratch
 };
@@ -1224,6 +1248,7 @@ struct PlanBatch {
     long long eall;
     int gout;
     int np, nq, nr;                    // psgd_p / psgd_q / psgd_qreduce grids
+    long long nd;                      // psgd_decode grid
 };
 struct Plan {
     std::vector<PlanMat> mats;
@@ -1317,6 +1342,8 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             pm.begin_r = pb.nr;
             const int qc = PS_THREADS / pm.qs;
             pb.nr += (m + qc - 1) / qc;
+            pm.begin_d = static_cast<int>(std::min<long long>(pb.nd, DEC_GRID_MAX));
+            pb.nd += static_cast<long long>((n + DEC_ROWS - 1) / DEC_ROWS) * nstrips_host(m);
             pm.ws_off = o;
             o += ws_round(static_cast<size_t>(n) * 16);                       // praw
             o += ws_round(static_cast<size_t>(pm.ng) * 16 * 8);               // gpart
@@ -1425,15 +1452,23 @@ int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& t
         if ((rc = check_launch("psgd_qreduce")) != GC_OK) return rc;
     }
     {
-        TimedLaunch tl("psgd_out", s);
+        const bool decode = DEF && pb.nd <= DEC_GRID_MAX;
+        TimedLaunch tl(decode ? "psgd_decode" : "psgd_out", s);
         // streaming accesses only pay when the pass moves far more than the
         // 256 MB last-level cache holds
         const double bytes_per_entry = DEF ? 4.0 : (BF16 ? 14.0 : 16.0);
         const bool stream = static_cast<double>(B.eall) * bytes_per_entry > STREAM_MIN_BYTES;
         constexpr int MODE = DEF ? OUT_DEFERRED : OUT_EXPLICIT;
-        if (stream) psgd_out<BF16, true, MODE><<<B.gout, PS_THREADS, 0, s>>>(B);
-        else psgd_out<BF16, false, MODE><<<B.gout, PS_THREADS, 0, s>>>(B);
-        if ((rc = check_launch("psgd_out")) != GC_OK) return rc;
+        if (decode) {
+            const unsigned grid = static_cast<unsigned>(pb.nd);
+            if (stream) psgd_decode<true><<<grid, PS_THREADS, 0, s>>>(B);
+            else psgd_decode<false><<<grid, PS_THREADS, 0, s>>>(B);
+        } else if (stream) {
+            psgd_out<BF16, true, MODE><<<B.gout, PS_THREADS, 0, s>>>(B);
+        } else {
+            psgd_out<BF16, false, MODE><<<B.gout, PS_THREADS, 0, s>>>(B);
+        }
+        if ((rc = check_launch(decode ? "psgd_decode" : "psgd_out")) != GC_OK) return rc;
     }
     return GC_OK;
 }
@@ -1518,6 +1553,7 @@ int powersgd_call(const char* fn, StepKind kind, const gc_mat* mats, const int32
             M.begin_p = pm.begin_p;
             M.begin_q = pm.begin_q;
             M.begin_r = pm.begin_r;
+            M.begin_d = pm.begin_d;
             M.qs = pm.qs;
             M.prank = kind == STEP_EXPLICIT ? 0 : prank[pm.idx];
         }
