@@ -88,10 +88,11 @@ struct PsMat {
     int qs;          // psgd_qreduce threads per column
     int rcost;       // fused classes: partition units per row (m + PQ_ROW_COST)
     int prank;       // deferred memory: rank of the previous step's P^, Q (0: mem holds the memory itself)
-    int begin_d;     // deferred step: first workgroup of the matrix in psgd_decode
+    int pad_;
+    long long dbeg;  // deferred step: first psgd_decode tile of the matrix
 };
 static_assert(sizeof(PsMat) % 8 == 0, "table entries are copied as words");
-static_assert(sizeof(PsMat) == 136, "table entry size stated in gc.h");
+static_assert(sizeof(PsMat) == 144, "table entry size stated in gc.h");
 
 // Fused-pass classes by row length: m <= 1024, m <= 2048, m <= 4096 (m % 4 == 0),
 // each with its own workgroup width; the rest take the split path.
@@ -152,14 +153,13 @@ __device__ __forceinline__ int mat_of_entry(const PsBatch& B, int i0, int i1, lo
     return lo;
 }
 
-enum BlockMap { MAP_P, MAP_Q, MAP_R, MAP_D };
+enum BlockMap { MAP_P, MAP_Q, MAP_R };
 
 template <BlockMap K>
 __device__ __forceinline__ int first_block(MatTable T, int i) {
     if constexpr (K == MAP_P) return T[i].begin_p;
     else if constexpr (K == MAP_Q) return T[i].begin_q;
-    else if constexpr (K == MAP_R) return T[i].begin_r;
-    else return T[i].begin_d;
+    else return T[i].begin_r;
 }
 
 // Matrix of workgroup blk among matrices [i0, i1) (last i with first block <= blk).
@@ -1190,24 +1190,36 @@ __global__ __launch_bounds__(PS_THREADS) void psgd_out(const PsBatch B) {
 // Output pass of the deferred step: out = P^ Q'^T and P^ into p, nothing
 // read but P, T and Q'.  A write-only pass runs fastest as many short
 // workgroups dispatched in address order (the writes sweep memory front to
-// back) rather than as a persistent grid of long contiguous shares: one
-// workgroup per DEC_ROWS rows x one column strip of a matrix.
+// back) rather than as a persistent grid of long contiguous shares.  Tile t
+// is DEC_ROWS rows x one column strip of one matrix; the tiles of a matrix
+// start at its dbeg, in row-major order of (row block, strip).  Workgroup b
+// takes tiles b, b + grid, ... (one each unless the batch has more than
+// DEC_GRID_MAX tiles).
 constexpr int DEC_ROWS = ROW_GROUP;
-// launch groups whose psgd_decode grid would exceed this take the persistent
-// psgd_out pass instead (the grid is an int)
 constexpr long long DEC_GRID_MAX = 1LL << 30;
 
 template <bool STREAM>
-__global__ __launch_bounds__(PS_THREADS) void psgd_decode(const PsBatch B) {
-    const PsMat M = mat_at(B, mat_of_block<MAP_D>(B, 0, B.count, blockIdx.x));
-    const int lwg = blockIdx.x - M.begin_d;
-    const int ns = nstrips_of(M.m);
-    const int strip = lwg % ns, r0 = (lwg / ns) * DEC_ROWS;
-    const int r1 = min(M.n, r0 + DEC_ROWS);
-    if (M.m % 4 == 0)
-        out_rows<false, 4, STREAM, OUT_DEFERRED>(M, B.eta, r0, r1, strip, strip + 1);
-    else
-        out_rows<false, 1, STREAM, OUT_DEFERRED>(M, B.eta, r0, r1, strip, strip + 1);
+__global__ __launch_bounds__(PS_THREADS) void psgd_decode(const PsBatch B, long long ntiles) {
+    const MatTable T = mat_table(B);
+    for (long long t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        // last matrix whose first tile is <= t
+        int lo = 0, hi = B.count;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (T[mid].dbeg <= t) lo = mid;
+            else hi = mid;
+        }
+        const PsMat M = mat_at(B, lo);
+        const long long lt = t - M.dbeg;
+        const int ns = nstrips_of(M.m);
+        const int strip = static_cast<int>(lt % ns);
+        const int r0 = static_cast<int>((lt / ns) * DEC_ROWS);
+        const int r1 = min(M.n, r0 + DEC_ROWS);
+        if (M.m % 4 == 0)
+            out_rows<false, 4, STREAM, OUT_DEFERRED>(M, B.eta, r0, r1, strip, strip + 1);
+        else
+            out_rows<false, 1, STREAM, OUT_DEFERRED>(M, B.eta, r0, r1, strip, strip + 1);
+    }
 }
 
 // ------------------------------------------------------------------ host side
@@ -1235,7 +1247,8 @@ struct PlanMat {
     long long off;      // first entry within the batch
     long long poff;     // fused classes: first partition unit within the batch
     int nq, ng;         // partial counts
-    int begin_p, begin_q, begin_r, begin_d;
+    int begin_p, begin_q, begin_r;
+    long long dbeg;     // first psgd_decode tile
     int qs;             // psgd_qreduce threads per column
     size_t ws_off;      // workspace offset of this matrix's scratch
 };
@@ -1342,7 +1355,7 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             pm.begin_r = pb.nr;
             const int qc = PS_THREADS / pm.qs;
             pb.nr += (m + qc - 1) / qc;
-            pm.begin_d = static_cast<int>(std::min<long long>(pb.nd, DEC_GRID_MAX));
+            pm.dbeg = pb.nd;
             pb.nd += static_cast<long long>((n + DEC_ROWS - 1) / DEC_ROWS) * nstrips_host(m);
             pm.ws_off = o;
             o += ws_round(static_cast<size_t>(n) * 16);                       // praw
@@ -1452,23 +1465,22 @@ int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& t
         if ((rc = check_launch("psgd_qreduce")) != GC_OK) return rc;
     }
     {
-        const bool decode = DEF && pb.nd <= DEC_GRID_MAX;
-        TimedLaunch tl(decode ? "psgd_decode" : "psgd_out", s);
+        const char* name = DEF ? "psgd_decode" : "psgd_out";
+        TimedLaunch tl(name, s);
         // streaming accesses only pay when the pass moves far more than the
         // 256 MB last-level cache holds
         const double bytes_per_entry = DEF ? 4.0 : (BF16 ? 14.0 : 16.0);
         const bool stream = static_cast<double>(B.eall) * bytes_per_entry > STREAM_MIN_BYTES;
-        constexpr int MODE = DEF ? OUT_DEFERRED : OUT_EXPLICIT;
-        if (decode) {
-            const unsigned grid = static_cast<unsigned>(pb.nd);
-            if (stream) psgd_decode<true><<<grid, PS_THREADS, 0, s>>>(B);
-            else psgd_decode<false><<<grid, PS_THREADS, 0, s>>>(B);
+        if constexpr (DEF) {
+            const unsigned grid = static_cast<unsigned>(std::min<long long>(pb.nd, DEC_GRID_MAX));
+            if (stream) psgd_decode<true><<<grid, PS_THREADS, 0, s>>>(B, pb.nd);
+            else psgd_decode<false><<<grid, PS_THREADS, 0, s>>>(B, pb.nd);
         } else if (stream) {
-            psgd_out<BF16, true, MODE><<<B.gout, PS_THREADS, 0, s>>>(B);
+            psgd_out<BF16, true, OUT_EXPLICIT><<<B.gout, PS_THREADS, 0, s>>>(B);
         } else {
-            psgd_out<BF16, false, MODE><<<B.gout, PS_THREADS, 0, s>>>(B);
+            psgd_out<BF16, false, OUT_EXPLICIT><<<B.gout, PS_THREADS, 0, s>>>(B);
         }
-        if ((rc = check_launch(decode ? "psgd_decode" : "psgd_out")) != GC_OK) return rc;
+        if ((rc = check_launch(name)) != GC_OK) return rc;
     }
     return GC_OK;
 }
@@ -1553,7 +1565,7 @@ int powersgd_call(const char* fn, StepKind kind, const gc_mat* mats, const int32
             M.begin_p = pm.begin_p;
             M.begin_q = pm.begin_q;
             M.begin_r = pm.begin_r;
-            M.begin_d = pm.begin_d;
+            M.dbeg = pm.dbeg;
             M.qs = pm.qs;
             M.prank = kind == STEP_EXPLICIT ? 0 : prank[pm.idx];
         }

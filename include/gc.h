@@ -153,7 +153,7 @@ size_t gc_powersgd_workspace_bytes(const gc_mat* mats, int nmats);
  *     out = P^ Q^T;  mem = M - out
  * float32 storage; the Gram matrix and the orthonormalisation are in float64.
  * Buffers of different matrices must not overlap.
- * The call copies a small matrix table (136 bytes per matrix) from host memory
+ * The call copies a small matrix table (144 bytes per matrix) from host memory
  * into ws with one hipMemcpyAsync on `stream`, then enqueues the kernels; the
  * host array may be reused as soon as the call returns.  Because of that copy
  * the call is not for graph capture (a replay would read freed host memory).

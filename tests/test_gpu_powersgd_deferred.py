@@ -231,3 +231,33 @@ def test_bert_large_set():
         compare_bitwise(A, B, f"BERT-large step {t}")
     del grads, A, B
     torch.cuda.empty_cache()
+
+
+def test_several_launch_groups():
+    """4100 small matrices (more than one launch group of 4096), fused and split
+    shapes mixed, mixed ranks: the per-group tables and decode tiles."""
+    print("case: deferred vs explicit, 4100 matrices", flush=True)
+    shapes = [(3 + i % 5, 8 if i % 3 else 5) for i in range(4100)]
+    ranks = [1 + i % 3 for i in range(4100)]
+    run_pair(shapes, ranks, lambda t: [gen.gaussian_mat(n, m, 1300 + 7 * t + i, 1e-2) for i, (n, m) in
+                                       enumerate(shapes)], 2, label="4100 matrices")
+
+
+def test_max_size_one_matrix():
+    """One 524287 x 4096 matrix (n*m = 2^31 - 4096, the largest the ABI takes),
+    bf16 gradients drawn on the device, rank 4: three deferred steps against
+    three explicit ones, compared on the device bit for bit (out, P^, Q, and
+    the memory written out by gc_powersgd_materialize)."""
+    n, m, r = 524287, 4096, 4
+    print(f"case: deferred vs explicit, max size {n}x{m} r={r} bf16", flush=True)
+    rng_t = torch.Generator(device=DEV)
+    rng_t.manual_seed(93)
+    A, B = Set([(n, m)], [r], gen.CFG_C5), Set([(n, m)], [r], gen.CFG_C5)
+    for t in range(3):
+        g = (torch.randn(n, m, generator=rng_t, dtype=torch.float32, device=DEV) * 1e-3).to(torch.bfloat16)
+        A.explicit([g], 1.0)
+        B.deferred([g], 1.0)
+        del g
+        compare_bitwise(A, B, f"max size step {t}")
+    del A, B
+    torch.cuda.empty_cache()
