@@ -34,14 +34,19 @@ std::vector<EventPair> g_events;
 TimedLaunch::TimedLaunch(const char* name, hipStream_t stream) : stream_(stream) {
     std::lock_guard<std::mutex> lk(g_tmu);
     if (g_timed_name.empty() || g_timed_name != name) return;
-    if (hipEventCreate(&start_) != hipSuccess) { start_ = nullptr; return; }
+    // timing-only events: no system-scope fence (its cache write-back and
+    // invalidate would slow the work after each event)
+    if (hipEventCreateWithFlags(&start_, hipEventDisableSystemFence) != hipSuccess) { start_ = nullptr; return; }
     if (hipEventRecord(start_, stream_) != hipSuccess) { (void)hipEventDestroy(start_); start_ = nullptr; }
 }
 
 TimedLaunch::~TimedLaunch() {
     if (!start_) return;
     hipEvent_t stop = nullptr;
-    if (hipEventCreate(&stop) != hipSuccess) { (void)hipEventDestroy(start_); return; }
+    if (hipEventCreateWithFlags(&stop, hipEventDisableSystemFence) != hipSuccess) {
+        (void)hipEventDestroy(start_);
+        return;
+    }
     if (hipEventRecord(stop, stream_) != hipSuccess) {
         (void)hipEventDestroy(start_);
         (void)hipEventDestroy(stop);
