@@ -106,7 +106,14 @@ class PowersgdPart:
         self.mem = [mv.view(n, m) for mv, (n, m) in zip(mem_views, shapes)]
         self.grads = [[g.view(n, m) for g, (n, m) in zip(gs, shapes)] for gs in grad_views_per_set]
         self.tables = [self._mats(s) for s in range(len(self.grads))]
-        self.ws = torch.empty(gc.gc_powersgd_workspace_bytes(self._mats(0).mats), dtype=torch.uint8, device=dev)
+        # one workspace per gradient set: a recorded step (gc_powersgd_plan)
+        # keeps its matrix table in its workspace, and each step then only
+        # launches kernels (gc_powersgd_run); a plan is recorded again when
+        # the ranks or the previous ranks change
+        nbytes = gc.gc_powersgd_workspace_bytes(self._mats(0).mats)
+        self.wss = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in self.grads]
+        self.plans = [None] * len(self.grads)
+        self.plan_keys = [None] * len(self.grads)
 
     def _mats(self, s):
         gc = self.gc
@@ -118,11 +125,14 @@ class PowersgdPart:
         self.tables = [self._mats(s) for s in range(len(self.grads))]
 
     def step(self, s, eta=1.0):
+        prev = self.prev if self.deferred else None
+        key = (tuple(self.ranks), None if prev is None else tuple(prev))
+        if self.plan_keys[s] != key:
+            self.plans[s] = self.gc.gc_powersgd_plan(self.tables[s], prev, self.wss[s])
+            self.plan_keys[s] = key
+        self.gc.gc_powersgd_run(self.plans[s], eta, self.wss[s])
         if self.deferred:
-            self.gc.gc_powersgd_ef_step_deferred(self.tables[s], self.prev, eta, self.ws)
             self.prev = self.ranks
-        else:
-            self.gc.gc_powersgd_ef_step(self.tables[s], eta, self.ws)
 
 
 def psgd_bytes(shapes, ranks, sg):

@@ -59,6 +59,9 @@ _sig("gc_powersgd_workspace_bytes", _sz, C.POINTER(gc_mat), _i32)
 _sig("gc_powersgd_ef_step", _i32, C.POINTER(gc_mat), _i32, _i32, _f32, _vp, _sz, _vp)
 _sig("gc_powersgd_ef_step_deferred", _i32, C.POINTER(gc_mat), C.POINTER(C.c_int32), _i32, _i32, _f32, _vp, _sz, _vp)
 _sig("gc_powersgd_materialize", _i32, C.POINTER(gc_mat), C.POINTER(C.c_int32), _i32, _vp, _sz, _vp)
+_sig("gc_powersgd_plan_bytes", _sz, C.POINTER(gc_mat), _i32)
+_sig("gc_powersgd_plan", _i32, C.POINTER(gc_mat), C.POINTER(C.c_int32), _i32, _i32, _vp, _sz, _vp, _sz, _vp)
+_sig("gc_powersgd_run", _i32, _vp, _sz, _f32, _vp, _vp)
 _sig("gc_grad_norm_workspace_bytes", _sz, C.POINTER(gc_span), _i32)
 _sig("gc_grad_norm", _i32, C.POINTER(gc_span), _i32, _i32, _vp, _vp, _sz, _vp)
 _sig("gc_accordion_select", _i32, C.POINTER(C.c_float), C.POINTER(C.c_float), _i32, _f32, _i32,
@@ -70,6 +73,7 @@ _sig("gc_kernel_names", C.c_char_p)
 EXPORTED = ["gc_status_str", "gc_last_error", "gc_topk_workspace_bytes", "gc_topk_ef_encode",
             "gc_topk_decode", "gc_randk_ef_encode", "gc_powersgd_workspace_bytes", "gc_powersgd_ef_step",
             "gc_powersgd_ef_step_deferred", "gc_powersgd_materialize",
+            "gc_powersgd_plan_bytes", "gc_powersgd_plan", "gc_powersgd_run",
             "gc_grad_norm_workspace_bytes", "gc_grad_norm", "gc_accordion_select",
             "gc_timing_enable", "gc_timing_read", "gc_kernel_names"]
 
@@ -283,6 +287,41 @@ def gc_powersgd_ef_step_deferred(mats, prev_rank, eta: float, ws, stream=None) -
         arr, count, dt = _mats(mats, prev), len(mats), _dtype_code(mats[0].grad)
     _check(lib.gc_powersgd_ef_step_deferred(arr, prev.ctypes.data_as(C.POINTER(C.c_int32)), count, dt, float(eta),
                                             _ptr(ws), _nbytes(ws), _stream(stream)), "gc_powersgd_ef_step_deferred")
+
+
+def gc_powersgd_plan_bytes(mats) -> int:
+    arr = mats.arr if isinstance(mats, MatArray) else _mats(mats, need_grad=False)
+    return int(lib.gc_powersgd_plan_bytes(arr, len(arr)))
+
+
+def gc_powersgd_plan(mats, prev_rank, ws, stream=None) -> np.ndarray:
+    """Records a PowerSGD step (prev_rank None: explicit memory; else the
+    deferred form with these previous ranks).  Returns the host plan.
+    mats: a list of Mat, or a MatArray built from one."""
+    prev = None
+    if isinstance(mats, MatArray):
+        arr, count, dt = mats.arr, mats.count, mats.dtype
+        if prev_rank is not None:
+            prev = np.ascontiguousarray(prev_rank, np.int32)
+            _need(prev.ndim == 1 and prev.size == count, "prev_rank needs one entry per matrix")
+            _need(bool(np.all(mats.pcols > 0)), "every matrix needs p: it keeps P^ for the deferred memory")
+            _need(bool(np.all((prev <= mats.qcols) & (prev <= mats.pcols))), "q and p need prev_rank columns")
+    else:
+        if prev_rank is not None:
+            prev = _prev_ranks(mats, prev_rank)
+        arr, count, dt = _mats(mats, prev), len(mats), _dtype_code(mats[0].grad)
+    plan = np.zeros(int(lib.gc_powersgd_plan_bytes(arr, count)), np.uint8)
+    pp = None if prev is None else prev.ctypes.data_as(C.POINTER(C.c_int32))
+    _check(lib.gc_powersgd_plan(arr, pp, count, dt, plan.ctypes.data, plan.nbytes, _ptr(ws), _nbytes(ws),
+                                _stream(stream)), "gc_powersgd_plan")
+    return plan
+
+
+def gc_powersgd_run(plan: np.ndarray, eta: float, ws, stream=None) -> None:
+    """Launches a recorded PowerSGD step (kernels only)."""
+    _need(isinstance(plan, np.ndarray) and plan.dtype == np.uint8, "plan must come from gc_powersgd_plan")
+    _check(lib.gc_powersgd_run(plan.ctypes.data, plan.nbytes, float(eta), _ptr(ws), _stream(stream)),
+           "gc_powersgd_run")
 
 
 def gc_powersgd_materialize(mats: Sequence[Mat], prev_rank, ws, stream=None) -> None:

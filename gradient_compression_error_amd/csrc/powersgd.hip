@@ -30,6 +30,7 @@
 // on a second round.  Every reduction has a fixed order: the result bits do
 // not depend on scheduling.
 #include <algorithm>
+#include <cstring>
 #include <vector>
 
 #include "gc_common.h"
@@ -1423,9 +1424,8 @@ int copy_table(const PsBatch& B, const std::vector<PsMat>& tbl, hipStream_t s) {
 // step (the first passes rebuild the previous residual and store M in mem;
 // the output pass writes out and P^ only).
 template <bool BF16, bool DEF>
-int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& tbl, hipStream_t s) {
+int launch_batch(const PsBatch& B, const PlanBatch& pb, hipStream_t s) {
     int rc;
-    if ((rc = copy_table(B, tbl, s)) != GC_OK) return rc;
     int fused = 0, team_grid = 0;
     for (int c = 0; c < PQ_CLASSES; ++c) {
         fused += B.cbeg[c + 1] > B.cbeg[c] ? 1 : 0;
@@ -1485,6 +1485,17 @@ int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& t
     return GC_OK;
 }
 
+template <bool BF16, bool DEF>
+int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& tbl, hipStream_t s) {
+    const int rc = copy_table(B, tbl, s);
+    return rc != GC_OK ? rc : launch_batch<BF16, DEF>(B, pb, s);
+}
+
+int launch_any(bool bf16, bool def, const PsBatch& B, const PlanBatch& pb, hipStream_t s) {
+    if (def) return bf16 ? launch_batch<true, true>(B, pb, s) : launch_batch<false, true>(B, pb, s);
+    return bf16 ? launch_batch<true, false>(B, pb, s) : launch_batch<false, false>(B, pb, s);
+}
+
 // mem = M_prev - P^_prev Q_prev^T for the matrices with prank > 0.
 int run_materialize(const PsBatch& B, const std::vector<PsMat>& tbl, hipStream_t s) {
     int rc;
@@ -1498,8 +1509,16 @@ enum StepKind { STEP_EXPLICIT, STEP_DEFERRED, STEP_MATERIALIZE };
 
 // Validation, plan, table and launches shared by the three PowerSGD calls.
 // prank: [host] previous ranks (deferred and materialize calls), else NULL.
+// One batch of a recorded step: its launch parameters (the table is in ws).
+struct PlanEntry {
+    PsBatch B;
+    PlanBatch pb;
+};
+
+// rec != NULL: record the step instead of running it (tables copied, no launch).
 int powersgd_call(const char* fn, StepKind kind, const gc_mat* mats, const int32_t* prank, int nmats,
-                  int grad_dtype, float eta, void* ws, size_t ws_bytes, hipStream_t s) {
+                  int grad_dtype, float eta, void* ws, size_t ws_bytes, hipStream_t s,
+                  std::vector<PlanEntry>* rec = nullptr) {
     const std::string f(fn);
     if (!mats || nmats < 1) return fail(GC_ERR_ARG, f + ": need mats and nmats >= 1");
     if (kind != STEP_EXPLICIT && !prank) return fail(GC_ERR_ARG, f + ": null prev_rank");
@@ -1570,6 +1589,11 @@ int powersgd_call(const char* fn, StepKind kind, const gc_mat* mats, const int32
             M.prank = kind == STEP_EXPLICIT ? 0 : prank[pm.idx];
         }
         int rc;
+        if (rec) {
+            if ((rc = copy_table(B, tbl, s)) != GC_OK) return rc;
+            rec->push_back(PlanEntry{B, pb});
+            continue;
+        }
         if (kind == STEP_MATERIALIZE) rc = run_materialize(B, tbl, s);
         else if (kind == STEP_DEFERRED)
             rc = grad_dtype == GC_BF16 ? run_batch<true, true>(B, pb, tbl, s) : run_batch<false, true>(B, pb, tbl, s);
@@ -1578,6 +1602,24 @@ int powersgd_call(const char* fn, StepKind kind, const gc_mat* mats, const int32
         if (rc != GC_OK) return rc;
     }
     return GC_OK;
+}
+
+// Host plan buffer: a header, then one PlanEntry per batch (copied with
+// memcpy: the caller's buffer needs no alignment).
+constexpr unsigned long long PLAN_MAGIC = 0x31504e414c504347ULL;   // "GCPLANP1"
+struct PlanHeader {
+    unsigned long long magic;
+    int nbatches;
+    int grad_dtype;
+    int deferred;
+    int pad;
+    const void* ws;
+    size_t ws_bytes;
+};
+
+size_t plan_bytes_for(int nmats) {
+    const int nb = (nmats + PS_MAXB - 1) / PS_MAXB;
+    return sizeof(PlanHeader) + static_cast<size_t>(nb) * sizeof(PlanEntry);
 }
 
 }  // namespace
@@ -1606,6 +1648,56 @@ int gc_powersgd_ef_step_deferred(const gc_mat* mats, const int32_t* prev_rank, i
                                  float eta, void* ws, size_t ws_bytes, void* stream) {
     return powersgd_call("gc_powersgd_ef_step_deferred", STEP_DEFERRED, mats, prev_rank, nmats, grad_dtype, eta, ws,
                          ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t gc_powersgd_plan_bytes(const gc_mat* mats, int nmats) {
+    if (!mats || nmats < 1) return 0;
+    return plan_bytes_for(nmats);
+}
+
+int gc_powersgd_plan(const gc_mat* mats, const int32_t* prev_rank, int nmats, int grad_dtype, void* plan,
+                     size_t plan_bytes, void* ws, size_t ws_bytes, void* stream) {
+    if (!plan) return fail(GC_ERR_ARG, "gc_powersgd_plan: null plan buffer");
+    if (!mats || nmats < 1) return fail(GC_ERR_ARG, "gc_powersgd_plan: need mats and nmats >= 1");
+    if (plan_bytes < plan_bytes_for(nmats))
+        return fail(GC_ERR_ARG, "gc_powersgd_plan: plan buffer smaller than gc_powersgd_plan_bytes");
+    const bool def = prev_rank != nullptr;
+    std::vector<PlanEntry> rec;
+    const int rc = powersgd_call("gc_powersgd_plan", def ? STEP_DEFERRED : STEP_EXPLICIT, mats, prev_rank, nmats,
+                                 grad_dtype, 1.0f, ws, ws_bytes, static_cast<hipStream_t>(stream), &rec);
+    if (rc != GC_OK) return rc;
+    PlanHeader h{};
+    h.magic = PLAN_MAGIC;
+    h.nbatches = static_cast<int>(rec.size());
+    h.grad_dtype = grad_dtype;
+    h.deferred = def ? 1 : 0;
+    h.ws = ws;
+    h.ws_bytes = ws_bytes;
+    char* out = static_cast<char*>(plan);
+    std::memcpy(out, &h, sizeof(h));
+    std::memcpy(out + sizeof(h), rec.data(), rec.size() * sizeof(PlanEntry));
+    return GC_OK;
+}
+
+int gc_powersgd_run(const void* plan, size_t plan_bytes, float eta, void* ws, void* stream) {
+    if (!plan || plan_bytes < sizeof(PlanHeader)) return fail(GC_ERR_ARG, "gc_powersgd_run: null or short plan");
+    PlanHeader h;
+    std::memcpy(&h, plan, sizeof(h));
+    if (h.magic != PLAN_MAGIC || h.nbatches < 1 || h.nbatches > (INT32_MAX / PS_MAXB) + 1)
+        return fail(GC_ERR_ARG, "gc_powersgd_run: not a plan written by gc_powersgd_plan");
+    if (plan_bytes < sizeof(PlanHeader) + static_cast<size_t>(h.nbatches) * sizeof(PlanEntry))
+        return fail(GC_ERR_ARG, "gc_powersgd_run: plan buffer shorter than the plan");
+    if (ws != h.ws) return fail(GC_ERR_ARG, "gc_powersgd_run: ws is not the workspace the plan was made with");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const char* in = static_cast<const char*>(plan) + sizeof(PlanHeader);
+    for (int b = 0; b < h.nbatches; ++b) {
+        PlanEntry e;
+        std::memcpy(&e, in + static_cast<size_t>(b) * sizeof(PlanEntry), sizeof(e));
+        e.B.eta = eta;
+        const int rc = launch_any(h.grad_dtype == GC_BF16, h.deferred != 0, e.B, e.pb, s);
+        if (rc != GC_OK) return rc;
+    }
+    return GC_OK;
 }
 
 int gc_powersgd_materialize(const gc_mat* mats, const int32_t* prev_rank, int nmats, void* ws, size_t ws_bytes,

@@ -194,6 +194,39 @@ int gc_powersgd_ef_step(const gc_mat* mats, int nmats, int grad_dtype, float eta
 int gc_powersgd_ef_step_deferred(const gc_mat* mats, const int32_t* prev_rank, int nmats, int grad_dtype,
                                  float eta, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Recorded PowerSGD steps: upload once, then launch kernels only ---- */
+
+/* Host bytes of a plan for nmats matrices (0 for NULL mats or nmats < 1). */
+size_t gc_powersgd_plan_bytes(const gc_mat* mats, int nmats);
+
+/* Records one PowerSGD step of these matrices for gc_powersgd_run.  It checks
+ * every argument exactly as the step would.  It copies the matrix table into
+ * ws with one hipMemcpyAsync on `stream`, and it writes the launch parameters
+ * into `plan` (caller-owned host memory of gc_powersgd_plan_bytes bytes, any
+ * alignment).  Nothing is launched.
+ *   prev_rank == NULL: the step of gc_powersgd_ef_step (explicit memory);
+ *   prev_rank != NULL: the step of gc_powersgd_ef_step_deferred with these
+ *                      previous ranks ([host], nmats entries).
+ * The plan fixes pointers, shapes, ranks and previous ranks; eta is given
+ * per run.  A deferred plan made with prev_rank = rank describes every step
+ * after the first one at unchanged ranks.
+ * Errors: those of the recorded step, and GC_ERR_ARG for a NULL plan or
+ * plan_bytes below gc_powersgd_plan_bytes. */
+int gc_powersgd_plan(const gc_mat* mats, const int32_t* prev_rank, int nmats, int grad_dtype, void* plan,
+                     size_t plan_bytes, void* ws, size_t ws_bytes, void* stream);
+
+/* Runs a recorded step on `stream`: kernel launches only.  There is no copy,
+ * no allocation and no host synchronisation, so the call may be captured in a
+ * HIP graph.  It computes what the recorded call would compute on the
+ * buffers' contents at run time.
+ * The buffers named in the plan must still be valid.  ws must be the
+ * workspace given to gc_powersgd_plan, with no other PowerSGD call on it
+ * since.  The run must be ordered after the plan call's table copy: use the
+ * same stream, or synchronise.
+ * Errors: GC_ERR_ARG for a NULL, short or foreign plan, or another ws;
+ * GC_ERR_HIP. */
+int gc_powersgd_run(const void* plan, size_t plan_bytes, float eta, void* ws, void* stream);
+
 /* Writes the deferred memory out: for every matrix with prev_rank[i] > 0,
  * mem = mem - P^ Q^T over the first prev_rank[i] columns of p and q.
  * Afterwards mem holds m', bit for bit what gc_powersgd_ef_step would have

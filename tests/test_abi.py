@@ -190,6 +190,26 @@ def test_powersgd_validation(gcl):
     assert mat(mats(grad=None), prev(2), wsb=need - 1) == gcl.GC_ERR_WORKSPACE
     assert mat(mats(grad=None, p=0x200000 + 64), prev(2)) == gcl.GC_ERR_ARG   # p inside mem
 
+    # recorded steps: the plan call validates like the step; the run checks its plan
+    pb = L.gc_powersgd_plan_bytes(mats(), 1)
+    assert pb > 0 and L.gc_powersgd_plan_bytes(None, 1) == 0
+    buf = (C.c_uint8 * pb)()
+
+    def plan(arr, pr, pbytes=pb, wsb=big, dt=gcl.GC_F32):
+        return L.gc_powersgd_plan(arr, pr, 1, dt, C.cast(buf, C.c_void_p), pbytes, 0x900000, wsb, None)
+
+    assert plan(mats(q=None), None) == gcl.GC_ERR_ARG
+    assert plan(mats(), None, pbytes=pb - 1) == gcl.GC_ERR_ARG
+    assert L.gc_powersgd_plan(mats(), None, 1, 0, None, pb, 0x900000, big, None) == gcl.GC_ERR_ARG
+    assert plan(mats(), None, wsb=need - 1) == gcl.GC_ERR_WORKSPACE
+    assert plan(mats(), None, dt=5) == gcl.GC_ERR_DTYPE
+    assert plan(mats(p=None), prev(2)) == gcl.GC_ERR_ARG                 # deferred form needs p
+    assert plan(mats(), prev(6)) == gcl.GC_ERR_ARG
+    zero = (C.c_uint8 * pb)()
+    assert L.gc_powersgd_run(None, pb, 1.0, 0x900000, None) == gcl.GC_ERR_ARG
+    assert L.gc_powersgd_run(C.cast(zero, C.c_void_p), pb, 1.0, 0x900000, None) == gcl.GC_ERR_ARG   # no magic
+    assert L.gc_powersgd_run(C.cast(zero, C.c_void_p), 8, 1.0, 0x900000, None) == gcl.GC_ERR_ARG    # short
+
 
 @no_gpu
 def test_norm_validation(gcl):
