@@ -271,6 +271,33 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU" in msg["error"]
 
 
+def test_bench_kernel_bytes_accounting():
+    """The bench's per-kernel algorithmic bytes: in the deferred form the first
+    pass and the decode of fused-class matrices add up to the method's bytes
+    per step, (s_g + 12) n m + 4 r (n + 2 m); the explicit form charges the
+    output pass the whole step.  Worked on the BERT-large and VGG-19 sets and a
+    hand case (one 4 x 8 matrix, rank 2, bf16: 14*32 + 4*2*(4 + 16) = 608)."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.psgd_bytes([(4, 8)], [2], 2) == 14 * 32 + 4 * 2 * (4 + 16) == 608
+    for shapes, sg in [(gen.BERT_MATS, 2), ([(4, 8), (1024, 4096), (3, 2048)], 4)]:
+        ranks = [min(4, n, m) for n, m in shapes]
+        kb = bench.psgd_kernel_bytes(shapes, ranks, sg, deferred=True)
+        assert set(kb) == {"psgd_pq", "psgd_decode"}
+        assert kb["psgd_pq"] + kb["psgd_decode"] == bench.psgd_bytes(shapes, ranks, sg)
+        kx = bench.psgd_kernel_bytes(shapes, ranks, sg, deferred=False)
+        assert kx["psgd_out"] == bench.psgd_bytes(shapes, ranks, sg)
+        fused, split = bench.fused_split_elems(shapes)
+        assert kx["psgd_pq"] == (sg + 4) * fused and split == 0
+    # split-path shapes (m % 4 != 0, m > 4096): the second read of M in psgd_q is charged on top
+    shapes, ranks = [(64, 27), (512, 4608)], [2, 4]
+    kb = bench.psgd_kernel_bytes(shapes, ranks, 4, deferred=True)
+    nm = 64 * 27 + 512 * 4608
+    assert kb["psgd_q"] == 4 * nm
+    assert kb["psgd_p"] + kb["psgd_decode"] == bench.psgd_bytes(shapes, ranks, 4)
+
+
 def test_binding_checks_sizes_and_dtypes(gcl):
     """The C ABI sees one length per call; the binding refuses tensors whose sizes
     or dtypes disagree with it before any pointer is passed (checked with host
