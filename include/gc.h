@@ -234,8 +234,8 @@ int gc_powersgd_run(const void* plan, size_t plan_bytes, float eta, void* ws, vo
  * Reads mem, p and q; grad, rank and out are not used (grad may be NULL).
  * Matrices with prev_rank[i] == 0 are left alone.
  * Workspace: gc_powersgd_workspace_bytes on the same array.
- * Errors: GC_ERR_ARG (NULL mats, prev_rank, mem, q or p where
- * prev_rank[i] > 0; prev_rank out of range; misaligned or overlapping
+ * Errors: GC_ERR_ARG (NULL mats, prev_rank, mem, q or p -- p is checked
+ * for every matrix; prev_rank out of range; misaligned or overlapping
  * buffers), GC_ERR_WORKSPACE, GC_ERR_HIP. */
 int gc_powersgd_materialize(const gc_mat* mats, const int32_t* prev_rank, int nmats, void* ws, size_t ws_bytes,
                             void* stream);
