@@ -19,7 +19,8 @@
 //                    the slots: only the level-2 histogram of bin b1 is built
 //                    from them.  Otherwise re-reads acc and appends every
 //                    entry with key>>19 >= b1 instead.  topk_select2 -> bin b2
-//   topk_refine      level-3 histogram over the captured entries only.
+//   topk_refine      level-3 histogram over the captured entries only (8
+//                    copies, like levels 1 and 2).
 //   topk_count       threshold T and ties to take from the level-3 histogram
 //                    (every workgroup), then #(key > T) and #(key == T) over
 //                    the workgroup's contiguous range of tiles.
@@ -83,7 +84,7 @@ TopkLayout topk_layout(long long d) {
     L.zero_from = o;
     L.hist1 = o;     o += NCOPY * H1_BINS * 4;
     L.hist2 = o;     o += NCOPY * H2_BINS * 4;
-    L.hist3 = o;     o += round_up(H3_BINS * 4, 256);
+    L.hist3 = o;     o += round_up(NCOPY * H3_BINS * 4, 256);
     L.zero_end = o;
     L.tile_cnt = o;  o += round_up(nt * 4, 256);
     L.wg_gt = o;     o += TK_SMALL_GRID * 4;
@@ -484,9 +485,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_refine(
         }
     }
     __syncthreads();
+    // merged into one of NCOPY copies: every workgroup adds to the same 128
+    // bins, so one copy would serialise the atomics
+    unsigned* dst = hist3 + (blockIdx.x % NCOPY) * H3_BINS;
     for (int i = threadIdx.x; i < H3_BINS; i += TK_THREADS) {
         const unsigned c = h[i];
-        if (c) atomicAdd(hist3 + i, c);
+        if (c) atomicAdd(dst + i, c);
     }
 }
 
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_count(
     __shared__ unsigned s_tmp[4];
     __shared__ unsigned s_bin, s_above;
     const unsigned above2 = st->above2, prefix2 = st->prefix2;
-    select_bin<H3_BINS, 1>(hist3, H3_BINS, k - above2, s_h, s_tmp, &s_bin, &s_above);
+    select_bin<H3_BINS, NCOPY>(hist3, H3_BINS, k - above2, s_h, s_tmp, &s_bin, &s_above);
     const unsigned thr = (prefix2 << H2_SHIFT) | s_bin;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         const unsigned above3 = above2 + s_above;
