@@ -23,12 +23,26 @@
 //                Gram matrix, writes Q' = (M^T P) T into q (warm start)
 //   psgd_out     P^ = P T per row, out = P^ Q'^T, mem = M - out, P^ into p
 //
-// M is never stored: psgd_pq and psgd_out each recompute it from (mem, grad).
+// Two forms of the memory:
+//   explicit     (gc_powersgd_ef_step) M is never stored: psgd_pq and psgd_out
+//                each recompute it from (mem, grad), so M's inputs are read
+//                twice per step.
+//   deferred     (gc_powersgd_ef_step_deferred) mem keeps M, p keeps P^ and q
+//                keeps Q between steps.  The next step's first pass rebuilds
+//                m' = M - P^ Q^T per entry (residual1, the output pass's own
+//                float32 operations), forms M = m' + eta*grad, stores it over
+//                mem and runs the products on it; psgd_decode then writes out
+//                and P^ only.  Every entry is read once and written once.
+//                psgd_out's third mode (materialize) writes the memory out.
+// Recorded steps (gc_powersgd_plan / gc_powersgd_run) copy the matrix table
+// once and then only launch these kernels.
+//
 // psgd_pq and psgd_out use a balanced persistent partition: the grid is about
 // what the GPU holds at once, and workgroup b takes the rows whose first entry
 // falls in the b-th equal share of the batch's entries, so no workgroup waits
-// on a second round.  Every reduction has a fixed order: the result bits do
-// not depend on scheduling.
+// on a second round.  psgd_decode is not persistent: short workgroups in
+// address order suit a write-only pass.  Every reduction has a fixed order:
+// the result bits do not depend on scheduling.
 #include <algorithm>
 #include <cstring>
 #include <vector>
