@@ -39,7 +39,7 @@ import gen  # noqa: E402
 METRIC = "gradient GB/s through encode+decode+EF (µs/step) at 1 GPU; % of HBM peak"
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-# PowerSGD memory form: deferred (gc_powersgd_ef_step_deferred) unless --explicit
+# error-feedback memory form (PowerSGD and top-k): deferred unless --explicit
 PSGD_DEFERRED = True
 
 
@@ -51,8 +51,9 @@ def parse():
     ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c3acc", "c3randk", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--explicit", action="store_true",
-                    help="PowerSGD workloads: write the memory out every step (gc_powersgd_ef_step) instead of "
-                         "keeping it in deferred form (gc_powersgd_ef_step_deferred)")
+                    help="write the error-feedback memory out every step (gc_powersgd_ef_step, gc_topk_ef_encode) "
+                         "instead of keeping it in deferred form (gc_powersgd_ef_step_deferred, "
+                         "gc_topk_ef_encode_deferred)")
     ap.add_argument("--flush", action="store_true",
                     help="between timed steps write 1 GiB, then read 1 GiB (cold last-level cache, no dirty lines)")
     ap.add_argument("--copy-calib", action="store_true", help="only run a 1 GiB device copy (counter calibration)")
@@ -135,6 +136,25 @@ class PowersgdPart:
             self.prev = self.ranks
 
 
+class TopkEncoder:
+    """Top-k encode with the memory in deferred form (gc_topk_ef_encode_deferred:
+    mem keeps acc, a selection record marks the selected entries, which the
+    next step takes as +0.0) unless --explicit (gc_topk_ef_encode)."""
+
+    def __init__(self, torch, gc, dev):
+        self.gc = gc
+        self.deferred = PSGD_DEFERRED
+        self.sel = torch.zeros(4, dtype=torch.int32, device=dev)
+        self.has_prev = False
+
+    def encode(self, grad, mem, eta, k, idx, val, ws):
+        if self.deferred:
+            self.gc.gc_topk_ef_encode_deferred(grad, mem, eta, k, idx, val, self.sel, self.has_prev, ws)
+            self.has_prev = True
+        else:
+            self.gc.gc_topk_ef_encode(grad, mem, eta, k, idx, val, ws)
+
+
 def psgd_bytes(shapes, ranks, sg):
     return sum((sg + 12) * n * m + 4 * r * (n + 2 * m) for (n, m), r in zip(shapes, ranks))
 
@@ -206,6 +226,7 @@ class C5(Workload):
         self.idx = torch.empty(self.k, dtype=torch.int32, device=dev)
         self.val = torch.empty(self.k, dtype=torch.float32, device=dev)
         self.tws = torch.empty(gc.gc_topk_workspace_bytes(emb_d, self.k), dtype=torch.uint8, device=dev)
+        self.enc = TopkEncoder(torch, gc, dev)
         self.norms = torch.empty(len(sizes), device=dev)
         self.nws = torch.empty(gc.gc_grad_norm_workspace_bytes(self.sets[0][1]), dtype=torch.uint8, device=dev)
         self.prev = np.zeros(len(sizes), np.float32)
@@ -228,6 +249,8 @@ class C5(Workload):
         self.config = {"workload": "bert-large gradient set", "params": total, "matrices": len(shapes),
                        "powersgd_rank": 4, "embedding": list(gen.BERT_EMB), "topk_k": self.k,
                        "grad_dtype": "bf16", "memory_dtype": "f32", "eta": 1.0, "accordion_check_every": 10}
+        self.config["topk_memory"] = "deferred: acc kept, selection record marks the zeros" \
+            if self.enc.deferred else "explicit: selected entries zeroed every step"
         self.config["powersgd_memory"] = "deferred: (M, P^, Q) kept, residual rebuilt in the next step's first pass" \
             if self.ps.deferred else "explicit: written out every step"
 
@@ -248,7 +271,7 @@ class C5(Workload):
             self.pending = self.torch.cuda.Event()
             self.pending.record()
         self.ps.step(s)
-        gc.gc_topk_ef_encode(views[-1], self.emb_mem, 1.0, self.k, self.idx, self.val, self.tws)
+        self.enc.encode(views[-1], self.emb_mem, 1.0, self.k, self.idx, self.val, self.tws)
         gc.gc_topk_decode(self.idx, self.val, self.emb_out)
 
 
@@ -293,15 +316,18 @@ class C3(Workload):
         self.idx = torch.empty(k, dtype=torch.int32, device=dev)
         self.val = torch.empty(k, dtype=torch.float32, device=dev)
         self.ws = torch.empty(gc.gc_topk_workspace_bytes(d, k), dtype=torch.uint8, device=dev)
+        self.enc = TopkEncoder(torch, gc, dev)
         self.grad_bytes = 4 * d
         self.alg_bytes = 16 * d + 16 * k
         self.kernel_bytes = {"topk_accum_hist": 12 * d, "topk_decode_set": 4 * d + 8 * k}
         self.description = gen.WORKLOADS["c3"].description + f" (k={k})"
         self.config = {"workload": "resnet50-sized flat gradient", "params": d, "topk_k": k,
                        "grad_dtype": "f32", "memory_dtype": "f32", "eta": 1.0}
+        self.config["topk_memory"] = "deferred: acc kept, selection record marks the zeros" \
+            if self.enc.deferred else "explicit: selected entries zeroed every step"
 
     def step(self, t):
-        self.gc.gc_topk_ef_encode(self.g[t % 2], self.mem, 1.0, self.k, self.idx, self.val, self.ws)
+        self.enc.encode(self.g[t % 2], self.mem, 1.0, self.k, self.idx, self.val, self.ws)
         self.gc.gc_topk_decode(self.idx, self.val, self.out)
 
 
@@ -349,6 +375,7 @@ class C3Acc(Workload):
         self.val = torch.empty(self.k_low, dtype=torch.float32, device=dev)
         self.ws = torch.empty(max(gc.gc_topk_workspace_bytes(d, self.k_low), gc.gc_topk_workspace_bytes(d, self.k_high)),
                               dtype=torch.uint8, device=dev)
+        self.enc = TopkEncoder(torch, gc, dev)
         self.norms = torch.empty(1, device=dev)
         self.nws = torch.empty(gc.gc_grad_norm_workspace_bytes([self.base[0]]), dtype=torch.uint8, device=dev)
         self.prev = np.zeros(1, np.float32)
@@ -361,6 +388,8 @@ class C3Acc(Workload):
         self.config = {"workload": "resnet50-sized flat gradient, accordion top-k", "params": d,
                        "levels": f"l_low=k {self.k_low} (1%), l_high=k {self.k_high} (0.1%)",
                        "grad_dtype": "f32", "memory_dtype": "f32", "eta": 1.0, "accordion_check_every": 10}
+        self.config["topk_memory"] = "deferred: acc kept, selection record marks the zeros" \
+            if self.enc.deferred else "explicit: selected entries zeroed every step"
 
     def prepare(self, tmax):
         # the scaled gradient of every step the run uses, made on the device before timing
@@ -383,7 +412,7 @@ class C3Acc(Workload):
             lv, self.prev = gc.gc_accordion_select(self.norms.cpu().numpy(), self.prev, gen.C4_THRESHOLD, t > 0)
             self.k = self.k_low if lv[0] == gc.GC_LEVEL_LOW else self.k_high
         self.ks.append(self.k)
-        gc.gc_topk_ef_encode(g, self.mem, 1.0, self.k, self.idx[:self.k], self.val[:self.k], self.ws)
+        self.enc.encode(g, self.mem, 1.0, self.k, self.idx[:self.k], self.val[:self.k], self.ws)
         gc.gc_topk_decode(self.idx[:self.k], self.val[:self.k], self.out)
 
 

@@ -54,6 +54,8 @@ _sig("gc_last_error", C.c_char_p)
 _sig("gc_topk_workspace_bytes", _sz, _i64, _i64)
 _sig("gc_topk_ef_encode", _i32, _vp, _i32, _vp, _i64, _f32, _i64, _vp, _vp, _vp, _sz, _vp)
 _sig("gc_topk_decode", _i32, _vp, _vp, _i64, _vp, _i64, _i32, _vp)
+_sig("gc_topk_ef_encode_deferred", _i32, _vp, _i32, _vp, _i64, _f32, _i64, _vp, _vp, _vp, _i32, _vp, _sz, _vp)
+_sig("gc_topk_materialize", _i32, _vp, _i64, _vp, _vp)
 _sig("gc_randk_ef_encode", _i32, _vp, _i32, _vp, _i64, _f32, _vp, _i64, _vp, _vp)
 _sig("gc_powersgd_workspace_bytes", _sz, C.POINTER(gc_mat), _i32)
 _sig("gc_powersgd_ef_step", _i32, C.POINTER(gc_mat), _i32, _i32, _f32, _vp, _sz, _vp)
@@ -71,6 +73,7 @@ _sig("gc_timing_read", _i32, C.POINTER(C.c_double), C.POINTER(C.c_int64))
 _sig("gc_kernel_names", C.c_char_p)
 
 EXPORTED = ["gc_status_str", "gc_last_error", "gc_topk_workspace_bytes", "gc_topk_ef_encode",
+            "gc_topk_ef_encode_deferred", "gc_topk_materialize",
             "gc_topk_decode", "gc_randk_ef_encode", "gc_powersgd_workspace_bytes", "gc_powersgd_ef_step",
             "gc_powersgd_ef_step_deferred", "gc_powersgd_materialize",
             "gc_powersgd_plan_bytes", "gc_powersgd_plan", "gc_powersgd_run",
@@ -163,6 +166,33 @@ def gc_topk_ef_encode(grad, mem, eta: float, k: int, out_idx, out_val, ws, strea
     _check(lib.gc_topk_ef_encode(_ptr(grad), _dtype_code(grad), _ptr(mem), mem.numel(), float(eta), int(k),
                                  _ptr(out_idx), _ptr(out_val), _ptr(ws), _nbytes(ws), _stream(stream)),
            "gc_topk_ef_encode")
+
+
+def gc_topk_ef_encode_deferred(grad, mem, eta: float, k: int, out_idx, out_val, sel, has_prev: bool, ws,
+                               stream=None) -> None:
+    """Top-k encode with the memory in deferred form: mem keeps acc and sel
+    (int32 device tensor of 4 entries) records the selection, whose entries
+    the next deferred call takes as +0.0."""
+    import torch
+    _dtype_is(mem, torch.float32, "mem")
+    _dtype_is(out_idx, torch.int32, "out_idx")
+    _dtype_is(out_val, torch.float32, "out_val")
+    _dtype_is(sel, torch.int32, "sel")
+    _need(sel.numel() >= 4, "sel needs 4 entries")
+    _need(grad.numel() == mem.numel(), "grad and mem must have the same number of entries")
+    _need(out_idx.numel() >= k and out_val.numel() >= k, "out_idx and out_val need room for k entries")
+    _check(lib.gc_topk_ef_encode_deferred(_ptr(grad), _dtype_code(grad), _ptr(mem), mem.numel(), float(eta), int(k),
+                                          _ptr(out_idx), _ptr(out_val), _ptr(sel), 1 if has_prev else 0, _ptr(ws),
+                                          _nbytes(ws), _stream(stream)), "gc_topk_ef_encode_deferred")
+
+
+def gc_topk_materialize(mem, sel, stream=None) -> None:
+    """Writes a deferred top-k memory out (the selected entries become +0.0)."""
+    import torch
+    _dtype_is(mem, torch.float32, "mem")
+    _dtype_is(sel, torch.int32, "sel")
+    _need(sel.numel() >= 4, "sel needs 4 entries")
+    _check(lib.gc_topk_materialize(_ptr(mem), mem.numel(), _ptr(sel), _stream(stream)), "gc_topk_materialize")
 
 
 def gc_randk_ef_encode(grad, mem, eta: float, idx, out_val, stream=None) -> None:

@@ -97,6 +97,31 @@ TopkLayout topk_layout(long long d) {
 
 // ---------------------------------------------------------------- device helpers
 
+// Deferred memory: mem holds acc of the previous step, and the selection
+// record {thr, cut} says which entries that step selected -- key > thr, or
+// key == thr and index <= cut (the ties it took, lowest indices first).  Those
+// entries are +0.0 in the memory the method carries.
+struct PrevSel {
+    unsigned thr;
+    long long cut;
+};
+
+__device__ __forceinline__ PrevSel read_sel(const unsigned* sel) {
+    PrevSel ps;
+    ps.thr = sel[0];
+    ps.cut = static_cast<int>(sel[1]);
+    return ps;
+}
+
+__device__ __forceinline__ bool was_selected(float a, long long i, const PrevSel& ps) {
+    const unsigned key = key_of(a);
+    return key > ps.thr || (key == ps.thr && i <= ps.cut);
+}
+
+__device__ __forceinline__ float mem_of(float a, long long i, const PrevSel& ps) {
+    return was_selected(a, i, ps) ? 0.0f : a;
+}
+
 // Bin b of the histogram (sum of NC copies spaced `stride` words apart,
 // scanned from the top) with
 //   sum(hist[b+1 ..]) < need <= sum(hist[b ..]);
@@ -176,10 +201,11 @@ constexpr int SAMPLES_PER_THREAD = SAMPLES / PREP_THREADS;
 // sets guess = lower edge of the bin holding the sample of rank `rank_g` from
 // the top (rank_g >= S: guess = 0, capture all).  Blocks 1..: zero the
 // histograms.
-template <bool BF16>
+template <bool BF16, bool DEFR>
 __global__ __launch_bounds__(PREP_THREADS) void topk_prep(
         const void* __restrict__ grad, const float* __restrict__ mem, long long d, float eta,
-        unsigned rank_g, TopkState* __restrict__ st, uint4* __restrict__ zero, int n16) {
+        unsigned rank_g, TopkState* __restrict__ st, uint4* __restrict__ zero, int n16,
+        const unsigned* __restrict__ sel) {
     if (blockIdx.x > 0) {
         const int stride = (gridDim.x - 1) * PREP_THREADS;
         for (int i = (blockIdx.x - 1) * PREP_THREADS + threadIdx.x; i < n16; i += stride)
@@ -203,6 +229,7 @@ __global__ __launch_bounds__(PREP_THREADS) void topk_prep(
         }
         mv[u] = mem[pos];
         gv[u] = load_grad1<BF16>(grad, pos);
+        if constexpr (DEFR) mv[u] = mem_of(mv[u], pos, read_sel(sel));
     }
 #pragma unroll
     for (int u = 0; u < SAMPLES_PER_THREAD; ++u) {
@@ -288,17 +315,19 @@ __device__ __forceinline__ unsigned append_chunks(const bool (&flag)[U][J], cons
 // acc = fl32(m + fl32(eta*g)) over TK_TILE entries per workgroup (sub-tile s+1
 // is loaded before sub-tile s is stored), with a level-1 histogram in LDS;
 // entries with key >= guess go to the tile's slots in index order.
-template <bool BF16>
+template <bool BF16, bool DEFR>
 __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
         const void* __restrict__ grad, float* __restrict__ mem, long long d, float eta,
         const TopkState* __restrict__ st, unsigned* __restrict__ hist1, int* __restrict__ slot_idx,
-        float* __restrict__ slot_val, unsigned* __restrict__ tile_cnt) {
+        float* __restrict__ slot_val, unsigned* __restrict__ tile_cnt, const unsigned* __restrict__ sel) {
     __shared__ unsigned h[H1_BINS];
     __shared__ unsigned s_cnt[2][TK_SUBS][4];
     for (int i = threadIdx.x; i < H1_BINS; i += TK_THREADS) h[i] = 0u;
     __syncthreads();
 
     const unsigned guess = st->guess;
+    PrevSel ps{};
+    if constexpr (DEFR) ps = read_sel(sel);
     const long long base = static_cast<long long>(blockIdx.x) * TK_TILE;
     int* const sidx = slot_idx + base;
     float* const sval = slot_val + base;
@@ -317,11 +346,17 @@ __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
         long long e0[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+            const long long i4 = b4 + u * TK_THREADS + threadIdx.x;
+            if constexpr (DEFR) {
+                mv[u].x = mem_of(mv[u].x, i4 * 4, ps);
+                mv[u].y = mem_of(mv[u].y, i4 * 4 + 1, ps);
+                mv[u].z = mem_of(mv[u].z, i4 * 4 + 2, ps);
+                mv[u].w = mem_of(mv[u].w, i4 * 4 + 3, ps);
+            }
             a[u][0] = ef_acc(mv[u].x, eta, gv[u].x);
             a[u][1] = ef_acc(mv[u].y, eta, gv[u].y);
             a[u][2] = ef_acc(mv[u].z, eta, gv[u].z);
             a[u][3] = ef_acc(mv[u].w, eta, gv[u].w);
-            const long long i4 = b4 + u * TK_THREADS + threadIdx.x;
             e0[u] = i4 * 4;
             reinterpret_cast<float4*>(mem)[i4] = make_float4(a[u][0], a[u][1], a[u][2], a[u][3]);
 #pragma unroll
@@ -348,7 +383,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
         float a[1][1] = {{0.0f}};
         const long long e0[1] = {i};
         if (i < t1) {
-            a[0][0] = ef_acc(mem[i], eta, load_grad1<BF16>(grad, i));
+            float mi = mem[i];
+            if constexpr (DEFR) mi = mem_of(mi, i, ps);
+            a[0][0] = ef_acc(mi, eta, load_grad1<BF16>(grad, i));
             mem[i] = a[0][0];
             const unsigned key = key_of(a[0][0]);
             atomicAdd(&h[key >> H1_SHIFT], 1u);
@@ -506,7 +543,7 @@ __device__ __forceinline__ int tile_lo(int b, int g, int ntiles) {
 __global__ __launch_bounds__(TK_THREADS) void topk_count(
         TopkState* __restrict__ st, const unsigned* __restrict__ hist3, unsigned k,
         const float* __restrict__ slot_val, const unsigned* __restrict__ tile_cnt, int ntiles,
-        unsigned* __restrict__ wg_gt, unsigned* __restrict__ wg_eq) {
+        unsigned* __restrict__ wg_gt, unsigned* __restrict__ wg_eq, unsigned* __restrict__ sel_out) {
     __shared__ unsigned s_red[8];
     __shared__ unsigned s_h[H3_BINS];
     __shared__ unsigned s_tmp[4];
@@ -519,6 +556,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_count(
         st->thr = thr;
         st->above3 = above3;
         st->need = k - above3;
+        if (sel_out) {
+            // the selection record of a deferred call; topk_emit sets the cut
+            // when ties are taken
+            sel_out[0] = thr;
+            sel_out[1] = 0xFFFFFFFFu;   // -1: no tie taken
+        }
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t0 = tile_lo(blockIdx.x, gridDim.x, ntiles), t1 = tile_lo(blockIdx.x + 1, gridDim.x, ntiles);
@@ -553,7 +596,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_emit(
         const TopkState* __restrict__ st, const int* __restrict__ slot_idx,
         const float* __restrict__ slot_val, const unsigned* __restrict__ tile_cnt,
         const unsigned* __restrict__ wg_gt, const unsigned* __restrict__ wg_eq, int ntiles,
-        unsigned k, int* __restrict__ out_idx, float* __restrict__ out_val, float* __restrict__ mem) {
+        unsigned k, int* __restrict__ out_idx, float* __restrict__ out_val, float* __restrict__ mem,
+        unsigned* __restrict__ sel_out) {
     __shared__ unsigned s_eq[4], s_sel[4];
     const unsigned thr = st->thr;
     const unsigned need = st->need;
@@ -616,12 +660,25 @@ __global__ __launch_bounds__(TK_THREADS) void topk_emit(
             if (sel && pos < k) {
                 out_idx[pos] = ix;
                 out_val[pos] = v;
-                mem[ix] = 0.0f;
+                // deferred memory: the selection record stands in for the zeros
+                if (!sel_out) mem[ix] = 0.0f;
+                else if (is_eq && rank + 1 == need) sel_out[1] = static_cast<unsigned>(ix);
             }
             eqr += teq;
             off += tsel;
             __syncthreads();
         }
+    }
+}
+
+// Writes the deferred memory out: the entries the selection record marks
+// become +0.0 (all d entries read, the selected ones written).
+__global__ __launch_bounds__(256) void topk_materialize(float* __restrict__ mem, long long d,
+                                                        const unsigned* __restrict__ sel) {
+    const PrevSel ps = read_sel(sel);
+    const long long stride = static_cast<long long>(gridDim.x) * 256;
+    for (long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x; i < d; i += stride) {
+        if (was_selected(mem[i], i, ps)) mem[i] = 0.0f;
     }
 }
 
@@ -757,39 +814,37 @@ unsigned guess_rank(long long d, long long k) {
     return r >= S ? static_cast<unsigned>(S) : static_cast<unsigned>(r);
 }
 
-}  // namespace
-}  // namespace gc
-
-using namespace gc;
-
-extern "C" {
-
-size_t gc_topk_workspace_bytes(int64_t d, int64_t k) {
-    if (d < 1 || d > INT32_MAX || k < 1 || k > d) return 0;
-    return topk_layout(d).total;
-}
-
-int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, float eta,
-                      int64_t k, int32_t* out_idx, float* out_val,
-                      void* ws, size_t ws_bytes, void* stream) {
+int topk_encode(const char* fname, const void* grad, int grad_dtype, float* mem, int64_t d, float eta, int64_t k,
+                int32_t* out_idx, float* out_val, unsigned* sel, bool deferred, bool has_prev, void* ws,
+                size_t ws_bytes, void* stream) {
+    const std::string fn(fname);
     if (!grad || !mem || !out_idx || !out_val || !ws)
-        return fail(GC_ERR_ARG, "gc_topk_ef_encode: null pointer argument");
+        return fail(GC_ERR_ARG, fn + ": null pointer argument");
     if (grad_dtype != GC_F32 && grad_dtype != GC_BF16)
-        return fail(GC_ERR_DTYPE, "gc_topk_ef_encode: grad_dtype must be GC_F32 or GC_BF16");
+        return fail(GC_ERR_DTYPE, fn + ": grad_dtype must be GC_F32 or GC_BF16");
     if (d < 1 || d > INT32_MAX)
-        return fail(GC_ERR_ARG, "gc_topk_ef_encode: d must be in [1, INT32_MAX]");
-    if (k < 1 || k > d) return fail(GC_ERR_ARG, "gc_topk_ef_encode: k must be in [1, d]");
+        return fail(GC_ERR_ARG, fn + ": d must be in [1, INT32_MAX]");
+    if (k < 1 || k > d) return fail(GC_ERR_ARG, fn + ": k must be in [1, d]");
     if (!aligned16(grad) || !aligned16(mem) || !aligned16(out_idx) || !aligned16(out_val) || !aligned16(ws))
-        return fail(GC_ERR_ARG, "gc_topk_ef_encode: device pointers must be 16-byte aligned");
+        return fail(GC_ERR_ARG, fn + ": device pointers must be 16-byte aligned");
     const size_t gbytes = static_cast<size_t>(d) * (grad_dtype == GC_BF16 ? 2 : 4);
     const size_t mbytes = static_cast<size_t>(d) * 4, kbytes = static_cast<size_t>(k) * 4;
     if (overlaps(out_idx, kbytes, mem, mbytes) || overlaps(out_val, kbytes, mem, mbytes) ||
         overlaps(out_idx, kbytes, out_val, kbytes) || overlaps(grad, gbytes, mem, mbytes) ||
         overlaps(out_idx, kbytes, grad, gbytes) || overlaps(out_val, kbytes, grad, gbytes))
-        return fail(GC_ERR_ARG, "gc_topk_ef_encode: output buffers overlap an input or each other");
+        return fail(GC_ERR_ARG, fn + ": output buffers overlap an input or each other");
+    if (deferred) {
+        if (!sel) return fail(GC_ERR_ARG, fn + ": null selection record");
+        if (!aligned16(sel)) return fail(GC_ERR_ARG, fn + ": the selection record must be 16-byte aligned");
+        if (overlaps(sel, 16, mem, mbytes) || overlaps(sel, 16, grad, gbytes) || overlaps(sel, 16, out_idx, kbytes) ||
+            overlaps(sel, 16, out_val, kbytes))
+            return fail(GC_ERR_ARG, fn + ": the selection record overlaps another buffer");
+    }
+    unsigned* sel_out = deferred ? sel : nullptr;
+    const bool defr = deferred && has_prev;
     const TopkLayout L = topk_layout(d);
     if (ws_bytes < L.total)
-        return fail(GC_ERR_WORKSPACE, "gc_topk_ef_encode: workspace smaller than gc_topk_workspace_bytes");
+        return fail(GC_ERR_WORKSPACE, fn + ": workspace smaller than gc_topk_workspace_bytes");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(ws);
@@ -812,20 +867,31 @@ int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, f
         const unsigned rank_g = guess_rank(d, k);
         uint4* zero = reinterpret_cast<uint4*>(w + L.zero_from);
         const int n16 = static_cast<int>((L.zero_end - L.zero_from) / 16);
-        if (grad_dtype == GC_BF16)
-            topk_prep<true><<<1 + PREP_ZERO_BLOCKS, PREP_THREADS, 0, s>>>(grad, mem, d, eta, rank_g, st, zero, n16);
+        const dim3 g(1 + PREP_ZERO_BLOCKS);
+        if (grad_dtype == GC_BF16 && defr)
+            topk_prep<true, true><<<g, PREP_THREADS, 0, s>>>(grad, mem, d, eta, rank_g, st, zero, n16, sel);
+        else if (grad_dtype == GC_BF16)
+            topk_prep<true, false><<<g, PREP_THREADS, 0, s>>>(grad, mem, d, eta, rank_g, st, zero, n16, sel);
+        else if (defr)
+            topk_prep<false, true><<<g, PREP_THREADS, 0, s>>>(grad, mem, d, eta, rank_g, st, zero, n16, sel);
         else
-            topk_prep<false><<<1 + PREP_ZERO_BLOCKS, PREP_THREADS, 0, s>>>(grad, mem, d, eta, rank_g, st, zero, n16);
+            topk_prep<false, false><<<g, PREP_THREADS, 0, s>>>(grad, mem, d, eta, rank_g, st, zero, n16, sel);
         if ((rc = check_launch("topk_prep")) != GC_OK) return rc;
     }
     {
         TimedLaunch tl("topk_accum_hist", s);
-        if (grad_dtype == GC_BF16)
-            topk_accum_hist<true><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx, slot_val,
-                                                                tile_cnt);
+        if (grad_dtype == GC_BF16 && defr)
+            topk_accum_hist<true, true><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx,
+                                                                      slot_val, tile_cnt, sel);
+        else if (grad_dtype == GC_BF16)
+            topk_accum_hist<true, false><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx,
+                                                                       slot_val, tile_cnt, sel);
+        else if (defr)
+            topk_accum_hist<false, true><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx,
+                                                                       slot_val, tile_cnt, sel);
         else
-            topk_accum_hist<false><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx, slot_val,
-                                                                 tile_cnt);
+            topk_accum_hist<false, false><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx,
+                                                                        slot_val, tile_cnt, sel);
         if ((rc = check_launch("topk_accum_hist")) != GC_OK) return rc;
     }
     {
@@ -850,16 +916,57 @@ int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, f
     }
     {
         TimedLaunch tl("topk_count", s);
-        topk_count<<<small_grid, TK_THREADS, 0, s>>>(st, hist3, ku, slot_val, tile_cnt, ntiles, wg_gt, wg_eq);
+        topk_count<<<small_grid, TK_THREADS, 0, s>>>(st, hist3, ku, slot_val, tile_cnt, ntiles, wg_gt, wg_eq,
+                                                     sel_out);
         if ((rc = check_launch("topk_count")) != GC_OK) return rc;
     }
     {
         TimedLaunch tl("topk_emit", s);
         topk_emit<<<small_grid, TK_THREADS, 0, s>>>(st, slot_idx, slot_val, tile_cnt, wg_gt, wg_eq,
-                                                    ntiles, ku, out_idx, out_val, mem);
+                                                    ntiles, ku, out_idx, out_val, mem, sel_out);
         if ((rc = check_launch("topk_emit")) != GC_OK) return rc;
     }
     return GC_OK;
+}
+
+}  // namespace
+}  // namespace gc
+
+using namespace gc;
+
+extern "C" {
+
+size_t gc_topk_workspace_bytes(int64_t d, int64_t k) {
+    if (d < 1 || d > INT32_MAX || k < 1 || k > d) return 0;
+    return topk_layout(d).total;
+}
+
+int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, float eta,
+                      int64_t k, int32_t* out_idx, float* out_val,
+                      void* ws, size_t ws_bytes, void* stream) {
+    return topk_encode("gc_topk_ef_encode", grad, grad_dtype, mem, d, eta, k, out_idx, out_val, nullptr, false, false,
+                       ws, ws_bytes, stream);
+}
+
+int gc_topk_ef_encode_deferred(const void* grad, int grad_dtype, float* mem, int64_t d, float eta, int64_t k,
+                               int32_t* out_idx, float* out_val, uint32_t* sel, int has_prev, void* ws,
+                               size_t ws_bytes, void* stream) {
+    return topk_encode("gc_topk_ef_encode_deferred", grad, grad_dtype, mem, d, eta, k, out_idx, out_val, sel, true,
+                       has_prev != 0, ws, ws_bytes, stream);
+}
+
+int gc_topk_materialize(float* mem, int64_t d, const uint32_t* sel, void* stream) {
+    if (!mem || !sel) return fail(GC_ERR_ARG, "gc_topk_materialize: null pointer argument");
+    if (d < 1 || d > INT32_MAX) return fail(GC_ERR_ARG, "gc_topk_materialize: d must be in [1, INT32_MAX]");
+    if (!aligned16(mem) || !aligned16(sel))
+        return fail(GC_ERR_ARG, "gc_topk_materialize: device pointers must be 16-byte aligned");
+    if (overlaps(sel, 16, mem, static_cast<size_t>(d) * 4))
+        return fail(GC_ERR_ARG, "gc_topk_materialize: the selection record overlaps mem");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const long long blocks = std::min<long long>((d + 255) / 256, 4096);
+    TimedLaunch tl("topk_materialize", s);
+    topk_materialize<<<static_cast<unsigned>(blocks), 256, 0, s>>>(mem, d, sel);
+    return check_launch("topk_materialize");
 }
 
 int gc_topk_decode(const int32_t* idx, const float* val, int64_t k, float* out, int64_t d,

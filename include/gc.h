@@ -94,6 +94,34 @@ int gc_topk_ef_encode(const void* grad, int grad_dtype, float* mem, int64_t d, f
                       int64_t k, int32_t* out_idx, float* out_val,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* The same top-k step with the memory in deferred form.  The selected
+ * entries are not set to +0.0 in mem (a scattered write of k entries).
+ * Instead mem keeps acc, and a 16-byte selection record `sel` (device,
+ * caller-owned, 16-byte aligned) describes the selection:
+ *   sel[0] = T     the threshold key (|x| bits without the sign)
+ *   sel[1] = cut   the index of the last tie taken, as int32 (-1: none)
+ * An entry i is selected, and +0.0 in the memory the method carries
+ * (Sparsified SGD with Memory, method section), iff key(acc_i) > T, or
+ * key(acc_i) == T and i <= cut.  The next deferred call reads the record in
+ * its accumulate pass and takes those entries as +0.0.
+ *   has_prev == 0: mem holds the memory itself (the first call, or after
+ *                  gc_topk_materialize); sel is only written.
+ *   has_prev != 0: mem and sel are as the previous deferred call left them.
+ * out_idx and out_val get the bits of gc_topk_ef_encode.  mem becomes that
+ * call's memory after gc_topk_materialize.
+ * Errors: those of gc_topk_ef_encode, and GC_ERR_ARG for a NULL, misaligned
+ * or overlapping sel. */
+int gc_topk_ef_encode_deferred(const void* grad, int grad_dtype, float* mem, int64_t d, float eta, int64_t k,
+                               int32_t* out_idx, float* out_val, uint32_t* sel, int has_prev, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Writes a deferred top-k memory out: the entries sel marks become +0.0
+ * (every entry is read; the selected ones are written).  Afterwards mem holds
+ * the memory itself, and the next deferred call takes has_prev = 0.
+ * Errors: GC_ERR_ARG (NULL, misaligned or overlapping pointers, d out of
+ * [1, INT32_MAX]), GC_ERR_HIP. */
+int gc_topk_materialize(float* mem, int64_t d, const uint32_t* sel, void* stream);
+
 /* Dense decode of a top-k message (the scatter side of the same method):
  *   accumulate == 0:  out = 0 everywhere, then out[idx[j]] = val[j]
  *                     (idx must be strictly ascending, as gc_topk_ef_encode writes it)

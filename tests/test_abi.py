@@ -104,6 +104,27 @@ def test_topk_validation(gcl):
     assert call(val=I) == gcl.GC_ERR_ARG                      # idx/val alias
     assert call(wsb=ws - 1) == gcl.GC_ERR_WORKSPACE
     assert "workspace" in gcl.gc_last_error()
+    # deferred encode: the selection record is checked too
+    S = 0x600000
+
+    def dcall(sel=S, has_prev=1, **kw):
+        a = {**ok, **kw}
+        return L.gc_topk_ef_encode_deferred(a["grad"], a["dt"], a["mem"], a["d"], a["eta"], a["k"], a["idx"],
+                                            a["val"], sel, has_prev, a["ws"], a["wsb"], None)
+
+    assert dcall(sel=None) == gcl.GC_ERR_ARG
+    assert dcall(sel=S + 4) == gcl.GC_ERR_ARG                 # misaligned
+    assert dcall(sel=B + 16) == gcl.GC_ERR_ARG                # inside mem
+    assert dcall(sel=V) == gcl.GC_ERR_ARG                     # overlaps out_val
+    assert dcall(grad=None) == gcl.GC_ERR_ARG
+    assert dcall(k=0) == gcl.GC_ERR_ARG
+    assert dcall(dt=9) == gcl.GC_ERR_DTYPE
+    assert dcall(wsb=ws - 1) == gcl.GC_ERR_WORKSPACE
+    assert L.gc_topk_materialize(None, 1000, S, None) == gcl.GC_ERR_ARG
+    assert L.gc_topk_materialize(B, 1000, None, None) == gcl.GC_ERR_ARG
+    assert L.gc_topk_materialize(B, 0, S, None) == gcl.GC_ERR_ARG
+    assert L.gc_topk_materialize(B, 1000, B + 16, None) == gcl.GC_ERR_ARG   # record inside mem
+    assert L.gc_topk_materialize(B + 8, 1000, S, None) == gcl.GC_ERR_ARG     # misaligned
     # decode
     assert L.gc_topk_decode(I, V, 10, None, 1000, 0, None) == gcl.GC_ERR_ARG
     assert L.gc_topk_decode(I, V, 1001, B, 1000, 0, None) == gcl.GC_ERR_ARG
