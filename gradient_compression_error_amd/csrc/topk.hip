@@ -28,6 +28,12 @@
 //                    counts, then the k (index, value) pairs in ascending
 //                    index order; zeroes the selected memory entries.
 //
+// Deferred memory (gc_topk_ef_encode_deferred): topk_emit leaves the selected
+// entries as they are (no scattered writes) and topk_count / topk_emit write
+// a selection record {T, index of the last tie taken}; the next call's
+// topk_prep and topk_accum_hist read those entries as +0.0 (mem_of), and
+// topk_materialize writes the zeros when the explicit memory is wanted.
+//
 // Only topk_accum_hist touches all d entries when the guess holds (12 B/entry
 // for fp32 gradients); the rest work on the captured entries, which are a
 // superset of the candidates at or above the threshold in index order, so
