@@ -148,3 +148,46 @@ def test_guess_too_high_and_materialize_restart():
     m = df.memory()
     torch.cuda.synchronize()
     assert torch.equal(ex.idx, df.idx) and torch.equal(ex_mem.view(torch.int32), m.view(torch.int32))
+
+
+@pytest.mark.parametrize("k", [10])
+def test_memsgd_loop_on_the_gpu(k):
+    """Mem-SGD on the strongly convex quadratic of the oracle's convergence pin
+    (d = 100, curvatures in [1, 10], noise 0.1, eta_t = 8 / (mu (a + t))), run
+    in float32 with the top-k step on the GPU in deferred form and the
+    iterate x updated on the host: every step's (idx, val) equals the float32
+    oracle step's bit for bit, so the two trajectories are the same, the final
+    written-out memory too, and the run converges (f(x_T) <= 1e-2 f(x_0))."""
+    d, mu, L, sigma = 100, 1.0, 10.0, 0.1
+    r = gen.rng(0, gen.KIND_MISC, 92, k)
+    lam = np.exp(r.uniform(np.log(mu), np.log(L), d)).astype(np.float32)
+    xstar = r.standard_normal(d).astype(np.float32)
+    T = int(50 * (d / k) * np.sqrt(L / mu))
+    noise = r.standard_normal((T, d)).astype(np.float32)
+    a = max(d / k, 16 * L / mu)
+    print(f"case: Mem-SGD loop on the GPU, d={d} k={k} T={T}", flush=True)
+    f = lambda x: 0.5 * float(np.sum(lam.astype(np.float64) * (x.astype(np.float64) - xstar) ** 2))
+    x_gpu = np.zeros(d, np.float32)
+    x_orc = np.zeros(d, np.float32)
+    mem_h = np.zeros(d, np.float32)
+    df = Deferred(d, k, mem_h)
+    grad_t = torch.empty(d, dtype=torch.float32, device=DEV)
+    for t in range(T):
+        eta = np.float32(8.0 / (mu * (a + t)))
+        g_gpu = (lam * (x_gpu - xstar) + np.float32(sigma) * noise[t]).astype(np.float32)
+        g_orc = (lam * (x_orc - xstar) + np.float32(sigma) * noise[t]).astype(np.float32)
+        grad_t.copy_(torch.from_numpy(g_gpu))
+        df.step(grad_t, float(eta))
+        ref = oracle.topk_ef_step(mem_h, g_orc, float(eta), k)
+        idx = df.idx.cpu().numpy()
+        val = df.val.cpu().numpy()
+        assert np.array_equal(idx, ref["idx"]) and np.array_equal(val.view(np.uint32), ref["val"].view(np.uint32)), \
+            f"step {t}: the GPU step differs from the oracle"
+        x_gpu[idx] -= val
+        x_orc[ref["idx"]] -= ref["val"]
+        mem_h = ref["mem"]
+    m = df.memory()
+    torch.cuda.synchronize()
+    assert np.array_equal(x_gpu.view(np.uint32), x_orc.view(np.uint32))
+    assert np.array_equal(f32_bits(m), f32_bits(mem_h))
+    assert f(x_gpu) <= 1e-2 * f(np.zeros(d, np.float32)), f"no convergence: f(x_T) = {f(x_gpu):.3e}"
