@@ -41,6 +41,7 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 # error-feedback memory form (PowerSGD and top-k): deferred unless --explicit
 PSGD_DEFERRED = True
+OVERLAP = False    # c5 --overlap: the embedding's top-k on a second stream beside the PowerSGD decode
 
 
 def parse():
@@ -54,6 +55,10 @@ def parse():
                     help="write the error-feedback memory out every step (gc_powersgd_ef_step, gc_topk_ef_encode) "
                          "instead of keeping it in deferred form (gc_powersgd_ef_step_deferred, "
                          "gc_topk_ef_encode_deferred)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="c5: run the embedding's top-k on a second stream beside the PowerSGD decode pass "
+                         "(gc_powersgd_run_phases) instead of after the PowerSGD step on one stream; measured "
+                         "slower, since the decode's many short workgroups hold every slot until they drain")
     ap.add_argument("--flush", action="store_true",
                     help="between timed steps write 1 GiB, then read 1 GiB (cold last-level cache, no dirty lines)")
     ap.add_argument("--copy-calib", action="store_true", help="only run a 1 GiB device copy (counter calibration)")
@@ -125,13 +130,20 @@ class PowersgdPart:
         self.ranks = list(ranks)
         self.tables = [self._mats(s) for s in range(len(self.grads))]
 
-    def step(self, s, eta=1.0):
+    def step(self, s, eta=1.0, between=None):
+        """One recorded step; between(), if given, is called after the encode
+        launches and before the decode launches."""
         prev = self.prev if self.deferred else None
         key = (tuple(self.ranks), None if prev is None else tuple(prev))
         if self.plan_keys[s] != key:
             self.plans[s] = self.gc.gc_powersgd_plan(self.tables[s], prev, self.wss[s])
             self.plan_keys[s] = key
-        self.gc.gc_powersgd_run(self.plans[s], eta, self.wss[s])
+        if between is None:
+            self.gc.gc_powersgd_run(self.plans[s], eta, self.wss[s])
+        else:
+            self.gc.gc_powersgd_run_phases(self.plans[s], eta, self.wss[s], self.gc.PHASE_ENCODE)
+            between()
+            self.gc.gc_powersgd_run_phases(self.plans[s], eta, self.wss[s], self.gc.PHASE_DECODE)
         if self.deferred:
             self.prev = self.ranks
 
@@ -227,6 +239,8 @@ class C5(Workload):
         self.val = torch.empty(self.k, dtype=torch.float32, device=dev)
         self.tws = torch.empty(gc.gc_topk_workspace_bytes(emb_d, self.k), dtype=torch.uint8, device=dev)
         self.enc = TopkEncoder(torch, gc, dev)
+        self.side = torch.cuda.Stream(device=dev)     # default priority
+        self.ev_fork, self.ev_join = torch.cuda.Event(), torch.cuda.Event()
         self.norms = torch.empty(len(sizes), device=dev)
         self.nws = torch.empty(gc.gc_grad_norm_workspace_bytes(self.sets[0][1]), dtype=torch.uint8, device=dev)
         self.prev = np.zeros(len(sizes), np.float32)
@@ -253,6 +267,8 @@ class C5(Workload):
             if self.enc.deferred else "explicit: selected entries zeroed every step"
         self.config["powersgd_memory"] = "deferred: (M, P^, Q) kept, residual rebuilt in the next step's first pass" \
             if self.ps.deferred else "explicit: written out every step"
+        self.config["streams"] = "embedding top-k on a second stream beside the PowerSGD decode" if OVERLAP \
+            else "one stream"
 
     def step(self, t):
         gc, s = self.gc, t % 2
@@ -270,9 +286,29 @@ class C5(Workload):
             self.norms_host.copy_(self.norms, non_blocking=True)
             self.pending = self.torch.cuda.Event()
             self.pending.record()
-        self.ps.step(s)
+        if not OVERLAP:
+            self.ps.step(s)
+            self._topk(views)
+            return
+        # the embedding's top-k is independent of the PowerSGD matrices: here
+        # it runs on a second stream beside the write-only decode pass (not
+        # beside the first pass, whose one-round persistent grid it would push
+        # into a second round), and the step ends when both streams are done
+        main = self.torch.cuda.current_stream()
+
+        def fork():
+            self.ev_fork.record(main)
+            self.side.wait_event(self.ev_fork)
+            with self.torch.cuda.stream(self.side):
+                self._topk(views)
+            self.ev_join.record(self.side)
+
+        self.ps.step(s, between=fork)
+        main.wait_event(self.ev_join)
+
+    def _topk(self, views):
         self.enc.encode(views[-1], self.emb_mem, 1.0, self.k, self.idx, self.val, self.tws)
-        gc.gc_topk_decode(self.idx, self.val, self.emb_out)
+        self.gc.gc_topk_decode(self.idx, self.val, self.emb_out)
 
 
 class C2(Workload):
@@ -620,8 +656,9 @@ def main():
         return
 
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
-    global PSGD_DEFERRED
+    global PSGD_DEFERRED, OVERLAP
     PSGD_DEFERRED = not args.explicit
+    OVERLAP = args.overlap
     W = {"c5": C5, "c2": C2, "c3": C3, "c3acc": C3Acc, "c3randk": C3Randk, "c4": C4}[args.workload](torch, gc, dev)
     if hasattr(W, "prepare"):
         W.prepare(args.warmup + args.steps + 2)

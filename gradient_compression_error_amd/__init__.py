@@ -64,6 +64,7 @@ _sig("gc_powersgd_materialize", _i32, C.POINTER(gc_mat), C.POINTER(C.c_int32), _
 _sig("gc_powersgd_plan_bytes", _sz, C.POINTER(gc_mat), _i32)
 _sig("gc_powersgd_plan", _i32, C.POINTER(gc_mat), C.POINTER(C.c_int32), _i32, _i32, _vp, _sz, _vp, _sz, _vp)
 _sig("gc_powersgd_run", _i32, _vp, _sz, _f32, _vp, _vp)
+_sig("gc_powersgd_run_phases", _i32, _vp, _sz, _f32, _vp, _i32, _vp)
 _sig("gc_grad_norm_workspace_bytes", _sz, C.POINTER(gc_span), _i32)
 _sig("gc_grad_norm", _i32, C.POINTER(gc_span), _i32, _i32, _vp, _vp, _sz, _vp)
 _sig("gc_accordion_select", _i32, C.POINTER(C.c_float), C.POINTER(C.c_float), _i32, _f32, _i32,
@@ -76,7 +77,7 @@ EXPORTED = ["gc_status_str", "gc_last_error", "gc_topk_workspace_bytes", "gc_top
             "gc_topk_ef_encode_deferred", "gc_topk_materialize",
             "gc_topk_decode", "gc_randk_ef_encode", "gc_powersgd_workspace_bytes", "gc_powersgd_ef_step",
             "gc_powersgd_ef_step_deferred", "gc_powersgd_materialize",
-            "gc_powersgd_plan_bytes", "gc_powersgd_plan", "gc_powersgd_run",
+            "gc_powersgd_plan_bytes", "gc_powersgd_plan", "gc_powersgd_run", "gc_powersgd_run_phases",
             "gc_grad_norm_workspace_bytes", "gc_grad_norm", "gc_accordion_select",
             "gc_timing_enable", "gc_timing_read", "gc_kernel_names"]
 
@@ -352,6 +353,16 @@ def gc_powersgd_run(plan: np.ndarray, eta: float, ws, stream=None) -> None:
     _need(isinstance(plan, np.ndarray) and plan.dtype == np.uint8, "plan must come from gc_powersgd_plan")
     _check(lib.gc_powersgd_run(plan.ctypes.data, plan.nbytes, float(eta), _ptr(ws), _stream(stream)),
            "gc_powersgd_run")
+
+
+PHASE_ENCODE, PHASE_DECODE = 1, 2
+
+
+def gc_powersgd_run_phases(plan: np.ndarray, eta: float, ws, phases: int, stream=None) -> None:
+    """Launches the encode (1), the decode (2) or both (3) of a recorded step."""
+    _need(isinstance(plan, np.ndarray) and plan.dtype == np.uint8, "plan must come from gc_powersgd_plan")
+    _check(lib.gc_powersgd_run_phases(plan.ctypes.data, plan.nbytes, float(eta), _ptr(ws), int(phases),
+                                      _stream(stream)), "gc_powersgd_run_phases")
 
 
 def gc_powersgd_materialize(mats: Sequence[Mat], prev_rank, ws, stream=None) -> None:

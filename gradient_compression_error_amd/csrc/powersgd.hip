@@ -1433,12 +1433,9 @@ int copy_table(const PsBatch& B, const std::vector<PsMat>& tbl, hipStream_t s) {
     return GC_OK;
 }
 
-// Launches all kernels of one batch: the table copy, the fused classes,
-// the split path, the Q reduction and the output pass.  DEF: the deferred
-// step (the first passes rebuild the previous residual and store M in mem;
-// the output pass writes out and P^ only).
+// First passes and Q reduction of one batch.
 template <bool BF16, bool DEF>
-int launch_batch(const PsBatch& B, const PlanBatch& pb, hipStream_t s) {
+int launch_encode(const PsBatch& B, const PlanBatch& pb, hipStream_t s) {
     int rc;
     int fused = 0, team_grid = 0;
     for (int c = 0; c < PQ_CLASSES; ++c) {
@@ -1478,6 +1475,13 @@ int launch_batch(const PsBatch& B, const PlanBatch& pb, hipStream_t s) {
         psgd_qreduce<<<pb.nr, PS_THREADS, 0, s>>>(B);
         if ((rc = check_launch("psgd_qreduce")) != GC_OK) return rc;
     }
+    return GC_OK;
+}
+
+// Output pass of one batch.
+template <bool BF16, bool DEF>
+int launch_decode(const PsBatch& B, const PlanBatch& pb, hipStream_t s) {
+    int rc;
     {
         const char* name = DEF ? "psgd_decode" : "psgd_out";
         TimedLaunch tl(name, s);
@@ -1499,15 +1503,34 @@ int launch_batch(const PsBatch& B, const PlanBatch& pb, hipStream_t s) {
     return GC_OK;
 }
 
+// Launches the kernels of one batch: with PH_ENCODE the fused classes, the
+// split path and the Q reduction (P^ and Q' complete); with PH_DECODE the
+// output pass.  DEF: the deferred step (the first passes rebuild the
+// previous residual and store M in mem; the output pass writes out and P^
+// only).
+enum Phase { PH_ENCODE = 1, PH_DECODE = 2, PH_ALL = 3 };
+
+template <bool BF16, bool DEF>
+int launch_batch(const PsBatch& B, const PlanBatch& pb, hipStream_t s, int phases = PH_ALL) {
+    int rc;
+    if (phases & PH_ENCODE) {
+        if ((rc = launch_encode<BF16, DEF>(B, pb, s)) != GC_OK) return rc;
+    }
+    if (phases & PH_DECODE) {
+        if ((rc = launch_decode<BF16, DEF>(B, pb, s)) != GC_OK) return rc;
+    }
+    return GC_OK;
+}
+
 template <bool BF16, bool DEF>
 int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& tbl, hipStream_t s) {
     const int rc = copy_table(B, tbl, s);
     return rc != GC_OK ? rc : launch_batch<BF16, DEF>(B, pb, s);
 }
 
-int launch_any(bool bf16, bool def, const PsBatch& B, const PlanBatch& pb, hipStream_t s) {
-    if (def) return bf16 ? launch_batch<true, true>(B, pb, s) : launch_batch<false, true>(B, pb, s);
-    return bf16 ? launch_batch<true, false>(B, pb, s) : launch_batch<false, false>(B, pb, s);
+int launch_any(bool bf16, bool def, const PsBatch& B, const PlanBatch& pb, hipStream_t s, int phases) {
+    if (def) return bf16 ? launch_batch<true, true>(B, pb, s, phases) : launch_batch<false, true>(B, pb, s, phases);
+    return bf16 ? launch_batch<true, false>(B, pb, s, phases) : launch_batch<false, false>(B, pb, s, phases);
 }
 
 // mem = M_prev - P^_prev Q_prev^T for the matrices with prank > 0.
@@ -1693,8 +1716,9 @@ int gc_powersgd_plan(const gc_mat* mats, const int32_t* prev_rank, int nmats, in
     return GC_OK;
 }
 
-int gc_powersgd_run(const void* plan, size_t plan_bytes, float eta, void* ws, void* stream) {
+int gc_powersgd_run_phases(const void* plan, size_t plan_bytes, float eta, void* ws, int phases, void* stream) {
     if (!plan || plan_bytes < sizeof(PlanHeader)) return fail(GC_ERR_ARG, "gc_powersgd_run: null or short plan");
+    if (phases < 1 || phases > PH_ALL) return fail(GC_ERR_ARG, "gc_powersgd_run_phases: phases must be 1, 2 or 3");
     PlanHeader h;
     std::memcpy(&h, plan, sizeof(h));
     if (h.magic != PLAN_MAGIC || h.nbatches < 1 || h.nbatches > (INT32_MAX / PS_MAXB) + 1)
@@ -1704,14 +1728,20 @@ int gc_powersgd_run(const void* plan, size_t plan_bytes, float eta, void* ws, vo
     if (ws != h.ws) return fail(GC_ERR_ARG, "gc_powersgd_run: ws is not the workspace the plan was made with");
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const char* in = static_cast<const char*>(plan) + sizeof(PlanHeader);
+    // every matrix has its own workspace region (P, partials, T), so all
+    // encode launches may run before all decode launches
     for (int b = 0; b < h.nbatches; ++b) {
         PlanEntry e;
         std::memcpy(&e, in + static_cast<size_t>(b) * sizeof(PlanEntry), sizeof(e));
         e.B.eta = eta;
-        const int rc = launch_any(h.grad_dtype == GC_BF16, h.deferred != 0, e.B, e.pb, s);
+        const int rc = launch_any(h.grad_dtype == GC_BF16, h.deferred != 0, e.B, e.pb, s, phases);
         if (rc != GC_OK) return rc;
     }
     return GC_OK;
+}
+
+int gc_powersgd_run(const void* plan, size_t plan_bytes, float eta, void* ws, void* stream) {
+    return gc_powersgd_run_phases(plan, plan_bytes, eta, ws, PH_ALL, stream);
 }
 
 int gc_powersgd_materialize(const gc_mat* mats, const int32_t* prev_rank, int nmats, void* ws, size_t ws_bytes,

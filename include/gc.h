@@ -255,6 +255,25 @@ int gc_powersgd_plan(const gc_mat* mats, const int32_t* prev_rank, int nmats, in
  * GC_ERR_HIP. */
 int gc_powersgd_run(const void* plan, size_t plan_bytes, float eta, void* ws, void* stream);
 
+/* One or both phases of a recorded step.  The utility-of-compression paper's
+ * method section splits a compressed step into encode, exchange and decode;
+ * for the low-rank compressor the P and Q products are the encode and
+ * out = P^ Q'^T is the decode.
+ *   phases = 1 (encode): the first passes and the Q reduction.  On return
+ *            (in stream order) q holds Q' = M^T P^, and the workspace holds
+ *            P and the triangular factor T with P^ = P T.  For explicit
+ *            memory, mem is not yet updated.
+ *   phases = 2 (decode): the output pass.  It writes out, and P^ into p.
+ *            For explicit memory it also writes mem = M - out.  It must run
+ *            after the encode of the same plan, with no other run of the
+ *            plan in between.
+ *   phases = 3: both, the same as gc_powersgd_run.
+ * Between the two phases the stream may carry unrelated work, or other
+ * streams may run beside the decode.  A data-parallel step would put the
+ * exchange of Q' there.
+ * Errors: those of gc_powersgd_run, and GC_ERR_ARG for phases outside 1..3. */
+int gc_powersgd_run_phases(const void* plan, size_t plan_bytes, float eta, void* ws, int phases, void* stream);
+
 /* Writes the deferred memory out: for every matrix with prev_rank[i] > 0,
  * mem = mem - P^ Q^T over the first prev_rank[i] columns of p and q.
  * Afterwards mem holds m', bit for bit what gc_powersgd_ef_step would have

@@ -230,6 +230,10 @@ def test_powersgd_validation(gcl):
     assert L.gc_powersgd_run(None, pb, 1.0, 0x900000, None) == gcl.GC_ERR_ARG
     assert L.gc_powersgd_run(C.cast(zero, C.c_void_p), pb, 1.0, 0x900000, None) == gcl.GC_ERR_ARG   # no magic
     assert L.gc_powersgd_run(C.cast(zero, C.c_void_p), 8, 1.0, 0x900000, None) == gcl.GC_ERR_ARG    # short
+    for ph in (0, 4, -1):
+        assert L.gc_powersgd_run_phases(C.cast(zero, C.c_void_p), pb, 1.0, 0x900000, ph, None) == gcl.GC_ERR_ARG
+    assert L.gc_powersgd_run_phases(C.cast(zero, C.c_void_p), pb, 1.0, 0x900000, 1, None) == gcl.GC_ERR_ARG
+    assert L.gc_powersgd_run_phases(None, pb, 1.0, 0x900000, 2, None) == gcl.GC_ERR_ARG
 
 
 @no_gpu

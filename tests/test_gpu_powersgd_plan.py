@@ -101,6 +101,61 @@ def test_deferred_plan_matches_direct(dtype):
         compare_bitwise(A, B, f"deferred plan step {t}")
 
 
+@pytest.mark.parametrize("case", ["deferred-bf16", "explicit-f32", "many-deferred"])
+def test_phases_match_run(case):
+    """gc_powersgd_run_phases: the encode, unrelated work on the same stream
+    and on a second stream, then the decode, against gc_powersgd_run of an
+    identical set, bit for bit.  "many": 4100 matrices, so the plan holds
+    several batches and all their encodes run before all their decodes."""
+    gc = lib()
+    deferred = case != "explicit-f32"
+    if case.startswith("many"):
+        shapes = [(3 + i % 5, 8 if i % 3 else 5) for i in range(4100)]
+        ranks = [1 + i % 3 for i in range(4100)]
+        tdt = torch.float32
+    else:
+        shapes = [(300, 1024), (64, 27), (33, 4608), (128, 2048), (40, 4096), (1024, 1024)]
+        ranks = [4, 2, 3, 1, 4, 4]
+        tdt = torch.bfloat16 if case.endswith("bf16") else torch.float32
+    print(f"case: phases vs run, {case}", flush=True)
+
+    def grads(t):
+        out = [gen.gaussian_mat(n, m, 1700 + 17 * t + i, 1e-2) for i, (n, m) in enumerate(shapes)]
+        return [gen.f32_to_bf16_bits(g).reshape(g.shape) for g in out] if tdt == torch.bfloat16 else out
+
+    A, B = Set(shapes, ranks, 5), Set(shapes, ranks, 5)
+    ga, gb = grad_buffers(shapes, tdt), grad_buffers(shapes, tdt)
+    wsa, wsb = ws_for(A, ga), ws_for(B, gb)
+    fill(ga, grads(0))
+    fill(gb, grads(0))
+    if deferred:
+        A.deferred(ga, 1.0)
+        B.deferred(gb, 1.0)
+    prev = list(ranks) if deferred else None
+    pa = gc.gc_powersgd_plan(A.mats(ga), prev, wsa)
+    pb = gc.gc_powersgd_plan(B.mats(gb), prev, wsb)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    x = torch.randn(1 << 22, device=DEV)
+    ev = torch.cuda.Event()
+    for t, eta in zip(range(1, 4), [1.0, 0.5, 1.0]):
+        fill(ga, grads(t))
+        fill(gb, grads(t))
+        gc.gc_powersgd_run(pa, eta, wsa)
+        gc.gc_powersgd_run_phases(pb, eta, wsb, gc.PHASE_ENCODE)
+        y = x * 2.0                       # unrelated work between the phases
+        ev.record(main)
+        side.wait_event(ev)
+        with torch.cuda.stream(side):     # and beside the decode
+            z = x + 1.0
+        gc.gc_powersgd_run_phases(pb, eta, wsb, gc.PHASE_DECODE)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(y, x * 2.0) and torch.equal(z, x + 1.0)
+        # identical sets, identical calls: every buffer (deferred: mem holds M) equal
+        compare_all(A, B, f"{case} step {t}")
+
+
 def test_plan_replayed_in_graph():
     """A deferred plan captured in a HIP graph on the ResNet-18 set: each
     replay is one step; new gradients are copied in eagerly between replays,
