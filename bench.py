@@ -41,7 +41,7 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 # error-feedback memory form (PowerSGD and top-k): deferred unless --explicit
 PSGD_DEFERRED = True
-OVERLAP = False    # c5 --overlap: the embedding's top-k on a second stream beside the PowerSGD decode
+ORDER = "after"    # c5: where the embedding's top-k runs relative to the PowerSGD step (--order)
 
 
 def parse():
@@ -55,10 +55,10 @@ def parse():
                     help="write the error-feedback memory out every step (gc_powersgd_ef_step, gc_topk_ef_encode) "
                          "instead of keeping it in deferred form (gc_powersgd_ef_step_deferred, "
                          "gc_topk_ef_encode_deferred)")
-    ap.add_argument("--overlap", action="store_true",
-                    help="c5: run the embedding's top-k on a second stream beside the PowerSGD decode pass "
-                         "(gc_powersgd_run_phases) instead of after the PowerSGD step on one stream; measured "
-                         "slower, since the decode's many short workgroups hold every slot until they drain")
+    ap.add_argument("--order", default="after", choices=["after", "between", "overlap"],
+                    help="c5: the embedding's top-k after the PowerSGD step (default), between its encode and "
+                         "decode phases on the same stream, or on a second stream beside its decode phase "
+                         "(gc_powersgd_run_phases)")
     ap.add_argument("--flush", action="store_true",
                     help="between timed steps write 1 GiB, then read 1 GiB (cold last-level cache, no dirty lines)")
     ap.add_argument("--copy-calib", action="store_true", help="only run a 1 GiB device copy (counter calibration)")
@@ -267,8 +267,9 @@ class C5(Workload):
             if self.enc.deferred else "explicit: selected entries zeroed every step"
         self.config["powersgd_memory"] = "deferred: (M, P^, Q) kept, residual rebuilt in the next step's first pass" \
             if self.ps.deferred else "explicit: written out every step"
-        self.config["streams"] = "embedding top-k on a second stream beside the PowerSGD decode" if OVERLAP \
-            else "one stream"
+        self.config["topk_order"] = {"after": "embedding top-k after the PowerSGD step, one stream",
+                                     "between": "embedding top-k between the PowerSGD encode and decode, one stream",
+                                     "overlap": "embedding top-k on a second stream beside the PowerSGD decode"}[ORDER]
 
     def step(self, t):
         gc, s = self.gc, t % 2
@@ -286,9 +287,12 @@ class C5(Workload):
             self.norms_host.copy_(self.norms, non_blocking=True)
             self.pending = self.torch.cuda.Event()
             self.pending.record()
-        if not OVERLAP:
+        if ORDER == "after":
             self.ps.step(s)
             self._topk(views)
+            return
+        if ORDER == "between":
+            self.ps.step(s, between=lambda: self._topk(views))
             return
         # the embedding's top-k is independent of the PowerSGD matrices: here
         # it runs on a second stream beside the write-only decode pass (not
@@ -656,9 +660,9 @@ def main():
         return
 
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
-    global PSGD_DEFERRED, OVERLAP
+    global PSGD_DEFERRED, ORDER
     PSGD_DEFERRED = not args.explicit
-    OVERLAP = args.overlap
+    ORDER = args.order
     W = {"c5": C5, "c2": C2, "c3": C3, "c3acc": C3Acc, "c3randk": C3Randk, "c4": C4}[args.workload](torch, gc, dev)
     if hasattr(W, "prepare"):
         W.prepare(args.warmup + args.steps + 2)
