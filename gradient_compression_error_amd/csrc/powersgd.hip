@@ -1659,6 +1659,29 @@ size_t plan_bytes_for(int nmats) {
     return sizeof(PlanHeader) + static_cast<size_t>(nb) * sizeof(PlanEntry);
 }
 
+// Launches the given phases of every batch of a plan.  Every matrix has its
+// own workspace region (P, partials, T), so all encode launches may run
+// before all decode launches.
+int run_plan(const char* fn, const void* plan, size_t plan_bytes, float eta, void* ws, int phases, hipStream_t s) {
+    if (!plan || plan_bytes < sizeof(PlanHeader)) return fail(GC_ERR_ARG, std::string(fn) + ": null or short plan");
+    PlanHeader h;
+    std::memcpy(&h, plan, sizeof(h));
+    if (h.magic != PLAN_MAGIC || h.nbatches < 1 || h.nbatches > (INT32_MAX / PS_MAXB) + 1)
+        return fail(GC_ERR_ARG, std::string(fn) + ": not a plan written by gc_powersgd_plan");
+    if (plan_bytes < sizeof(PlanHeader) + static_cast<size_t>(h.nbatches) * sizeof(PlanEntry))
+        return fail(GC_ERR_ARG, std::string(fn) + ": plan buffer shorter than the plan");
+    if (ws != h.ws) return fail(GC_ERR_ARG, std::string(fn) + ": ws is not the workspace the plan was made with");
+    const char* in = static_cast<const char*>(plan) + sizeof(PlanHeader);
+    for (int b = 0; b < h.nbatches; ++b) {
+        PlanEntry e;
+        std::memcpy(&e, in + static_cast<size_t>(b) * sizeof(PlanEntry), sizeof(e));
+        e.B.eta = eta;
+        const int rc = launch_any(h.grad_dtype == GC_BF16, h.deferred != 0, e.B, e.pb, s, phases);
+        if (rc != GC_OK) return rc;
+    }
+    return GC_OK;
+}
+
 }  // namespace
 }  // namespace gc
 
@@ -1717,31 +1740,12 @@ int gc_powersgd_plan(const gc_mat* mats, const int32_t* prev_rank, int nmats, in
 }
 
 int gc_powersgd_run_phases(const void* plan, size_t plan_bytes, float eta, void* ws, int phases, void* stream) {
-    if (!plan || plan_bytes < sizeof(PlanHeader)) return fail(GC_ERR_ARG, "gc_powersgd_run: null or short plan");
     if (phases < 1 || phases > PH_ALL) return fail(GC_ERR_ARG, "gc_powersgd_run_phases: phases must be 1, 2 or 3");
-    PlanHeader h;
-    std::memcpy(&h, plan, sizeof(h));
-    if (h.magic != PLAN_MAGIC || h.nbatches < 1 || h.nbatches > (INT32_MAX / PS_MAXB) + 1)
-        return fail(GC_ERR_ARG, "gc_powersgd_run: not a plan written by gc_powersgd_plan");
-    if (plan_bytes < sizeof(PlanHeader) + static_cast<size_t>(h.nbatches) * sizeof(PlanEntry))
-        return fail(GC_ERR_ARG, "gc_powersgd_run: plan buffer shorter than the plan");
-    if (ws != h.ws) return fail(GC_ERR_ARG, "gc_powersgd_run: ws is not the workspace the plan was made with");
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    const char* in = static_cast<const char*>(plan) + sizeof(PlanHeader);
-    // every matrix has its own workspace region (P, partials, T), so all
-    // encode launches may run before all decode launches
-    for (int b = 0; b < h.nbatches; ++b) {
-        PlanEntry e;
-        std::memcpy(&e, in + static_cast<size_t>(b) * sizeof(PlanEntry), sizeof(e));
-        e.B.eta = eta;
-        const int rc = launch_any(h.grad_dtype == GC_BF16, h.deferred != 0, e.B, e.pb, s, phases);
-        if (rc != GC_OK) return rc;
-    }
-    return GC_OK;
+    return run_plan("gc_powersgd_run_phases", plan, plan_bytes, eta, ws, phases, static_cast<hipStream_t>(stream));
 }
 
 int gc_powersgd_run(const void* plan, size_t plan_bytes, float eta, void* ws, void* stream) {
-    return gc_powersgd_run_phases(plan, plan_bytes, eta, ws, PH_ALL, stream);
+    return run_plan("gc_powersgd_run", plan, plan_bytes, eta, ws, PH_ALL, static_cast<hipStream_t>(stream));
 }
 
 int gc_powersgd_materialize(const gc_mat* mats, const int32_t* prev_rank, int nmats, void* ws, size_t ws_bytes,
