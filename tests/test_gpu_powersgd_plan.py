@@ -156,14 +156,16 @@ def test_phases_match_run(case):
         compare_all(A, B, f"{case} step {t}")
 
 
-def test_plan_replayed_in_graph():
+@pytest.mark.parametrize("split", [False, True], ids=["run", "phases"])
+def test_plan_replayed_in_graph(split):
     """A deferred plan captured in a HIP graph on the ResNet-18 set: each
     replay is one step; new gradients are copied in eagerly between replays,
-    and every replay is compared with the direct deferred call."""
+    and every replay is compared with the direct deferred call.  "phases":
+    the capture holds the encode, a torch kernel, then the decode."""
     gc = lib()
     gc.gc_timing_enable(None)   # no timing events in the capture
     shapes, ranks = gen.RESNET18_MATS, [2] * len(gen.RESNET18_MATS)
-    print("case: deferred plan in a captured graph, ResNet-18", flush=True)
+    print(f"case: deferred plan in a captured graph, ResNet-18, split={split}", flush=True)
     A, B = Set(shapes, ranks, gen.CFG_C2), Set(shapes, ranks, gen.CFG_C2)
     ga, gb = grad_buffers(shapes, torch.float32), grad_buffers(shapes, torch.float32)
     wsb = ws_for(B, gb)
@@ -177,9 +179,16 @@ def test_plan_replayed_in_graph():
     graph = torch.cuda.CUDAGraph()
     # the capture records the launches only; what it computes is checked on replay
     snapshot = [[t.clone() for t in lst] for lst in (B.mem, B.q, B.p, B.out)]
+    x = torch.arange(4096, dtype=torch.float32, device=DEV)
+    y = torch.zeros_like(x)
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
-            gc.gc_powersgd_run(plan, 1.0, wsb)
+            if split:
+                gc.gc_powersgd_run_phases(plan, 1.0, wsb, gc.PHASE_ENCODE)
+                y.copy_(x * 3.0)
+                gc.gc_powersgd_run_phases(plan, 1.0, wsb, gc.PHASE_DECODE)
+            else:
+                gc.gc_powersgd_run(plan, 1.0, wsb)
     torch.cuda.synchronize()
     for lst, snap in zip((B.mem, B.q, B.p, B.out), snapshot):
         for t, s0 in zip(lst, snap):
@@ -194,6 +203,8 @@ def test_plan_replayed_in_graph():
         torch.cuda.synchronize()
         B.prev = list(ranks)
         compare_bitwise(A, B, f"graph replay {t}")
+        if split:
+            assert torch.equal(y, x * 3.0)
 
 
 def test_run_refuses_another_workspace():
