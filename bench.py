@@ -1,14 +1,17 @@
 """Benchmark: gradient GB/s through encode + decode + error feedback on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c2|c3|c3acc|c3randk|c4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c1|c2|c3|c3acc|c3randk|c4]
 
 A step is one pass of the whole compressor hot path over one gradient set:
   c5 (default): BERT-large gradient set (bf16 grads, fp32 memory):
       PowerSGD EF rank 4 on the 144 weight matrices, top-k EF (k = 1%) encode +
       decode on the 30522 x 1024 embedding, and every 10th step the Accordion
       check (per-layer norms of all 145 tensors -> host switch).
-  c2: ResNet-18 PowerSGD EF (rank 2), c3: ResNet-50-sized top-k EF (k = 1%),
-  c4: VGG-19 Accordion PowerSGD (rank 4/2, norms every 10 steps).
+  c1: the tiny Mem-SGD top-k case (d = 10,000, k = 100; latency only),
+  c2: ResNet-18 PowerSGD EF (rank 2) + its BN/bias vectors uncompressed,
+  c3: ResNet-50-sized top-k EF (k = 1%),
+  c4: VGG-19 Accordion PowerSGD (rank 4/2, norms every 10 steps) over the
+      steps of its norm trajectory around the first jump.
 Inputs are seeded synthetic arrays (gen/), uploaded before timing.
 
 Prints one JSON line (rank 0).  `value` is gradient GB/s = gradient bytes in
@@ -49,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c5", choices=["c2", "c3", "c3acc", "c3randk", "c4", "c5"])
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c3acc", "c3randk", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--explicit", action="store_true",
                     help="write the error-feedback memory out every step (gc_powersgd_ef_step, gc_topk_ef_encode) "
@@ -61,7 +64,12 @@ def parse():
                          "(gc_powersgd_run_phases)")
     ap.add_argument("--flush", action="store_true",
                     help="between timed steps write 1 GiB, then read 1 GiB (cold last-level cache, no dirty lines)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as a captured HIP graph (one graph per gradient set; steps that wait on "
+                         "the host, such as Accordion checks, run eagerly)")
     ap.add_argument("--copy-calib", action="store_true", help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--read-calib", action="store_true",
+                    help="only run a 1 GiB read-only reduction (second counter calibration)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     return ap.parse_args()
 
@@ -75,6 +83,19 @@ class Workload:
     alg_bytes = 0.0           # per step, amortised
     kernel_bytes = {}         # kernel name -> algorithmic bytes per step
     config = {}
+    dtype = "f32"             # arithmetic type of the path (gradients widen exactly to float32)
+    graphable = False         # steps may be captured as HIP graphs (--graph)
+
+    def graph_key(self, t):
+        """Which captured graph replays step t (None: run it eagerly)."""
+        return None
+
+    def host_part(self, t):
+        """Host-only work of step t that stays outside a captured graph."""
+
+    def device_step(self, t):
+        """The launches of step t (what a graph captures)."""
+        self.step(t)
 
     def step(self, t):
         raise NotImplementedError
@@ -97,7 +118,7 @@ class PowersgdPart:
     """Device buffers + ctypes table for a list of matrices sharing one flat memory buffer."""
 
     def __init__(self, torch, gc, shapes, ranks, grad_views_per_set, mem_views, dev, qcfg, deferred=None):
-        self.gc = gc
+        self.gc, self.torch = gc, torch
         # deferred: the memory is kept as (M, P^, Q) and rebuilt in the next
         # step's first pass (gc_powersgd_ef_step_deferred); prev = the ranks
         # of the previous call (0: mem holds the memory itself)
@@ -127,8 +148,15 @@ class PowersgdPart:
                                    p=self.p[i], out=self.out[i]) for i in range(len(self.shapes))])
 
     def set_ranks(self, ranks):
+        # the tables of the sets are brought to these ranks when next used
         self.ranks = list(ranks)
-        self.tables = [self._mats(s) for s in range(len(self.grads))]
+
+    def _sync_ranks(self, s):
+        tbl = self.tables[s]
+        for i, r in enumerate(self.ranks):
+            if tbl.arr[i].rank != r:
+                tbl.arr[i].rank = r
+                tbl.mats[i].rank = r
 
     def step(self, s, eta=1.0, between=None):
         """One recorded step; between(), if given, is called after the encode
@@ -136,6 +164,7 @@ class PowersgdPart:
         prev = self.prev if self.deferred else None
         key = (tuple(self.ranks), None if prev is None else tuple(prev))
         if self.plan_keys[s] != key:
+            self._sync_ranks(s)
             self.plans[s] = self.gc.gc_powersgd_plan(self.tables[s], prev, self.wss[s])
             self.plan_keys[s] = key
         if between is None:
@@ -271,9 +300,17 @@ class C5(Workload):
                                      "between": "embedding top-k between the PowerSGD encode and decode, one stream",
                                      "overlap": "embedding top-k on a second stream beside the PowerSGD decode"}[ORDER]
 
+    graphable = True
+
+    def graph_key(self, t):
+        return None if t % 10 == 0 else t % 2
+
     def step(self, t):
-        gc, s = self.gc, t % 2
-        views = self.sets[s][1]
+        self.host_part(t)
+        self.device_step(t)
+
+    def host_part(self, t):
+        gc = self.gc
         if self.pending is not None and self.pending.query():
             # the rank here is fixed, so the switch of the last check is only
             # recorded: it runs on the host once its norms have arrived,
@@ -282,6 +319,10 @@ class C5(Workload):
                                                             self.checks > 0)
             self.checks += 1
             self.pending = None
+
+    def device_step(self, t):
+        gc, s = self.gc, t % 2
+        views = self.sets[s][1]
         if t % 10 == 0:
             gc.gc_grad_norm(views, self.norms, self.nws)
             self.norms_host.copy_(self.norms, non_blocking=True)
@@ -315,6 +356,41 @@ class C5(Workload):
         self.gc.gc_topk_decode(self.idx, self.val, self.emb_out)
 
 
+class C1(Workload):
+    """The tiny Mem-SGD case: d = 10,000, k = 100, eta = 0.1, fresh N(0,1)
+    gradients per step (10 pre-generated, cycled).  Latency only: the vector
+    fits in one workgroup's worth of tiles, so no bandwidth claim is made."""
+    name = "c1"
+
+    def __init__(self, torch, gc, dev):
+        self.gc = gc
+        d, self.k = gen.C1_D, gen.C1_K
+        self.g = [torch.from_numpy(gen.c1_grad(t)).to(dev) for t in range(gen.C1_STEPS)]
+        self.mem = torch.zeros(d, device=dev)
+        self.out = torch.zeros(d, device=dev)
+        self.idx = torch.empty(self.k, dtype=torch.int32, device=dev)
+        self.val = torch.empty(self.k, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(gc.gc_topk_workspace_bytes(d, self.k), dtype=torch.uint8, device=dev)
+        self.enc = TopkEncoder(torch, gc, dev)
+        self.grad_bytes = 4 * d
+        self.alg_bytes = 16 * d + 16 * self.k
+        self.kernel_bytes = {"topk_accum_hist": 12 * d, "topk_decode_set": 4 * d + 8 * self.k}
+        self.description = gen.WORKLOADS["c1"].description + " (latency only)"
+        self.config = {"workload": "mem-sgd tiny vector", "params": d, "topk_k": self.k, "eta": gen.C1_ETA,
+                       "grad_dtype": "f32", "memory_dtype": "f32", "claim": "latency only"}
+        self.config["topk_memory"] = "deferred: acc kept, selection record marks the zeros" \
+            if self.enc.deferred else "explicit: selected entries zeroed every step"
+
+    graphable = True
+
+    def graph_key(self, t):
+        return t % len(self.g)
+
+    def step(self, t):
+        self.enc.encode(self.g[t % len(self.g)], self.mem, gen.C1_ETA, self.k, self.idx, self.val, self.ws)
+        self.gc.gc_topk_decode(self.idx, self.val, self.out)
+
+
 class C2(Workload):
     name = "c2"
 
@@ -329,18 +405,36 @@ class C2(Workload):
             self.sets.append(views)
         self.mem_buf, mem_views = _flat(torch, sizes, torch.float32, dev, 64)
         self.ps = PowersgdPart(torch, gc, shapes, [rank] * len(shapes), self.sets, mem_views, dev, gen.CFG_C2)
-        self.grad_bytes = 4 * sum(sizes)
-        self.alg_bytes = psgd_bytes(shapes, self.ps.ranks, 4)
+        # the BN/bias vectors, sent uncompressed (out = eta * g, no memory)
+        self.gc = gc
+        vsizes = gen.RESNET18_VECTORS
+        self.vsets = []
+        for s in range(2):
+            buf, views = _flat(torch, vsizes, torch.float32, dev, 64)
+            for v, g in enumerate(gen.c2_vectors(s)):
+                views[v].copy_(torch.from_numpy(g))
+            self.vsets.append(views)
+        self.vout_buf, self.vout = _flat(torch, vsizes, torch.float32, dev, 64)
+        ve = sum(vsizes)
         me = sum(sizes)
-        self.kernel_bytes = psgd_kernel_bytes(shapes, self.ps.ranks, 4)
+        self.grad_bytes = 4 * (me + ve)
+        self.alg_bytes = psgd_bytes(shapes, self.ps.ranks, 4) + 8 * ve
+        self.kernel_bytes = {**psgd_kernel_bytes(shapes, self.ps.ranks, 4), "passthrough": 8 * ve}
         self.description = gen.WORKLOADS["c2"].description + f" (rank {rank})"
-        self.config = {"workload": "resnet18 gradient set", "params": me, "powersgd_rank": rank,
+        self.config = {"workload": "resnet18 gradient set", "params": me + ve, "matrix_params": me,
+                       "vector_params": ve, "vectors": len(vsizes), "powersgd_rank": rank,
                        "grad_dtype": "f32", "memory_dtype": "f32"}
         self.config["powersgd_memory"] = "deferred: (M, P^, Q) kept, residual rebuilt in the next step's first pass" \
             if self.ps.deferred else "explicit: written out every step"
 
+    graphable = True
+
+    def graph_key(self, t):
+        return t % 2
+
     def step(self, t):
         self.ps.step(t % 2)
+        self.gc.gc_passthrough(self.vsets[t % 2], self.vout, 1.0)
 
 
 class C3(Workload):
@@ -365,6 +459,11 @@ class C3(Workload):
                        "grad_dtype": "f32", "memory_dtype": "f32", "eta": 1.0}
         self.config["topk_memory"] = "deferred: acc kept, selection record marks the zeros" \
             if self.enc.deferred else "explicit: selected entries zeroed every step"
+
+    graphable = True
+
+    def graph_key(self, t):
+        return t % 2
 
     def step(self, t):
         self.enc.encode(self.g[t % 2], self.mem, 1.0, self.k, self.idx, self.val, self.ws)
@@ -391,6 +490,11 @@ class C3Randk(Workload):
         self.description = gen.WORKLOADS["c3randk"].description
         self.config = {"workload": "resnet50-sized flat gradient, rand-k", "params": d, "randk_k": k,
                        "grad_dtype": "f32", "memory_dtype": "f32", "eta": 1.0}
+
+    graphable = True
+
+    def graph_key(self, t):
+        return t % 2
 
     def step(self, t):
         s = t % 2
@@ -456,46 +560,121 @@ class C3Acc(Workload):
         gc.gc_topk_decode(self.idx[:self.k], self.val[:self.k], self.out)
 
 
+def refill_q(part, layer, t, old_rank, new_rank, cfg):
+    """Rank growth on an Accordion switch: Q's columns past the old rank get
+    fresh seeded N(0,1) values (the first old_rank columns stay as written)."""
+    if new_rank > old_rank:
+        n, m = part.shapes[layer]
+        fresh = gen.q_refill(cfg, layer, t, m, 4)[old_rank:new_rank]
+        part.q[layer][old_rank:new_rank].copy_(part.torch.from_numpy(fresh))
+
+
 class C4(Workload):
+    """VGG-19 with Accordion on PowerSGD over its norm trajectory.
+
+    Every call is the next step tau of the trajectory (an internal counter:
+    the bench's warm-up, dominant-kernel and timed passes each advance it), and
+    tau's gradient (c4_grads(tau): the per-layer scale decays as e^(-tau/200)
+    and jumps x4 on [105, 205)) is pre-generated on the device.  The first
+    timed step is tau = 100, so the default 20 timed steps hold the check at
+    100 (l_high, rank 2) and the one at 110 after the jump (l_low, rank 4).
+    The norm history is seeded from the check at 90, as if the run had been
+    going since step 0.  At a check step the norms of tau's gradient decide
+    the ranks used from tau on (the norms are read back through pinned memory;
+    the host waits for them, since the step's ranks depend on them).  Rank
+    growth refills Q's new columns from the seeded stream.
+    Each step's gradient lives in its own buffer, so each has its own recorded
+    plan; a rehearsal of the whole run before timing records them all (a
+    training loop would reuse one gradient buffer and one plan per rank set)."""
     name = "c4"
+    FIRST_TIMED = 100
 
     def __init__(self, torch, gc, dev):
         self.gc, self.torch, self.dev = gc, torch, dev
-        shapes = gen.VGG19_MATS
-        sizes = [n * m for n, m in shapes]
-        self.shapes = shapes
+        self.shapes = shapes = gen.VGG19_MATS
+        self.sizes = [n * m for n, m in shapes]
+        self.mem_buf, self.mem_views = _flat(torch, self.sizes, torch.float32, dev, 64)
+        self.norms = torch.empty(len(shapes), device=dev)
+        self.norms_host = torch.empty(len(shapes), dtype=torch.float32, pin_memory=True)
+        self.ev_norm = torch.cuda.Event()
+        me = sum(self.sizes)
+        self.grad_bytes = 4 * me
+        self.ranks_log = []
+        self.kernel_bytes = {**psgd_kernel_bytes(shapes, [4] * len(shapes), 4), "norm_partial": 4 * me / 10.0}
+        self.description = gen.WORKLOADS["c4"].description + " (trajectory steps from 100, around the jump at 105)"
+        self.config = {"workload": "vgg19 gradient set", "params": me, "levels": "l_low=rank4, l_high=rank2",
+                       "grad_dtype": "f32", "memory_dtype": "f32", "accordion_check_every": 10,
+                       "first_timed_trajectory_step": self.FIRST_TIMED}
+        self.config["powersgd_memory"] = "deferred: (M, P^, Q) kept, residual rebuilt in the next step's first pass" \
+            if PSGD_DEFERRED else "explicit: written out every step"
+
+    def prepare(self, ncalls_before_timed, ncalls_total):
+        torch, gc = self.torch, self.gc
+        self.t0 = self.FIRST_TIMED - ncalls_before_timed
+        self.ntraj = ncalls_total
         self.sets = []
-        for s in range(2):
-            buf, views = _flat(torch, sizes, torch.float32, dev, 64)
-            for l, g in enumerate(gen.c4_grads(100 + s)):
+        for i in range(ncalls_total):
+            buf, views = _flat(torch, self.sizes, torch.float32, self.dev, 64)
+            for l, g in enumerate(gen.c4_grads(self.t0 + i)):
                 views[l].copy_(torch.from_numpy(g.ravel()))
             self.sets.append(views)
-        self.mem_buf, mem_views = _flat(torch, sizes, torch.float32, dev, 64)
-        self.ps = PowersgdPart(torch, gc, shapes, [4] * len(shapes), self.sets, mem_views, dev, gen.CFG_C4)
-        self.norms = torch.empty(len(sizes), device=dev)
-        self.nws = torch.empty(gc.gc_grad_norm_workspace_bytes(self.sets[0]), dtype=torch.uint8, device=dev)
-        self.prev = np.zeros(len(sizes), np.float32)
-        self.checks = 0
-        me = sum(sizes)
-        self.grad_bytes = 4 * me
-        self.alg_bytes = psgd_bytes(shapes, [4] * len(shapes), 4) + 4 * me / 10.0
-        self.kernel_bytes = {**psgd_kernel_bytes(shapes, [4] * len(shapes), 4), "norm_partial": 4 * me / 10.0}
-        self.description = gen.WORKLOADS["c4"].description
-        self.config = {"workload": "vgg19 gradient set", "params": me, "levels": "l_low=rank4, l_high=rank2",
-                       "grad_dtype": "f32", "memory_dtype": "f32", "accordion_check_every": 10}
-        self.config["powersgd_memory"] = "deferred: (M, P^, Q) kept, residual rebuilt in the next step's first pass" \
-            if self.ps.deferred else "explicit: written out every step"
+        self.ps = PowersgdPart(torch, gc, self.shapes, [4] * len(self.shapes), self.sets, self.mem_views, self.dev,
+                               gen.CFG_C4)
+        self.nws = torch.empty(gc.gc_grad_norm_workspace_bytes(self.sets[0]), dtype=torch.uint8, device=self.dev)
+        # the check before the window: its norms seed the history
+        last = (self.t0 - 1) // gen.C4_CHECK_EVERY * gen.C4_CHECK_EVERY
+        seed_views = _flat(torch, self.sizes, torch.float32, self.dev, 64)[1]
+        for l, g in enumerate(gen.c4_grads(last)):
+            seed_views[l].copy_(torch.from_numpy(g.ravel()))
+        gc.gc_grad_norm(seed_views, self.norms, self.nws)
+        self.seed_prev = self.norms.cpu().numpy().copy()
+        del seed_views
+        # rehearsal: records every step's plan, then the state starts over
+        self.reset()
+        for _ in range(ncalls_total):
+            self.step(None)
+        torch.cuda.synchronize()
+        self.reset()
+
+    def reset(self):
+        torch = self.torch
+        self.i = 0
+        self.prev_norms = self.seed_prev.copy()
+        self.mem_buf.zero_()
+        for l, (n, m) in enumerate(self.shapes):
+            self.ps.q[l].copy_(torch.from_numpy(gen.q_init(gen.CFG_C4, l, m)))
+        self.ps.prev = [0] * len(self.shapes)
+        # ranks in force before the first check of the window: those of the seeded check (l_high)
+        self.ps.set_ranks([gen.C4_RANK_HIGH_COMPRESSION] * len(self.shapes))
+        self.ranks_log = []
+
+    def timed_begin(self):
+        self.ranks_log = []
+
+    @property
+    def alg_bytes(self):
+        log = self.ranks_log or [[4] * len(self.shapes)]
+        me = sum(self.sizes)
+        return sum(psgd_bytes(self.shapes, r, 4) for r in log) / len(log) + 4 * me / 10.0
 
     def step(self, t):
-        gc, s = self.gc, t % 2
-        if t % 10 == 0:
-            gc.gc_grad_norm(self.sets[s], self.norms, self.nws)
-            lv, self.prev = gc.gc_accordion_select(self.norms.cpu().numpy(), self.prev, gen.C4_THRESHOLD,
-                                                   self.checks > 0)
-            self.checks += 1
-            self.ps.set_ranks([gen.C4_RANK_LOW_COMPRESSION if v == gc.GC_LEVEL_LOW else gen.C4_RANK_HIGH_COMPRESSION
-                               for v in lv])
-        self.ps.step(s)
+        gc, i = self.gc, self.i
+        tau = self.t0 + i
+        views = self.sets[i]
+        if tau % gen.C4_CHECK_EVERY == 0:
+            gc.gc_grad_norm(views, self.norms, self.nws)
+            self.norms_host.copy_(self.norms, non_blocking=True)
+            self.ev_norm.record()
+            self.ev_norm.synchronize()
+            lv, self.prev_norms = gc.gc_accordion_select(self.norms_host.numpy(), self.prev_norms,
+                                                         gen.C4_THRESHOLD, True)
+            new = [gen.C4_RANK_LOW_COMPRESSION if v == gc.GC_LEVEL_LOW else gen.C4_RANK_HIGH_COMPRESSION for v in lv]
+            for l, (old_r, new_r) in enumerate(zip(self.ps.ranks, new)):
+                refill_q(self.ps, l, tau, old_r, new_r, gen.CFG_C4)
+            self.ps.set_ranks(new)
+        self.ranks_log.append(list(self.ps.ranks))
+        self.ps.step(i)
+        self.i += 1
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
@@ -649,6 +828,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.read_calib:
+        n = 1 << 28   # 1 GiB of float32, summed: read once, a few bytes written
+        a = torch.ones(n, device=dev)
+        for _ in range(3):
+            a.sum()
+        torch.cuda.synchronize()
+        print(json.dumps({"read_calib_bytes_read": 4 * n, "launches": 3}))
+        return
+
     if args.copy_calib:
         n = 1 << 28   # 1 GiB of float32
         a = torch.ones(n, device=dev)
@@ -663,8 +851,13 @@ def main():
     global PSGD_DEFERRED, ORDER
     PSGD_DEFERRED = not args.explicit
     ORDER = args.order
-    W = {"c5": C5, "c2": C2, "c3": C3, "c3acc": C3Acc, "c3randk": C3Randk, "c4": C4}[args.workload](torch, gc, dev)
-    if hasattr(W, "prepare"):
+    W = {"c5": C5, "c1": C1, "c2": C2, "c3": C3, "c3acc": C3Acc, "c3randk": C3Randk,
+         "c4": C4}[args.workload](torch, gc, dev)
+    if isinstance(W, C4):
+        # calls before the timed ones: warm-up, then one per kernel in the dominant-kernel pass
+        before = args.warmup + len(W.kernel_bytes)
+        W.prepare(before, before + 2 * args.steps)
+    elif hasattr(W, "prepare"):
         W.prepare(args.warmup + args.steps + 2)
     torch.cuda.synchronize()
     # cold steps: writing 1 GiB evicts the step's buffers from the 256 MB
@@ -689,8 +882,39 @@ def main():
     gc.gc_timing_enable(None)
     dominant = max(shares, key=shares.get)
 
-    print(f"[bench] timing {args.steps} steps (dominant kernel {dominant})", file=sys.stderr, flush=True)
-    gc.gc_timing_enable(dominant)
+    graphs = {}
+    if args.graph:
+        if not W.graphable or args.flush:
+            print(json.dumps({"error": f"--graph is not available for workload {W.name}"
+                                       f"{' with --flush' if args.flush else ''}"}))
+            sys.exit(2)
+        # one graph per gradient set, captured after the warm-up (plans recorded,
+        # deferred memories past their first step); the launches are the step's own
+        steps_all = [args.warmup + 1 + t for t in range(args.steps)]
+        for t in steps_all:
+            key = W.graph_key(t)
+            if key is None or key in graphs:
+                continue
+            W.host_part(t)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                W.device_step(t)
+            graphs[key] = g
+        torch.cuda.synchronize()
+
+    def run_step(t):
+        key = W.graph_key(t) if graphs else None
+        if key is None:
+            W.step(t)
+        else:
+            W.host_part(t)
+            graphs[key].replay()
+
+    print(f"[bench] timing {args.steps} steps (dominant kernel {dominant}"
+          f"{', hip graph replay' if graphs else ''})", file=sys.stderr, flush=True)
+    # a replayed graph launches nothing through the library: its kernel times
+    # come from an eager pass after the timed one
+    gc.gc_timing_enable(None if graphs else dominant)
     if hasattr(W, "timed_begin"):
         W.timed_begin()
     torch.cuda.synchronize()
@@ -712,9 +936,14 @@ def main():
         # the timed region holds the steps and the dominant kernel's events only
         t0 = time.perf_counter()
         for t in range(args.steps):
-            W.step(args.warmup + 1 + t)
+            run_step(args.warmup + 1 + t)
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3
+    if graphs:
+        gc.gc_timing_enable(dominant)
+        for t in range(args.steps):
+            W.step(args.warmup + 1 + t)
+        torch.cuda.synchronize()
     k_ms, k_launches = gc.gc_timing_read()
     gc.gc_timing_enable(None)
     if not args.flush:
@@ -726,7 +955,7 @@ def main():
             W.timed_begin()
         for t in range(args.steps):
             evs[t].record()
-            W.step(args.warmup + 1 + t)
+            run_step(args.warmup + 1 + t)
         evs[-1].record()
         torch.cuda.synchronize()
         step_ms = [evs[t].elapsed_time(evs[t + 1]) for t in range(args.steps)]
@@ -754,8 +983,10 @@ def main():
             "us_per_step_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 1),
             "device_copy_gbs": round(copy_gbs, 1),
             "frac_of_device_copy_step": round(W.alg_bytes / (ms_step * 1e-3) / 1e9 / copy_gbs, 4),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": W.dtype,
+            "grad_dtype": W.config.get("grad_dtype", "f32"), "memory_dtype": W.config.get("memory_dtype", "f32"),
             "data": "synthetic", "cache": "cold: 1 GiB written then 1 GiB read between steps" if args.flush else "warm (back-to-back steps)",
+            "launch": "hip graph replay (eager: steps that wait on the host)" if graphs else "eager",
             "config": W.config, "description": W.description, "device": torch.cuda.get_device_name(0),
             "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
             "roofline": roof}

@@ -83,8 +83,13 @@ RESNET18_MATS = _expand([
     (3, 512, 4608), (1, 512, 256), (1, 100, 512),
 ])
 # BN weight+bias for every BN layer (4800 channels x 2) plus the fc bias (100):
-# passed uncompressed.
+# passed uncompressed.  BN layers of the CIFAR ResNet-18: the stem (64), four in
+# stage 1 (64), five in each later stage (two per block plus the shortcut's):
+# 128, 256, 512 channels.  Each BN layer has a scale and a shift vector.
+RESNET18_BN_CHANNELS = [64] * 5 + [128] * 5 + [256] * 5 + [512] * 5
+RESNET18_VECTORS = [c for c in RESNET18_BN_CHANNELS for _ in range(2)] + [100]
 RESNET18_VECTOR_ELEMS = 9700
+assert sum(RESNET18_VECTORS) == RESNET18_VECTOR_ELEMS
 
 # VGG-19 (CIFAR-100): 16 conv 3x3 layers, fc 512x512, 512x512, 100x512.
 VGG19_MATS = _expand([
@@ -138,6 +143,18 @@ def gaussian_matrix(config: int, step: int, layer: int, n: int, m: int, sigma: f
 def c2_grads(step: int) -> list[np.ndarray]:
     sig = layer_sigmas(CFG_C2, len(RESNET18_MATS))
     return [gaussian_matrix(CFG_C2, step, l, n, m, sig[l]) for l, (n, m) in enumerate(RESNET18_MATS)]
+
+
+def c2_vectors(step: int) -> list[np.ndarray]:
+    """The ResNet-18 BN/bias gradients of one step: N(0, s_v^2) per vector,
+    s_v = 10**U(-4,-2) fixed per vector (a stream of its own, so the matrix
+    draws above are unchanged)."""
+    sig = rng(CFG_C2, KIND_SCALE, 1).uniform(-4.0, -2.0, size=len(RESNET18_VECTORS))
+    out = []
+    for v, n in enumerate(RESNET18_VECTORS):
+        z = rng(CFG_C2, KIND_GRAD, step, 1000 + v).standard_normal(n, dtype=np.float32)
+        out.append((z * np.float32(10.0 ** sig[v])).astype(np.float32))
+    return out
 
 
 def q_init(config: int, layer: int, m: int, cols: int = 4) -> np.ndarray:
@@ -255,7 +272,7 @@ class Workload:
 
 WORKLOADS = {
     "c1": Workload("c1", "Mem-SGD top-k tiny: fp32 d=10,000, k=100, eta=0.1, 10 steps"),
-    "c2": Workload("c2", "ResNet-18 (CIFAR-100) gradient set, 21 matrices, PowerSGD EF rank 1/2"),
+    "c2": Workload("c2", "ResNet-18 (CIFAR-100) gradient set, 21 matrices PowerSGD EF rank 1/2 + 41 BN/bias vectors (9,700 entries) uncompressed"),
     "c3": Workload("c3", "ResNet-50-sized flat fp32 gradient d=25.6M, Student-t(3)*1e-3, top-k EF k=0.1%/1%"),
     "c3randk": Workload("c3randk", "ResNet-50-sized flat fp32 gradient d=25.6M, Student-t(3)*1e-3, rand-k EF k=1% (seeded subsets)"),
     "c4": Workload("c4", "VGG-19 (CIFAR-100) gradient set, Accordion PowerSGD rank 4/2, checks every 10 steps"),

@@ -41,6 +41,10 @@ class gc_span(C.Structure):
     _fields_ = [("ptr", C.c_void_p), ("len", C.c_int64)]
 
 
+class gc_vec(C.Structure):
+    _fields_ = [("grad", C.c_void_p), ("out", C.c_void_p), ("len", C.c_int64)]
+
+
 def _sig(name, res, *args):
     f = getattr(lib, name)
     f.restype = res
@@ -67,6 +71,7 @@ _sig("gc_powersgd_run", _i32, _vp, _sz, _f32, _vp, _vp)
 _sig("gc_powersgd_run_phases", _i32, _vp, _sz, _f32, _vp, _i32, _vp)
 _sig("gc_grad_norm_workspace_bytes", _sz, C.POINTER(gc_span), _i32)
 _sig("gc_grad_norm", _i32, C.POINTER(gc_span), _i32, _i32, _vp, _vp, _sz, _vp)
+_sig("gc_passthrough", _i32, C.POINTER(gc_vec), _i32, _i32, _f32, _vp)
 _sig("gc_accordion_select", _i32, C.POINTER(C.c_float), C.POINTER(C.c_float), _i32, _f32, _i32,
      C.POINTER(C.c_int))
 _sig("gc_timing_enable", _i32, C.c_char_p)
@@ -78,7 +83,8 @@ EXPORTED = ["gc_status_str", "gc_last_error", "gc_topk_workspace_bytes", "gc_top
             "gc_topk_decode", "gc_randk_ef_encode", "gc_powersgd_workspace_bytes", "gc_powersgd_ef_step",
             "gc_powersgd_ef_step_deferred", "gc_powersgd_materialize",
             "gc_powersgd_plan_bytes", "gc_powersgd_plan", "gc_powersgd_run", "gc_powersgd_run_phases",
-            "gc_grad_norm_workspace_bytes", "gc_grad_norm", "gc_accordion_select",
+            "gc_grad_norm_workspace_bytes", "gc_grad_norm", "gc_passthrough",
+            "gc_accordion_select",
             "gc_timing_enable", "gc_timing_read", "gc_kernel_names"]
 
 
@@ -371,6 +377,22 @@ def gc_powersgd_materialize(mats: Sequence[Mat], prev_rank, ws, stream=None) -> 
     arr = _mats([Mat(grad=None, mem=a.mem, q=a.q, rank=a.rank, p=a.p) for a in mats], prev, need_grad=False)
     _check(lib.gc_powersgd_materialize(arr, prev.ctypes.data_as(C.POINTER(C.c_int32)), len(mats), _ptr(ws),
                                        _nbytes(ws), _stream(stream)), "gc_powersgd_materialize")
+
+
+# ------------------------------------------------------------------ uncompressed tensors
+
+def gc_passthrough(grads, outs, eta: float, stream=None) -> None:
+    """Vectors sent uncompressed: outs[i] = eta * grads[i] (float32, one rounding)."""
+    import torch
+    _need(len(grads) >= 1 and len(grads) == len(outs), "need one out per gradient, at least one")
+    arr = (gc_vec * len(grads))()
+    for i, (g, o) in enumerate(zip(grads, outs)):
+        _dtype_is(o, torch.float32, f"outs[{i}]")
+        _need(g.dtype == grads[0].dtype, "every gradient must have the first one's dtype")
+        _need(g.numel() == o.numel(), f"grads[{i}] and outs[{i}] must have the same number of entries")
+        arr[i] = gc_vec(_ptr(g), _ptr(o), g.numel())
+    _check(lib.gc_passthrough(arr, len(grads), _dtype_code(grads[0]), float(eta), _stream(stream)),
+           "gc_passthrough")
 
 
 # ------------------------------------------------------------------ norms / Accordion

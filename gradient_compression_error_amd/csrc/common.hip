@@ -1,4 +1,5 @@
 // Status strings, per-thread error detail and the optional launch timing hooks.
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -24,7 +25,10 @@ int check_launch(const char* what) {
 
 // ---------------------------------------------------------------- timing hooks
 
+// The hooks are the library's only process-wide state.  A launch with
+// timing off reads one atomic flag and takes no lock.
 namespace {
+std::atomic<bool> g_timing_on{false};
 std::mutex g_tmu;
 std::string g_timed_name;
 struct EventPair { hipEvent_t a, b; };
@@ -32,6 +36,7 @@ std::vector<EventPair> g_events;
 }  // namespace
 
 TimedLaunch::TimedLaunch(const char* name, hipStream_t stream) : stream_(stream) {
+    if (!g_timing_on.load(std::memory_order_acquire)) return;
     std::lock_guard<std::mutex> lk(g_tmu);
     if (g_timed_name.empty() || g_timed_name != name) return;
     // timing-only events: no system-scope fence (its cache write-back and
@@ -85,6 +90,7 @@ int gc_timing_enable(const char* kernel_name) {
     std::lock_guard<std::mutex> lk(gc::g_tmu);
     gc::drop_events_locked();
     gc::g_timed_name = kernel_name ? kernel_name : "";
+    gc::g_timing_on.store(!gc::g_timed_name.empty(), std::memory_order_release);
     return GC_OK;
 }
 
@@ -114,7 +120,7 @@ const char* gc_kernel_names(void) {
     return "topk_prep,topk_accum_hist,topk_select1,topk_capture,topk_select2,topk_refine,"
            "topk_count,topk_emit,topk_materialize,topk_decode_set,topk_decode_add,randk_encode,"
            "psgd_pq,psgd_p,psgd_q,psgd_qreduce,psgd_out,psgd_decode,psgd_materialize,"
-           "norm_partial,norm_final";
+           "norm_partial,norm_final,passthrough";
 }
 
 }  // extern "C"

@@ -33,6 +33,12 @@ private:
 // Checks the launch status right after a kernel launch.
 int check_launch(const char* what);
 
+// Per-layer norms (norm.hip): argument checks, the number of float64 tile
+// partials, and the two launches with the partials in `partial`.
+int check_norm_args(const char* fn, const gc_span* layers, int nlayers, int grad_dtype, const float* norms);
+size_t partial_count(const gc_span* layers, int nlayers);
+int launch_norms(const gc_span* layers, int nlayers, int grad_dtype, float* norms, double* partial, hipStream_t s);
+
 // ---------------------------------------------------------------- device side
 
 constexpr int WAVE = 64;

@@ -8,6 +8,7 @@
 //                 sums (float64) one 16384-entry tile of one layer
 //   norm_final    one workgroup per layer sums its tile partials in a fixed
 //                 order and writes sqrt(sum) as float32
+// gc_grad_norm takes the tile partials in the caller's workspace.
 // gc_accordion_select is plain host code: the decision needs the norms of
 // the previous check, which the caller keeps.
 #include <cmath>
@@ -79,44 +80,34 @@ __global__ __launch_bounds__(NM_THREADS) void norm_final(const NmBatch B) {
     if (threadIdx.x == 0) B.norms[blockIdx.x] = static_cast<float>(sqrt(((s_w[0] + s_w[1]) + s_w[2]) + s_w[3]));
 }
 
+}  // namespace
+
+// Tile partials (float64) the norm pass writes for these layers.
 size_t partial_count(const gc_span* layers, int nlayers) {
     size_t n = 0;
     for (int i = 0; i < nlayers; ++i) n += static_cast<size_t>((layers[i].len + NM_TILE - 1) / NM_TILE);
     return n;
 }
 
-}  // namespace
-}  // namespace gc
-
-using namespace gc;
-
-extern "C" {
-
-size_t gc_grad_norm_workspace_bytes(const gc_span* layers, int nlayers) {
-    if (!layers || nlayers < 1) return 0;
-    for (int i = 0; i < nlayers; ++i)
-        if (layers[i].len < 1) return 0;
-    return round_up(partial_count(layers, nlayers) * sizeof(double), 256);
-}
-
-int gc_grad_norm(const gc_span* layers, int nlayers, int grad_dtype, float* norms,
-                 void* ws, size_t ws_bytes, void* stream) {
-    if (!layers || nlayers < 1 || !norms || !ws)
-        return fail(GC_ERR_ARG, "gc_grad_norm: null pointer or nlayers < 1");
+// Argument checks of the norm entry points (fn names the caller).
+int check_norm_args(const char* fn, const gc_span* layers, int nlayers, int grad_dtype, const float* norms) {
+    const std::string f(fn);
+    if (!layers || nlayers < 1 || !norms) return fail(GC_ERR_ARG, f + ": null pointer or nlayers < 1");
     if (grad_dtype != GC_F32 && grad_dtype != GC_BF16)
-        return fail(GC_ERR_DTYPE, "gc_grad_norm: grad_dtype must be GC_F32 or GC_BF16");
-    if (!aligned16(norms) || !aligned16(ws))
-        return fail(GC_ERR_ARG, "gc_grad_norm: device pointers must be 16-byte aligned");
+        return fail(GC_ERR_DTYPE, f + ": grad_dtype must be GC_F32 or GC_BF16");
+    if (!aligned16(norms)) return fail(GC_ERR_ARG, f + ": device pointers must be 16-byte aligned");
     for (int i = 0; i < nlayers; ++i) {
         if (!layers[i].ptr || layers[i].len < 1)
-            return fail(GC_ERR_ARG, "gc_grad_norm: layer " + std::to_string(i) + " has a null pointer or len < 1");
+            return fail(GC_ERR_ARG, f + ": layer " + std::to_string(i) + " has a null pointer or len < 1");
         if (!aligned16(layers[i].ptr))
-            return fail(GC_ERR_ARG, "gc_grad_norm: layer " + std::to_string(i) + " is not 16-byte aligned");
+            return fail(GC_ERR_ARG, f + ": layer " + std::to_string(i) + " is not 16-byte aligned");
     }
-    if (ws_bytes < gc_grad_norm_workspace_bytes(layers, nlayers))
-        return fail(GC_ERR_WORKSPACE, "gc_grad_norm: workspace smaller than gc_grad_norm_workspace_bytes");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    double* partial = static_cast<double*>(ws);
+    return GC_OK;
+}
+
+// The two norm launches over every layer, the tile partials in `partial`
+// (partial_count doubles).
+int launch_norms(const gc_span* layers, int nlayers, int grad_dtype, float* norms, double* partial, hipStream_t s) {
     for (int l0 = 0; l0 < nlayers; l0 += NM_MAXL) {
         NmBatch B{};
         B.partial = partial;
@@ -145,6 +136,30 @@ int gc_grad_norm(const gc_span* layers, int nlayers, int grad_dtype, float* norm
         partial += blocks;
     }
     return GC_OK;
+}
+
+}  // namespace gc
+
+using namespace gc;
+
+extern "C" {
+
+size_t gc_grad_norm_workspace_bytes(const gc_span* layers, int nlayers) {
+    if (!layers || nlayers < 1) return 0;
+    for (int i = 0; i < nlayers; ++i)
+        if (layers[i].len < 1) return 0;
+    return round_up(partial_count(layers, nlayers) * sizeof(double), 256);
+}
+
+int gc_grad_norm(const gc_span* layers, int nlayers, int grad_dtype, float* norms,
+                 void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_norm_args("gc_grad_norm", layers, nlayers, grad_dtype, norms);
+    if (rc != GC_OK) return rc;
+    if (!ws) return fail(GC_ERR_ARG, "gc_grad_norm: null workspace");
+    if (!aligned16(ws)) return fail(GC_ERR_ARG, "gc_grad_norm: device pointers must be 16-byte aligned");
+    if (ws_bytes < gc_grad_norm_workspace_bytes(layers, nlayers))
+        return fail(GC_ERR_WORKSPACE, "gc_grad_norm: workspace smaller than gc_grad_norm_workspace_bytes");
+    return launch_norms(layers, nlayers, grad_dtype, norms, static_cast<double*>(ws), static_cast<hipStream_t>(stream));
 }
 
 int gc_accordion_select(const float* norm_now, float* norm_prev, int nlayers, float threshold,

@@ -31,6 +31,10 @@
  *   - Results are deterministic: the same inputs give the same bits on every
  *     call (all reductions have a fixed order; no floating-point atomics).
  *   - Calls that share a workspace must not overlap in time (use one stream).
+ *   - Process-wide state: the library keeps none in its compute calls, so
+ *     calls on different streams with their own buffers are independent.  One
+ *     exception, documented where declared: the measurement hooks
+ *     (gc_timing_enable / gc_timing_read).
  */
 #ifndef GC_H
 #define GC_H
@@ -269,8 +273,12 @@ int gc_powersgd_run(const void* plan, size_t plan_bytes, float eta, void* ws, vo
  *            plan in between.
  *   phases = 3: both, the same as gc_powersgd_run.
  * Between the two phases the stream may carry unrelated work, or other
- * streams may run beside the decode.  A data-parallel step would put the
- * exchange of Q' there.
+ * streams may run beside the decode.  The split point is where a
+ * data-parallel step would exchange Q'.  That alone would not make a correct
+ * multi-worker step: the fused encode forms M^T P from this worker's own P
+ * before orthonormalising, whereas a multi-worker step has to reduce P over
+ * the workers first, which needs the encode split again (P pass, exchange of
+ * P, then the Q pass).  These phases are the single-worker step.
  * Errors: those of gc_powersgd_run, and GC_ERR_ARG for phases outside 1..3. */
 int gc_powersgd_run_phases(const void* plan, size_t plan_bytes, float eta, void* ws, int phases, void* stream);
 
@@ -286,6 +294,27 @@ int gc_powersgd_run_phases(const void* plan, size_t plan_bytes, float eta, void*
  * buffers), GC_ERR_WORKSPACE, GC_ERR_HIP. */
 int gc_powersgd_materialize(const gc_mat* mats, const int32_t* prev_rank, int nmats, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Tensors sent uncompressed                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* One vector sent without compression (a batch-norm scale or shift, a bias). */
+typedef struct gc_vec {
+    const void* grad;  /* [len] float32 or bf16, read only   */
+    float* out;        /* [len] float32 out                  */
+    int64_t len;       /* 1 <= len <= INT32_MAX              */
+} gc_vec;
+
+/* The step of the tensors a gradient set sends as they are: the compressors
+ * of the Accordion paper's method section work on the weight matrices, and
+ * the vectors of the set (batch-norm parameters, biases) go out uncompressed:
+ *     out = fl32(eta * grad)            (one float32 rounding)
+ * They keep no error-feedback memory: nothing is left out.  One launch per
+ * 120 vectors ([host] array vecs, nvecs >= 1).
+ * Errors: GC_ERR_ARG (null pointer, len out of range, misalignment, an out
+ * overlapping any gradient or another out), GC_ERR_DTYPE, GC_ERR_HIP. */
+int gc_passthrough(const gc_vec* vecs, int nvecs, int grad_dtype, float eta, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Accordion: per-layer norms and the l_low / l_high switch                 */
@@ -306,6 +335,7 @@ size_t gc_grad_norm_workspace_bytes(const gc_span* layers, int nlayers);
 int gc_grad_norm(const gc_span* layers, int nlayers, int grad_dtype, float* norms,
                  void* ws, size_t ws_bytes, void* stream);
 
+
 /* Host-only level choice for one check (Accordion, method section), per layer l:
  *   has_prev == 0            -> GC_LEVEL_LOW
  *   rho = |prev - now| / prev (prev == 0: rho = +inf if now > 0, else 0)
@@ -322,7 +352,10 @@ int gc_accordion_select(const float* norm_now, float* norm_prev, int nlayers, fl
 
 /* Bracket every launch of the kernel named `kernel_name` (as listed by
  * gc_kernel_names) with a pair of HIP events recorded on the launch stream;
- * NULL or "" switches timing off and drops recorded events.  Process-wide. */
+ * NULL or "" switches timing off and drops recorded events.
+ * These hooks are process-wide state (one timed kernel name and its recorded
+ * events, behind a mutex).  With timing off a launch only reads one atomic
+ * flag and takes no lock. */
 int gc_timing_enable(const char* kernel_name);
 
 /* Synchronise on the recorded events and return the summed duration (ms) and

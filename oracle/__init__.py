@@ -22,7 +22,8 @@ Sources (the three review pages):
 
 PowerSGD's individual steps (P = M Q, orthonormalise P, Q = M^T P, decode
 P Q^T, residual into memory) are not spelled out on the pages; the oracle takes
-them in that plain order (see ``powersgd.py``).
+them in that plain order (see ``powersgd.py``).  The vectors of a gradient set
+(batch-norm parameters, biases) are sent uncompressed (``passthrough.py``).
 
 Parity pins: every function here is checked in ``tests/test_oracle_*.py``
 against closed forms, brute force, library special cases or invariants fixed by
@@ -33,12 +34,13 @@ from .topk_ef import (ef_accumulate, grad_to_f64, topk_select, topk_ef_step,
                       topk_decode, magnitude_order)
 from .randk_ef import randk_ef_step
 from .powersgd import orthonormalize_mgs, powersgd_ef_step
+from .passthrough import passthrough_step
 from .norms import grad_norm
 from .accordion import accordion_select, LEVEL_LOW, LEVEL_HIGH
 from .memsgd import run_memsgd, QuadraticProblem
 
 __all__ = [
     "ef_accumulate", "grad_to_f64", "topk_select", "topk_ef_step", "topk_decode",
-    "magnitude_order", "randk_ef_step", "orthonormalize_mgs", "powersgd_ef_step", "grad_norm",
+    "magnitude_order", "randk_ef_step", "orthonormalize_mgs", "powersgd_ef_step", "passthrough_step", "grad_norm",
     "accordion_select", "LEVEL_LOW", "LEVEL_HIGH", "run_memsgd", "QuadraticProblem",
 ]

@@ -251,6 +251,40 @@ def test_norm_validation(gcl):
     assert L.gc_grad_norm(empty, 1, 0, 0x300000, 0x400000, 1 << 20, None) == gcl.GC_ERR_ARG
 
 
+@no_gpu
+def test_passthrough_validation(gcl):
+    L = gcl.lib
+    V = gcl.gc_vec
+    ok = (V * 2)(V(0x100000, 0x200000, 64), V(0x300000, 0x400000, 9000))
+    assert L.gc_passthrough(None, 2, 0, 1.0, None) == gcl.GC_ERR_ARG
+    assert L.gc_passthrough(ok, 0, 0, 1.0, None) == gcl.GC_ERR_ARG
+    assert L.gc_passthrough(ok, 2, 9, 1.0, None) == gcl.GC_ERR_DTYPE
+    for bad in [V(None, 0x200000, 64), V(0x100000, None, 64), V(0x100000, 0x200000, 0),
+                V(0x100000, 0x200000, 2**31), V(0x100004, 0x200000, 64), V(0x100000, 0x200008, 64)]:
+        arr = (V * 2)(bad, V(0x300000, 0x400000, 9000))
+        assert L.gc_passthrough(arr, 2, 0, 1.0, None) == gcl.GC_ERR_ARG
+    # an output over its own gradient, over another vector's gradient, over another output
+    for a, b in [(V(0x100000, 0x100000, 64), V(0x300000, 0x400000, 10)),
+                 (V(0x100000, 0x300010, 64), V(0x300000, 0x400000, 10)),
+                 (V(0x100000, 0x400020, 64), V(0x300000, 0x400000, 10))]:
+        assert L.gc_passthrough((V * 2)(a, b), 2, 0, 1.0, None) == gcl.GC_ERR_ARG
+    assert "overlaps" in gcl.gc_last_error()
+    # gradients may overlap each other (read only): fails later only on the missing GPU, not on validation
+    # (not called here: validation would pass and a launch would follow)
+
+
+@no_gpu
+def test_passthrough_binding_checks(gcl):
+    import torch
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)
+    with pytest.raises(ValueError, match="same number of entries"):
+        gcl.gc_passthrough([f32(4)], [f32(5)], 1.0)
+    with pytest.raises(ValueError, match="one out per gradient"):
+        gcl.gc_passthrough([f32(4), f32(4)], [f32(4)], 1.0)
+    with pytest.raises(TypeError, match="outs"):
+        gcl.gc_passthrough([f32(4)], [torch.zeros(4, dtype=torch.float64)], 1.0)
+
+
 def test_accordion_host_matches_oracle(gcl):
     r = gen.rng(0, gen.KIND_MISC, 200)
     for trial in range(50):

@@ -1,0 +1,208 @@
+"""GPU parity of whole configurations, through the code the benchmark runs.
+
+Each test drives the benchmark's own step objects (bench.py: PowersgdPart's
+recorded deferred plans, TopkEncoder's deferred top-k, the uncompressed
+vectors) and compares every checked step with the float64 oracle from the
+state the GPU held before that step: the deferred memories are written out
+(gc_powersgd_materialize / gc_topk_materialize on copies) and fed to the
+oracle step together with Q and the step's gradient.  PowerSGD results (P^,
+Q, out, memory) must agree within a relative Frobenius error of 1e-4 per
+matrix (an absolute 1e-4 * ||M|| where the oracle's value is ~0); top-k and
+the uncompressed vectors must agree bit for bit.
+
+  * ResNet-18 (CIFAR-100): 21 matrices at rank 2 plus the 41 BN/bias vectors
+    sent uncompressed, 4 steps over the two alternating gradient sets.
+  * VGG-19 with Accordion: the norm trajectory from step 0 to 220, one
+    gradient buffer refilled per step (as a training loop would), the per-layer
+    norms taken on the GPU every 10 steps, the levels chosen by
+    gc_accordion_select (l_low = rank 4, l_high = rank 2), the plan recorded
+    again at each switch and Q's new columns refilled on rank growth.  Every
+    step of 100..120 and 200..220 (both jumps) is compared with the oracle;
+    the decisions at every check equal the closed-form schedule, and at the
+    window checks the oracle's own norms give the same decisions.
+  * BERT-large: the benchmark's C5 step (all 144 matrices in one recorded
+    plan, the embedding's top-k 1%), 4 steps; encoder layers 0 and 23 (12
+    matrices) and the embedding are compared every step.
+"""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gpu_util import DEV, f32_bits, lib, rel_err, require_gpu, to_dev
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+class Snapshot:
+    """The state a PowerSGD step starts from, for the chosen matrices: the
+    memory the method carries (the deferred memory written out into copies)
+    and the first `rank` columns of Q."""
+
+    def __init__(self, part, layers, ws):
+        gc = lib()
+        copies = [part.mem[i].clone() for i in layers]
+        mats = [gc.Mat(grad=None, mem=c, q=part.q[i], rank=max(1, part.ranks[i]), p=part.p[i])
+                for c, i in zip(copies, layers)]
+        gc.gc_powersgd_materialize(mats, [part.prev[i] for i in layers], ws)
+        torch.cuda.synchronize()
+        self.mem = {i: c.cpu().numpy() for c, i in zip(copies, layers)}
+        self.q = {i: part.q[i][: part.ranks[i]].cpu().numpy().T.copy() for i in layers}
+
+
+def materialize_ws(part, layers):
+    gc = lib()
+    mats = [gc.Mat(grad=None, mem=part.mem[i], q=part.q[i], rank=1, p=part.p[i]) for i in layers]
+    return torch.empty(gc.gc_powersgd_workspace_bytes(mats), dtype=torch.uint8, device=DEV)
+
+
+def check_psgd_step(part, layers, before, after, grads_h, label):
+    """The GPU step (before -> after, and its out / P^ / Q) against the oracle step from `before`."""
+    worst = 0.0
+    for i in layers:
+        r = part.ranks[i]
+        ref = oracle.powersgd_ef_step(grads_h[i], before.mem[i], before.q[i], 1.0, r)
+        Mn = np.linalg.norm(ref["M"])
+        checks = [("P", part.p[i][:r].cpu().numpy().T, ref["P"]), ("Q", after.q[i], ref["Q"]),
+                  ("out", part.out[i].cpu().numpy(), ref["out"]), ("mem", after.mem[i], ref["mem"])]
+        for name, got, want in checks:
+            if name in ("mem", "out") and np.linalg.norm(want) < 1e-6 * Mn:
+                err = float(np.linalg.norm(got.astype(np.float64) - want) / Mn)
+            else:
+                err = rel_err(got, want)
+            worst = max(worst, err)
+            assert err <= TOL, f"{label}: matrix {i} {part.shapes[i]} r={r} {name}: rel err {err:.3e}"
+    return worst
+
+
+def test_c2_resnet18_with_vectors():
+    """The ResNet-18 step of the benchmark: PowerSGD rank 2 (recorded deferred
+    plan) on the 21 matrices and the BN/bias vectors uncompressed."""
+    print("case: C2 ResNet-18 config, 4 steps", flush=True)
+    gc = lib()
+    W = bench.C2(torch, gc, DEV)
+    part = W.ps
+    layers = list(range(len(part.shapes)))
+    ws = materialize_ws(part, layers)
+    for t in range(4):
+        grads_h = gen.c2_grads(t % 2)
+        before = Snapshot(part, layers, ws)
+        W.step(t)
+        torch.cuda.synchronize()
+        after = Snapshot(part, layers, ws)
+        worst = check_psgd_step(part, layers, before, after, grads_h, f"C2 step {t}")
+        for v, h in enumerate(gen.c2_vectors(t % 2)):
+            assert np.array_equal(f32_bits(W.vout[v]), f32_bits(oracle.passthrough_step(h, 1.0))), \
+                f"C2 step {t} vector {v}"
+        print(f"C2 step {t}: worst PowerSGD relative error {worst:.2e}", flush=True)
+
+
+WINDOWS = list(range(100, 121)) + list(range(200, 221))
+
+
+def test_c4_vgg19_accordion_end_to_end():
+    print("case: C4 VGG-19 Accordion end to end, steps 0..220", flush=True)
+    gc = lib()
+    gold = json.load(open(os.path.join(GOLD, "c4_accordion_schedule.json")))
+    thr = gold["threshold"]
+    shapes = gen.VGG19_MATS
+    sizes = [n * m for n, m in shapes]
+    L = len(shapes)
+    _, mem_views = bench._flat(torch, sizes, torch.float32, DEV, 64)
+    _, gviews = bench._flat(torch, sizes, torch.float32, DEV, 64)
+    part = bench.PowersgdPart(torch, gc, shapes, [gen.C4_RANK_LOW_COMPRESSION] * L, [gviews], mem_views, DEV,
+                              gen.CFG_C4, deferred=True)
+    layers = list(range(L))
+    ws = materialize_ws(part, layers)
+    norms = torch.empty(L, device=DEV)
+    nws = torch.empty(gc.gc_grad_norm_workspace_bytes(gviews), dtype=torch.uint8, device=DEV)
+    prev = np.zeros(L, np.float32)
+    lows, worst, plans = [], 0.0, 0
+    last_key = None
+    for t in range(WINDOWS[-1] + 1):
+        host = gen.c4_grads(t)
+        for v, h in zip(gviews, host):
+            v.copy_(torch.from_numpy(h.ravel()))
+        if t % gold["check_every"] == 0:
+            gc.gc_grad_norm(gviews, norms, nws)
+            got = norms.cpu().numpy()
+            prev_before = prev.copy()
+            lv, prev = gc.gc_accordion_select(got, prev, thr, t > 0)
+            assert len(set(lv.tolist())) == 1, f"check {t}: layers disagree {lv}"
+            if lv[0] == gc.GC_LEVEL_LOW:
+                lows.append(t)
+            if t in WINDOWS:
+                want = np.array([oracle.grad_norm(h) for h in host])
+                assert np.all(np.abs(got - want) <= TOL * want), f"check {t}: norms"
+                olv, _ = oracle.accordion_select(want.astype(np.float32), prev_before, True, thr)
+                assert np.array_equal(olv, lv), f"check {t}: oracle decisions differ"
+            new = [gen.C4_RANK_LOW_COMPRESSION if x == gc.GC_LEVEL_LOW else gen.C4_RANK_HIGH_COMPRESSION for x in lv]
+            for l in layers:
+                bench.refill_q(part, l, t, part.ranks[l], new[l], gen.CFG_C4)
+            part.set_ranks(new)
+        check = t in WINDOWS
+        if check:
+            before = Snapshot(part, layers, ws)
+        part.step(0)
+        if part.plan_keys[0] != last_key:
+            plans += 1
+            last_key = part.plan_keys[0]
+        if check:
+            torch.cuda.synchronize()
+            after = Snapshot(part, layers, ws)
+            worst = max(worst, check_psgd_step(part, layers, before, after, host, f"C4 step {t}"))
+    assert lows == [c for c in gold["low_checks"] if c <= WINDOWS[-1]]
+    # plans: the first step (prev 0), the steady rank-4 plan, then per switch the
+    # switching step's plan and the steady plan after it
+    assert plans >= 6
+    print(f"C4 checks at l_low: {lows}; plans recorded: {plans}; worst relative error {worst:.2e}", flush=True)
+
+
+def test_c5_bert_shipped_steps():
+    print("case: C5 BERT-large shipped step (bench.C5), 4 steps", flush=True)
+    gc = lib()
+    W = bench.C5(torch, gc, DEV)
+    part = W.ps
+    layers = list(range(6)) + list(range(138, 144))
+    ws = materialize_ws(part, layers)
+    d, k = W.emb_mem.numel(), W.k
+    for t in range(4):
+        s = t % 2
+        grads_h = {i: gen.c5_matrix_bf16(s, i).reshape(part.shapes[i]) for i in layers}
+        before = Snapshot(part, layers, ws)
+        emb_before = W.emb_mem.clone()
+        if W.enc.has_prev:
+            gc.gc_topk_materialize(emb_before, W.enc.sel)
+        W.step(t)
+        torch.cuda.synchronize()
+        after = Snapshot(part, layers, ws)
+        worst = check_psgd_step(part, layers, before, after, grads_h, f"C5 step {t}")
+        emb_after = W.emb_mem.clone()
+        gc.gc_topk_materialize(emb_after, W.enc.sel)
+        ref = oracle.topk_ef_step(emb_before.cpu().numpy(), gen.c5_embedding_bf16(s), 1.0, k)
+        torch.cuda.synchronize()
+        assert np.array_equal(W.idx.cpu().numpy(), ref["idx"]), f"C5 step {t}: embedding top-k indices"
+        assert np.array_equal(f32_bits(W.val), f32_bits(ref["val"])), f"C5 step {t}: embedding top-k values"
+        assert np.array_equal(f32_bits(emb_after), f32_bits(ref["mem"])), f"C5 step {t}: embedding memory"
+        out = W.emb_out.cpu().numpy()
+        assert np.array_equal(out, oracle.topk_decode(ref["idx"], ref["val"], d)), f"C5 step {t}: decode"
+        print(f"C5 step {t}: worst PowerSGD relative error {worst:.2e}", flush=True)
+    del W
+    torch.cuda.empty_cache()

@@ -60,8 +60,9 @@ def check_step(ps, grads_h, eta, label="", cond_scaled=False):
     """One GPU step compared with the oracle from the same state; returns max error.
 
     cond_scaled: allow max(1e-4, 10 * 2^-24 * cond(P)) per matrix -- the float32
-    limit of any method on a nearly rank-deficient P (the pages' 1e-4 holds for
-    the configured data, whose P are well conditioned)."""
+    limit of any method on a nearly rank-deficient P.  Only
+    test_conditioning_limit_near_degenerate_p uses it; every other case holds
+    the flat 1e-4 of the method statement."""
     mem_before = [t.cpu().numpy() for t in ps.mem]
     q_before = [t.cpu().numpy() for t in ps.q]
     ps.step([to_dev(g) for g in grads_h], eta)
@@ -124,15 +125,66 @@ def test_c2_resnet18(rank):
         check_step(ps, gen.c2_grads(t), 1.0, f"C2 step {t}")
 
 
+# Parity sets at the flat 1e-4 bar avoid near-degenerate P: a matrix whose
+# P = M Q_in (predicted with the oracle for every step the test runs) has a
+# condition number above COND_MAX is drawn again.  float32 rounding of P moves
+# its column space by about eps32 * cond(P), which at cond(P) <= 100 stays far
+# below 1e-4; larger condition numbers are the subject of
+# test_conditioning_limit_near_degenerate_p alone.
+COND_MAX = 100.0
+
+
+def well_conditioned(grad_h, q_h, r, steps, eta=1.0):
+    """cond(P) <= COND_MAX at each of `steps` oracle steps from m = 0 and Q_in = q_h (cols, m)."""
+    mem = np.zeros(grad_h.shape, np.float32)
+    q = q_h[:r].T.astype(np.float32)
+    for _ in range(steps):
+        M = mem.astype(np.float64) + np.float64(np.float32(eta)) * oracle.grad_to_f64(grad_h).reshape(mem.shape)
+        if np.linalg.cond(M @ q.astype(np.float64)) > COND_MAX:
+            return False
+        ref = oracle.powersgd_ef_step(grad_h, mem, q, eta, r)
+        mem, q = ref["mem"].astype(np.float32), ref["Q"].astype(np.float32)
+    return True
+
+
+def draw_well_conditioned(n, m, r, q_h, seed, scale, steps, bf16=False):
+    """The first of the seeded draws seed, seed + 100000, ... with well-conditioned P."""
+    for a in range(50):
+        g = gen.gaussian_mat(n, m, seed + 100_000 * a, scale)
+        if bf16:
+            g = gen.f32_to_bf16_bits(g).reshape(n, m)
+        if well_conditioned(g, q_h, r, steps):
+            return g
+    raise AssertionError(f"no well-conditioned draw for {n}x{m} r={r}")
+
+
 def test_more_matrices_than_one_launch_group():
-    """4100 matrices: more than one launch group (4096), fused and split shapes mixed."""
+    """4100 matrices: more than one launch group (4096), fused and split shapes
+    mixed, at the flat 1e-4 bar (draws with near-degenerate P replaced)."""
     print("case: 4100 small matrices", flush=True)
     shapes = [(3 + i % 5, 8 if i % 3 else 5) for i in range(4100)]
     ranks = [1 + i % 3 for i in range(4100)]
     ps = PsgdSet(shapes, ranks)
+    q0 = [t.cpu().numpy() for t in ps.q]
+    grads = [draw_well_conditioned(n, m, ranks[i], q0[i], 7000 + i, 1e-2, 1) for i, (n, m) in enumerate(shapes)]
+    check_step(ps, grads, 1.0, "4100 matrices")
+
+
+def test_conditioning_limit_near_degenerate_p():
+    """The float32 limit on nearly rank-deficient P, on its own.
+
+    The same 4100 tiny random matrices without the redraw: some P are nearly
+    singular (cond(P) up to about 1.2e4).  Orthonormalising such a P in any
+    float32 method moves its column space by about eps32 * cond(P), so each
+    matrix is held to max(1e-4, 10 * 2^-24 * cond(P)) -- the 1e-4 bar where
+    cond(P) <= 167, proportionally more above it.  Every parity set elsewhere
+    keeps cond(P) <= 100 and the flat 1e-4."""
+    print("case: conditioning limit, 4100 small matrices", flush=True)
+    shapes = [(3 + i % 5, 8 if i % 3 else 5) for i in range(4100)]
+    ranks = [1 + i % 3 for i in range(4100)]
+    ps = PsgdSet(shapes, ranks)
     grads = [gen.gaussian_mat(n, m, 7000 + i, 1e-2) for i, (n, m) in enumerate(shapes)]
-    # a few of these random small P are nearly singular (cond up to 1.2e4)
-    check_step(ps, grads, 1.0, "4100 matrices", cond_scaled=True)
+    check_step(ps, grads, 1.0, "4100 matrices, raw draws", cond_scaled=True)
 
 
 def test_many_matrices_multi_batch():
@@ -253,9 +305,8 @@ def test_random_shape_sets(seed, dtype):
         ranks.append(int(rs.integers(1, min(4, n, m) + 1)))
     print(f"case: random PowerSGD set seed={seed} {dtype} {shapes} ranks={ranks}", flush=True)
     ps = PsgdSet(shapes, ranks, q_cfg=7)
-    grads = []
-    for l, (n, m) in enumerate(shapes):
-        g = gen.gaussian_mat(n, m, 300 + 13 * seed + l, 10.0 ** rs.uniform(-4, -2))
-        grads.append(gen.f32_to_bf16_bits(g).reshape(n, m) if dtype == "bf16" else g)
+    q0 = [t.cpu().numpy() for t in ps.q]
+    grads = [draw_well_conditioned(n, m, ranks[l], q0[l], 300 + 13 * seed + l, 10.0 ** rs.uniform(-4, -2), 2,
+                                   bf16=dtype == "bf16") for l, (n, m) in enumerate(shapes)]
     for step in range(2):
-        check_step(ps, grads, 1.0, f"random set {seed} step {step}", cond_scaled=True)
+        check_step(ps, grads, 1.0, f"random set {seed} step {step}")
