@@ -71,6 +71,7 @@ _sig("gc_powersgd_run", _i32, _vp, _sz, _f32, _vp, _vp)
 _sig("gc_powersgd_run_phases", _i32, _vp, _sz, _f32, _vp, _i32, _vp)
 _sig("gc_grad_norm_workspace_bytes", _sz, C.POINTER(gc_span), _i32)
 _sig("gc_grad_norm", _i32, C.POINTER(gc_span), _i32, _i32, _vp, _vp, _sz, _vp)
+_sig("gc_grad_norm_noalloc", _i32, C.POINTER(gc_span), _i32, _i32, _vp, _vp)
 _sig("gc_passthrough", _i32, C.POINTER(gc_vec), _i32, _i32, _f32, _vp)
 _sig("gc_accordion_select", _i32, C.POINTER(C.c_float), C.POINTER(C.c_float), _i32, _f32, _i32,
      C.POINTER(C.c_int))
@@ -83,7 +84,7 @@ EXPORTED = ["gc_status_str", "gc_last_error", "gc_topk_workspace_bytes", "gc_top
             "gc_topk_decode", "gc_randk_ef_encode", "gc_powersgd_workspace_bytes", "gc_powersgd_ef_step",
             "gc_powersgd_ef_step_deferred", "gc_powersgd_materialize",
             "gc_powersgd_plan_bytes", "gc_powersgd_plan", "gc_powersgd_run", "gc_powersgd_run_phases",
-            "gc_grad_norm_workspace_bytes", "gc_grad_norm", "gc_passthrough",
+            "gc_grad_norm_workspace_bytes", "gc_grad_norm", "gc_grad_norm_noalloc", "gc_passthrough",
             "gc_accordion_select",
             "gc_timing_enable", "gc_timing_read", "gc_kernel_names"]
 
@@ -415,6 +416,19 @@ def gc_grad_norm(layers, norms, ws, stream=None) -> None:
     _need(all(t.dtype == layers[0].dtype for t in layers), "every layer must have the first one's dtype")
     _check(lib.gc_grad_norm(_spans(layers), len(layers), _dtype_code(layers[0]), _ptr(norms), _ptr(ws), _nbytes(ws),
                             _stream(stream)), "gc_grad_norm")
+
+
+GC_NORM_SCRATCH_TILES = 65536
+
+
+def gc_grad_norm_noalloc(layers, norms, stream=None) -> None:
+    """gc_grad_norm with the library's fixed per-device scratch instead of a workspace."""
+    import torch
+    _dtype_is(norms, torch.float32, "norms")
+    _need(norms.numel() >= len(layers), "norms needs one entry per layer")
+    _need(all(t.dtype == layers[0].dtype for t in layers), "every layer must have the first one's dtype")
+    _check(lib.gc_grad_norm_noalloc(_spans(layers), len(layers), _dtype_code(layers[0]), _ptr(norms),
+                                    _stream(stream)), "gc_grad_norm_noalloc")
 
 
 def gc_accordion_select(norm_now, norm_prev, threshold: float, has_prev: bool):

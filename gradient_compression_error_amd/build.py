@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgc.so")
-SOURCES = ["common.hip", "topk.hip", "powersgd.hip", "norm.hip", "passthrough.hip"]
+SOURCES = ["common.hip", "topk.hip", "powersgd.hip", "norm.hip", "passthrough.hip", "noalloc.hip"]
 ARCH = os.environ.get("GC_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -42,7 +42,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     cmds = [[HIPCC, *CFLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
-    with ThreadPoolExecutor(max_workers=min(5, len(cmds))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(cmds))) as ex:
         outs = list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"
     outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]))

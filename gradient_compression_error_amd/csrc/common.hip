@@ -25,8 +25,9 @@ int check_launch(const char* what) {
 
 // ---------------------------------------------------------------- timing hooks
 
-// The hooks are the library's only process-wide state.  A launch with
-// timing off reads one atomic flag and takes no lock.
+// The hooks are the library's only process-wide state besides the scratch
+// addresses of the allocation-free entry point.  A launch with timing off
+// reads one atomic flag and takes no lock.
 namespace {
 std::atomic<bool> g_timing_on{false};
 std::mutex g_tmu;

@@ -32,9 +32,10 @@
  *     call (all reductions have a fixed order; no floating-point atomics).
  *   - Calls that share a workspace must not overlap in time (use one stream).
  *   - Process-wide state: the library keeps none in its compute calls, so
- *     calls on different streams with their own buffers are independent.  One
- *     exception, documented where declared: the measurement hooks
- *     (gc_timing_enable / gc_timing_read).
+ *     calls on different streams with their own buffers are independent.  Two
+ *     exceptions, both documented where declared: the measurement hooks
+ *     (gc_timing_enable / gc_timing_read) and the per-device scratch array of
+ *     the allocation-free entry point gc_grad_norm_noalloc.
  */
 #ifndef GC_H
 #define GC_H
@@ -335,6 +336,28 @@ size_t gc_grad_norm_workspace_bytes(const gc_span* layers, int nlayers);
 int gc_grad_norm(const gc_span* layers, int nlayers, int grad_dtype, float* norms,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* Tiles (16384 entries each) of the per-device scratch of gc_grad_norm_noalloc. */
+#define GC_NORM_SCRATCH_TILES 65536
+
+/* gc_grad_norm without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * allocation).  The float64 tile partials go to a fixed scratch array that
+ * the library holds on each device (512 KiB, GC_NORM_SCRATCH_TILES tiles)
+ * until the process ends.  The call allocates nothing.
+ *   - The calling thread's current device must be the device of `stream`
+ *     and of the buffers; the first call on a device looks up that device's
+ *     scratch address once.
+ *   - Limit: the sum over layers of ceil(len / 16384) must be at most
+ *     GC_NORM_SCRATCH_TILES (2^30 entries in all when every len is a
+ *     multiple of 16384); larger calls fail with GC_ERR_ARG.
+ *   - Every call on a device shares that device's scratch: calls that overlap
+ *     in time on one device (different streams, other threads) race and give
+ *     wrong norms.  Calls on one stream are ordered and safe.  Nothing in the
+ *     scratch needs clearing: every partial a call reads it writes first.
+ * Results are bit for bit those of gc_grad_norm (same kernels, same order).
+ * Errors: those of gc_grad_norm (without GC_ERR_WORKSPACE), GC_ERR_ARG above
+ * the limit, GC_ERR_HIP when the scratch address cannot be looked up. */
+int gc_grad_norm_noalloc(const gc_span* layers, int nlayers, int grad_dtype, float* norms, void* stream);
 
 /* Host-only level choice for one check (Accordion, method section), per layer l:
  *   has_prev == 0            -> GC_LEVEL_LOW

@@ -252,6 +252,26 @@ def test_norm_validation(gcl):
 
 
 @no_gpu
+def test_norm_noalloc_validation(gcl):
+    """The allocation-free norm: the argument checks of gc_grad_norm, and a
+    refusal above its fixed scratch (GC_NORM_SCRATCH_TILES tiles of 16384),
+    all before the scratch address is looked up (no HIP call)."""
+    L = gcl.lib
+    S = gcl.gc_span
+    spans = (S * 2)(S(0x100000, 5), S(0x200000, 9000))
+    assert L.gc_grad_norm_noalloc(spans, 0, 0, 0x300000, None) == gcl.GC_ERR_ARG
+    assert L.gc_grad_norm_noalloc(spans, 2, 5, 0x300000, None) == gcl.GC_ERR_DTYPE
+    assert L.gc_grad_norm_noalloc(spans, 2, 0, None, None) == gcl.GC_ERR_ARG
+    assert L.gc_grad_norm_noalloc((S * 1)(S(0x100004, 5)), 1, 0, 0x300000, None) == gcl.GC_ERR_ARG
+    tiles = gcl.GC_NORM_SCRATCH_TILES
+    over = (S * 2)(S(0x100000, 16384 * (tiles - 1)), S(0x200000, 16385))     # tiles + 1 tiles
+    assert L.gc_grad_norm_noalloc(over, 2, 0, 0x300000, None) == gcl.GC_ERR_ARG
+    assert "GC_NORM_SCRATCH_TILES" in gcl.gc_last_error()
+    many = (S * (tiles + 1))(*[S(0x100000 + 16 * i, 1) for i in range(tiles + 1)])
+    assert L.gc_grad_norm_noalloc(many, tiles + 1, 0, 0x300000, None) == gcl.GC_ERR_ARG
+
+
+@no_gpu
 def test_passthrough_validation(gcl):
     L = gcl.lib
     V = gcl.gc_vec
