@@ -560,13 +560,15 @@ class C3Acc(Workload):
         gc.gc_topk_decode(self.idx[:self.k], self.val[:self.k], self.out)
 
 
-def refill_q(part, layer, t, old_rank, new_rank, cfg):
+def refill_q(part, layer, t, old_rank, new_rank, cfg, fresh=None):
     """Rank growth on an Accordion switch: Q's columns past the old rank get
-    fresh seeded N(0,1) values (the first old_rank columns stay as written)."""
+    fresh seeded N(0,1) values (the first old_rank columns stay as written).
+    fresh: the (4, m) draw of this step and layer, already on the device."""
     if new_rank > old_rank:
-        n, m = part.shapes[layer]
-        fresh = gen.q_refill(cfg, layer, t, m, 4)[old_rank:new_rank]
-        part.q[layer][old_rank:new_rank].copy_(part.torch.from_numpy(fresh))
+        if fresh is None:
+            n, m = part.shapes[layer]
+            fresh = part.torch.from_numpy(gen.q_refill(cfg, layer, t, m, 4))
+        part.q[layer][old_rank:new_rank].copy_(fresh[old_rank:new_rank])
 
 
 class C4(Workload):
@@ -621,6 +623,13 @@ class C4(Workload):
         self.ps = PowersgdPart(torch, gc, self.shapes, [4] * len(self.shapes), self.sets, self.mem_views, self.dev,
                                gen.CFG_C4)
         self.nws = torch.empty(gc.gc_grad_norm_workspace_bytes(self.sets[0]), dtype=torch.uint8, device=self.dev)
+        # Q columns a rank growth may need at each check step of the run, drawn now
+        self.refills = {}
+        for i in range(ncalls_total):
+            tau = self.t0 + i
+            if tau % gen.C4_CHECK_EVERY == 0:
+                for l, (n, m) in enumerate(self.shapes):
+                    self.refills[(tau, l)] = torch.from_numpy(gen.q_refill(gen.CFG_C4, l, tau, m, 4)).to(self.dev)
         # the check before the window: its norms seed the history
         last = (self.t0 - 1) // gen.C4_CHECK_EVERY * gen.C4_CHECK_EVERY
         seed_views = _flat(torch, self.sizes, torch.float32, self.dev, 64)[1]
@@ -670,7 +679,7 @@ class C4(Workload):
                                                          gen.C4_THRESHOLD, True)
             new = [gen.C4_RANK_LOW_COMPRESSION if v == gc.GC_LEVEL_LOW else gen.C4_RANK_HIGH_COMPRESSION for v in lv]
             for l, (old_r, new_r) in enumerate(zip(self.ps.ranks, new)):
-                refill_q(self.ps, l, tau, old_r, new_r, gen.CFG_C4)
+                refill_q(self.ps, l, tau, old_r, new_r, gen.CFG_C4, self.refills[(tau, l)])
             self.ps.set_ranks(new)
         self.ranks_log.append(list(self.ps.ranks))
         self.ps.step(i)
