@@ -45,6 +45,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # error-feedback memory form (PowerSGD and top-k): deferred unless --explicit
 PSGD_DEFERRED = True
 ORDER = "after"    # c5: where the embedding's top-k runs relative to the PowerSGD step (--order)
+FUSED_MAX_ROW = 8192   # longest row (a multiple of 4) the one-pass PowerSGD kernel takes
 
 
 def parse():
@@ -202,8 +203,8 @@ def psgd_bytes(shapes, ranks, sg):
 
 def fused_split_elems(shapes):
     """Entries of the matrices the one-pass kernel (psgd_pq) takes: rows of a
-    multiple of 4 and at most 4096 entries; the others take psgd_p + psgd_q."""
-    fused = sum(n * m for n, m in shapes if m % 4 == 0 and m <= 4096)
+    multiple of 4 and at most 8192 entries; the others take psgd_p + psgd_q."""
+    fused = sum(n * m for n, m in shapes if m % 4 == 0 and m <= FUSED_MAX_ROW)
     return fused, sum(n * m for n, m in shapes) - fused
 
 
@@ -233,7 +234,7 @@ def psgd_kernel_bytes(shapes, ranks, sg, deferred=None):
     kb = {"psgd_decode": sum(4 * n * m + 4 * r * (n + m) for (n, m), r in zip(shapes, ranks))}
     qin = {True: 0, False: 0}
     for (n, m), r in zip(shapes, ranks):
-        qin[m % 4 == 0 and m <= 4096] += 4 * r * m
+        qin[m % 4 == 0 and m <= FUSED_MAX_ROW] += 4 * r * m
     if fused:
         kb["psgd_pq"] = (sg + 8) * fused + qin[True]
     if split:

@@ -12,13 +12,15 @@
 // the orthonormalisation:
 //
 //   psgd_pq      one pass over M: a workgroup spanning a row (thread t owns
-//                columns 4t..4t+3) takes rows in groups, finishes each row's
+//                columns 4t..4t+3, and with two chunks per thread also
+//                4(t+NT)..) takes rows in groups, finishes each row's
 //                P = M Q_in with a DPP reduce-scatter plus one LDS exchange,
 //                and adds M[i,:]^T P[i,:] into per-thread M^T P accumulators;
 //                one M^T P and one Gram (float64) partial per workgroup and
-//                matrix.  Three classes by row length (<= 1024, 2048, 4096)
+//                matrix.  Five classes by row length (<= 1024, 2048, 4096,
+//                6144, 8192, m a multiple of 4)
 //   psgd_p/psgd_q the same two products as separate passes, for the other
-//                shapes (m not a multiple of 4, or m > 4096)
+//                shapes (m not a multiple of 4, or m > 8192)
 //   psgd_qreduce sums the partials in a fixed order, builds T from the summed
 //                Gram matrix, writes Q' = (M^T P) T into q (warm start)
 //   psgd_out     P^ = P T per row, out = P^ Q'^T, mem = M - out, P^ into p
@@ -109,9 +111,9 @@ struct PsMat {
 static_assert(sizeof(PsMat) % 8 == 0, "table entries are copied as words");
 static_assert(sizeof(PsMat) == 144, "table entry size stated in gc.h");
 
-// Fused-pass classes by row length: m <= 1024, m <= 2048, m <= 4096 (m % 4 == 0),
-// each with its own workgroup width; the rest take the split path.
-constexpr int PQ_CLASSES = 3;
+// Fused-pass classes by row length (m % 4 == 0): m <= 1024, 2048, 4096, 6144,
+// 8192, each with its own workgroup shape; the rest take the split path.
+constexpr int PQ_CLASSES = 5;
 constexpr int SPLIT_CLASS = PQ_CLASSES;
 
 // Launch parameters of one launch group; the matrices (sorted by class) are
@@ -529,62 +531,87 @@ __device__ __forceinline__ int rev4(int x) {
 }
 
 // Rows [r0, r1) of one matrix, RG rows at a time, by a workgroup of NT
-// threads that spans a row: thread t owns float4 chunk t (columns 4t..4t+3),
-// so Q_in and the M^T P accumulators of its columns stay in registers.
+// threads that spans a row: thread t owns the VPT float4 chunks t, t + NT, ...
+// (columns 4(t + c NT) .. +3), so Q_in and the M^T P accumulators of its
+// columns stay in registers.
 //   1. the RG rows' raw data (loaded one group ahead) become M;
-//   2. each thread forms its share of the RG x 4 dot products M[i,:] Q_in;
-//   3. a DPP reduce-scatter over each 16-lane row leaves V/16 of the V = 4 RG
-//      sums per lane; the 4 NT/64 row partials go to LDS (double-buffered,
-//      one barrier per group);
+//   2. each thread forms its share of the RG x 4 dot products M[i,:] Q_in
+//      (its chunks in order);
+//   3. a DPP reduce-scatter over each 16-lane row leaves the V = 4 RG sums
+//      spread over the row's lanes (lane li holds entry rev(li); with V < 16
+//      the lanes past V hold copies and the last steps are plain adds); the
+//      NT/16 row partials go to LDS (double-buffered, one barrier per group);
 //   4. every wave sums the partials of each value in a fixed order (its lanes
-//      split the partials, then two lane-exchange adds) and reads the V
-//      finished P entries into scalars;
+//      split the partials, then lane-exchange adds) and reads the V finished
+//      P entries into scalars;
 //   5. M^T P accumulators += M[i, cols] P[i, :]; wave 0 stores the P rows and
 //      accumulates the Gram matrix (float64).
 // The accumulators and Gram entries of the workgroup are partial `part`.
-template <bool BF16, int NT, int RG, bool DEF>
+template <bool BF16, int NT, int RG, int VPT, bool DEF>
 __device__ __forceinline__ void pq_rows(const PsMat& M, float eta, int r0, int r1, int part,
                                         float (*s_part)[NT / 16][4 * RG], int& par) {
     constexpr int V = 4 * RG;          // P entries per row group
     constexpr int NP = NT / 16;        // partials per entry (16-lane rows of the workgroup)
     constexpr int L = 64 / V;          // lanes sharing the sum of one entry
-    static_assert(V == 16 || V == 32, "row group of 4 or 8 rows");
+    constexpr int PER = V > 16 ? V / 16 : 1;   // entries per lane after the reduce-scatter
+    static_assert(V == 4 || V == 8 || V == 16 || V == 32, "row groups of 1, 2, 4 or 8 rows");
+    static_assert(NP % L == 0, "partials split evenly over the lanes of an entry");
     const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int m = M.m, c4 = m / 4, nr = r1 - r0;
-    const bool act = t < c4;
+    bool act[VPT];
+#pragma unroll
+    for (int c = 0; c < VPT; ++c) act[c] = t + c * NT < c4;
 
-    float q[4][4], qt[4][4], qr[4][4];
+    // Q of the thread's columns: Q_in for P = M Q_in, and in the deferred form
+    // also Q_prev for the residual rebuild.  Columns past max(rank, prev rank)
+    // are zero.  On a rank change the two differ only in columns that meet a
+    // zero: past the previous rank the stored P^_prev row is zero (the
+    // residual sum gains exact +0 terms), and P's columns past the rank never
+    // reach T, Q' or P^ (T is zero there) -- so one copy gives the bits of
+    // separately masked ones.
+    float q[VPT][4][4], qt[VPT][4][4];
     const int qn = DEF ? max(M.rank, M.prank) : M.rank;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (act && j < qn) v = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m)[t];
-        const bool in = j < M.rank, ip = j < M.prank;
-        q[0][j] = in ? v.x : 0.f; q[1][j] = in ? v.y : 0.f; q[2][j] = in ? v.z : 0.f; q[3][j] = in ? v.w : 0.f;
-        qr[0][j] = ip ? v.x : 0.f; qr[1][j] = ip ? v.y : 0.f; qr[2][j] = ip ? v.z : 0.f; qr[3][j] = ip ? v.w : 0.f;
+    for (int c = 0; c < VPT; ++c) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (act[c] && j < qn) v = reinterpret_cast<const float4*>(M.q + static_cast<long long>(j) * m)[t + c * NT];
+            q[c][0][j] = v.x; q[c][1][j] = v.y; q[c][2][j] = v.z; q[c][3][j] = v.w;
+        }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qt[c][cc][j] = 0.0f;
     }
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) qt[cc][j] = 0.0f;
 
     const long long e0 = static_cast<long long>(r0) * m, ne = static_cast<long long>(nr) * m;
     const __amdgpu_buffer_rsrc_t rm = rows_rsrc(M.mem, e0, 4, ne);
     const __amdgpu_buffer_rsrc_t rg = rows_rsrc(M.grad, e0, BF16 ? 2 : 4, ne);
-    const unsigned colm = act ? static_cast<unsigned>(t) * 16u : OOB_OFFSET;
-    const unsigned colg = act ? static_cast<unsigned>(t) * (BF16 ? 8u : 16u) : OOB_OFFSET;
+    unsigned colm[VPT], colg[VPT];
+#pragma unroll
+    for (int c = 0; c < VPT; ++c) {
+        colm[c] = act[c] ? static_cast<unsigned>(t + c * NT) * 16u : OOB_OFFSET;
+        colg[c] = act[c] ? static_cast<unsigned>(t + c * NT) * (BF16 ? 8u : 16u) : OOB_OFFSET;
+    }
     const unsigned rowm = static_cast<unsigned>(m) * 4u, rowg = static_cast<unsigned>(m) * (BF16 ? 2u : 4u);
 
-    RawChunk<BF16> raw[RG];
+    RawChunk<BF16> raw[RG][VPT];
     auto load_group = [&](int k) {
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
             const unsigned kr = static_cast<unsigned>(k + r);
-            raw[r].m = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rm, colm + kr * rowm, 0, 0));
-            if constexpr (BF16)
-                raw[r].g = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rg, colg + kr * rowg, 0, 0));
-            else
-                raw[r].g = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rg, colg + kr * rowg, 0, 0));
+#pragma unroll
+            for (int c = 0; c < VPT; ++c) {
+                raw[r][c].m = __builtin_bit_cast(float4,
+                                                 __builtin_amdgcn_raw_buffer_load_b128(rm, colm[c] + kr * rowm, 0, 0));
+                if constexpr (BF16)
+                    raw[r][c].g = __builtin_bit_cast(uint2,
+                                                     __builtin_amdgcn_raw_buffer_load_b64(rg, colg[c] + kr * rowg, 0, 0));
+                else
+                    raw[r][c].g = __builtin_bit_cast(float4,
+                                                     __builtin_amdgcn_raw_buffer_load_b128(rg, colg[c] + kr * rowg, 0, 0));
+            }
         }
     };
 
@@ -594,50 +621,85 @@ __device__ __forceinline__ void pq_rows(const PsMat& M, float eta, int r0, int r
     double g = 0.0;
     load_group(0);
     for (int k = 0; k < nr; k += RG) {
-        float v[RG][4];
+        float v[RG][VPT][4];
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
-            float4 x;
+            // deferred memory: M replaces M_prev in mem; rows past r1 and idle
+            // lanes store nothing.  Rows past r1 read as zero and take a zero
+            // P^ row, so their M stays zero (no P, Gram or M^T P terms)
+            float ph[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (DEF) {
-                // M replaces M_prev in mem; rows past r1 and idle lanes store
-                // nothing.  Rows past r1 read as zero and take a zero P^ row,
-                // so their M stays zero (no P, Gram or M^T P terms)
-                float ph[4] = {0.f, 0.f, 0.f, 0.f};
                 if (k + r < nr) prev_phat_row(M, r0 + k + r, ph);
-                x = raw_to_M_def<BF16>(raw[r], eta, ph, qr);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rm,
-                                                       colm + static_cast<unsigned>(k + r) * rowm, 0, 0);
-            } else {
-                x = raw_to_M<BF16>(raw[r], eta);
             }
-            v[r][0] = x.x; v[r][1] = x.y; v[r][2] = x.z; v[r][3] = x.w;
+#pragma unroll
+            for (int c = 0; c < VPT; ++c) {
+                float4 x;
+                if constexpr (DEF) {
+                    x = raw_to_M_def<BF16>(raw[r][c], eta, ph, q[c]);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rm,
+                                                           colm[c] + static_cast<unsigned>(k + r) * rowm, 0, 0);
+                } else {
+                    x = raw_to_M<BF16>(raw[r][c], eta);
+                }
+                v[r][c][0] = x.x; v[r][c][1] = x.y; v[r][c][2] = x.z; v[r][c][3] = x.w;
+            }
         }
         load_group(k + RG);
-        float x32[V];
+        float xs[V];
 #pragma unroll
         for (int r = 0; r < RG; ++r)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float a = v[r][0] * q[0][j];
-                a = fmaf(v[r][1], q[1][j], a);
-                a = fmaf(v[r][2], q[2][j], a);
-                x32[4 * r + j] = fmaf(v[r][3], q[3][j], a);
-            }
-        float x16[V / 2], x8[V / 4], x4[V / 8], x2[V / 16];
-        scatter_step<DPP_XOR1, 1>(x32, x16, lane);
-        scatter_step<DPP_XOR2, 2>(x16, x8, lane);
-        scatter_step<DPP_ROR4, 4>(x8, x4, lane);
-        scatter_step<DPP_ROR8, 8>(x4, x2, lane);
-        // lane li of a 16-lane row now holds entries (V/16) rev4(li) + i
-        float* dst = &s_part[par][w * 4 + lr][(V / 16) * rev4(li)];
+                float a = v[r][0][0] * q[0][0][j];
+                a = fmaf(v[r][0][1], q[0][1][j], a);
+                a = fmaf(v[r][0][2], q[0][2][j], a);
+                a = fmaf(v[r][0][3], q[0][3][j], a);
 #pragma unroll
-        for (int i = 0; i < V / 16; ++i) dst[i] = x2[i];
+                for (int c = 1; c < VPT; ++c)
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) a = fmaf(v[r][c][cc], q[c][cc][j], a);
+                xs[4 * r + j] = a;
+            }
+        float red[PER];
+        if constexpr (V == 32) {
+            float x16[16], x8[8], x4[4];
+            scatter_step<DPP_XOR1, 1>(xs, x16, lane);
+            scatter_step<DPP_XOR2, 2>(x16, x8, lane);
+            scatter_step<DPP_ROR4, 4>(x8, x4, lane);
+            scatter_step<DPP_ROR8, 8>(x4, red, lane);
+        } else if constexpr (V == 16) {
+            float x8[8], x4[4], x2[2];
+            scatter_step<DPP_XOR1, 1>(xs, x8, lane);
+            scatter_step<DPP_XOR2, 2>(x8, x4, lane);
+            scatter_step<DPP_ROR4, 4>(x4, x2, lane);
+            scatter_step<DPP_ROR8, 8>(x2, red, lane);
+        } else if constexpr (V == 8) {
+            float x4[4], x2[2], x1[1];
+            scatter_step<DPP_XOR1, 1>(xs, x4, lane);
+            scatter_step<DPP_XOR2, 2>(x4, x2, lane);
+            scatter_step<DPP_ROR4, 4>(x2, x1, lane);
+            red[0] = x1[0] + dpp_f32<DPP_ROR8>(x1[0]);
+        } else {
+            float x2[2], x1[1];
+            scatter_step<DPP_XOR1, 1>(xs, x2, lane);
+            scatter_step<DPP_XOR2, 2>(x2, x1, lane);
+            const float y = x1[0] + dpp_f32<DPP_ROR4>(x1[0]);
+            red[0] = y + dpp_f32<DPP_ROR8>(y);
+        }
+        // lane li of a 16-lane row holds entries PER * rev(li) + i (rev over
+        // log2(min(V, 16)) bits); with V < 16 lanes li >= V hold copies
+        if (V >= 16 || li < V) {
+            const int e = V >= 16 ? PER * rev4(li) : V == 8 ? rev4(li) >> 1 : rev4(li) >> 2;
+            float* dst = &s_part[par][w * 4 + lr][e];
+#pragma unroll
+            for (int i = 0; i < PER; ++i) dst[i] = red[i];
+        }
         __syncthreads();
         float pv = 0.0f;
 #pragma unroll
         for (int u = 0; u < NP / L; ++u) pv += s_part[par][lg * (NP / L) + u][vi];
-        if constexpr (L == 4) pv += __shfl_xor(pv, 16, WAVE);
-        pv += __shfl_xor(pv, 32, WAVE);
+#pragma unroll
+        for (int sh = V; sh < 64; sh <<= 1) pv += __shfl_xor(pv, sh, WAVE);
         par ^= 1;
         float p[RG][4];
 #pragma unroll
@@ -647,9 +709,11 @@ __device__ __forceinline__ void pq_rows(const PsMat& M, float eta, int r0, int r
 #pragma unroll
         for (int r = 0; r < RG; ++r)
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc)
+            for (int c = 0; c < VPT; ++c)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) qt[cc][j] = fmaf(v[r][cc], p[r][j], qt[cc][j]);
+                for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) qt[c][cc][j] = fmaf(v[r][c][cc], p[r][j], qt[c][cc][j]);
         if (w == 0) {
             // rows past r1 read as zero: their P entries and Gram terms are zero
             if (lane < V && k + vi / 4 < nr) M.praw[static_cast<long long>(r0 + k) * 4 + vi] = pv;
@@ -667,26 +731,36 @@ __device__ __forceinline__ void pq_rows(const PsMat& M, float eta, int r0, int r
             }
         }
     }
-    if (act) {
-        float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(part) * m + 4 * t;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) dst[cc] = make_float4(qt[cc][0], qt[cc][1], qt[cc][2], qt[cc][3]);
+    for (int c = 0; c < VPT; ++c) {
+        if (act[c]) {
+            float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(part) * m + 4 * (t + c * NT);
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+                dst[cc] = make_float4(qt[c][cc][0], qt[c][cc][1], qt[c][cc][2], qt[c][cc][3]);
+        }
     }
     if (w == 0 && lane < 16) M.gpart[static_cast<long long>(part) * 16 + lane] = g;
 }
 
-// Waves per SIMD the fused pass is compiled for (bounds its registers).
-template <int NT>
-constexpr int pq_min_waves() { return NT == 256 ? 3 : NT == 512 ? 4 : 4; }
+// Workgroup shape of each fused class: threads, rows per group, float4 chunks
+// per thread, waves per SIMD the kernel is compiled for (bounds its registers).
+template <int CLS> struct PqShape;
+template <> struct PqShape<0> { static constexpr int NT = 256, RG = 8, VPT = 1, WAVES = 3; };
+template <> struct PqShape<1> { static constexpr int NT = 512, RG = 4, VPT = 1, WAVES = 4; };
+template <> struct PqShape<2> { static constexpr int NT = 1024, RG = 4, VPT = 1, WAVES = 4; };
+template <> struct PqShape<3> { static constexpr int NT = 768, RG = 2, VPT = 2, WAVES = 3; };
+template <> struct PqShape<4> { static constexpr int NT = 1024, RG = 1, VPT = 2, WAVES = 4; };
 
-// One pass over the matrices of fused class CLS (m % 4 == 0, m <= 4 NT):
-// workgroup b takes its balanced share of their rows, matrix by matrix.
-template <bool BF16, int NT, int RG, bool DEF>
-__global__ __launch_bounds__(NT, pq_min_waves<NT>()) void psgd_pq(const PsBatch B, int cls) {
+// One pass over the matrices of fused class CLS: workgroup b takes its
+// balanced share of their rows, matrix by matrix.
+template <bool BF16, int CLS, bool DEF>
+__global__ __launch_bounds__(PqShape<CLS>::NT, PqShape<CLS>::WAVES) void psgd_pq(const PsBatch B) {
+    constexpr int NT = PqShape<CLS>::NT, RG = PqShape<CLS>::RG, VPT = PqShape<CLS>::VPT;
     __shared__ float s_part[2][NT / 16][4 * RG];
-    const int b = blockIdx.x, G = B.cgrid[cls];
-    const int i0 = B.cbeg[cls], i1 = B.cbeg[cls + 1];
-    const long long E = B.cent[cls], base = B.cbase[cls];
+    const int b = blockIdx.x, G = B.cgrid[CLS];
+    const int i0 = B.cbeg[CLS], i1 = B.cbeg[CLS + 1];
+    const long long E = B.cent[CLS], base = B.cbase[CLS];
     const long long s_lo = base + share_lo(E, G, b), s_hi = base + share_lo(E, G, b + 1);
     int par = 0;
     for (int i = mat_of_entry<true>(B, i0, i1, s_lo); i < i1; ++i) {
@@ -695,7 +769,7 @@ __global__ __launch_bounds__(NT, pq_min_waves<NT>()) void psgd_pq(const PsBatch 
         int r0, r1;
         rows_in_part(M, s_lo, s_hi, r0, r1);
         if (r0 >= r1) continue;
-        pq_rows<BF16, NT, RG, DEF>(M, B.eta, r0, r1, b - owner_of(M.poff - base, E, G), s_part, par);
+        pq_rows<BF16, NT, RG, VPT, DEF>(M, B.eta, r0, r1, b - owner_of(M.poff - base, E, G), s_part, par);
     }
 }
 
@@ -714,7 +788,7 @@ __global__ __launch_bounds__(NT, pq_min_waves<NT>()) void psgd_pq(const PsBatch 
 constexpr int TEAM_NT = 1024;
 constexpr int TEAM_RG = 4;
 constexpr int TEAM_CLASSES = 3;   // the classes a team kernel runs (row widths 256, 512, 1024 threads)
-static_assert(TEAM_CLASSES == PQ_CLASSES, "one team width per fused class");
+static_assert(TEAM_CLASSES <= PQ_CLASSES, "one team width per team class");
 constexpr long long TEAM_MAX_ENTRIES = 1LL << 26;   // launch groups up to this size use the team kernel
 
 __host__ __device__ constexpr int team_width(int cls) { return cls == 0 ? 256 : cls == 1 ? 512 : 1024; }
@@ -1246,7 +1320,8 @@ int nstrips_host(int m) {
 
 // Fused-pass class of a row length (SPLIT_CLASS: the split path)
 struct PqClass { int max_m, threads, blocks_per_cu; };
-constexpr PqClass PQ_CLASS[PQ_CLASSES] = {{1024, 256, 3}, {2048, 512, 2}, {4096, 1024, 1}};
+constexpr PqClass PQ_CLASS[PQ_CLASSES] = {{1024, 256, 3}, {2048, 512, 2}, {4096, 1024, 1}, {6144, 768, 1},
+                                          {8192, 1024, 1}};
 
 int shape_class(int m) {
     if (m % 4 != 0) return SPLIT_CLASS;
@@ -1315,8 +1390,9 @@ Plan make_plan(const gc_mat* mats, int nmats) {
         pb.count = j - i;
         pb.tbl_off = o;
         o += ws_round(static_cast<size_t>(pb.count) * sizeof(PsMat));
-        int ccount[PQ_CLASSES + 1] = {0, 0, 0, 0};
-        int cmax[PQ_CLASSES] = {1, 1, 1};
+        int ccount[PQ_CLASSES + 1] = {};
+        int cmax[PQ_CLASSES];
+        for (int c = 0; c < PQ_CLASSES; ++c) cmax[c] = 1;
         for (int a : idx) {
             const int c = shape_class(mats[a].m);
             ++ccount[c];
@@ -1438,24 +1514,29 @@ template <bool BF16, bool DEF>
 int launch_encode(const PsBatch& B, const PlanBatch& pb, hipStream_t s) {
     int rc;
     int fused = 0, team_grid = 0;
-    for (int c = 0; c < PQ_CLASSES; ++c) {
+    for (int c = 0; c < TEAM_CLASSES; ++c) {
         fused += B.cbeg[c + 1] > B.cbeg[c] ? 1 : 0;
         team_grid += team_wgs(B.cgrid[c], c);
     }
-    if (fused >= 2 && B.eall <= TEAM_MAX_ENTRIES) {
+    const bool teams = fused >= 2 && B.eall <= TEAM_MAX_ENTRIES;
+    if (teams) {
         // small group, several classes: one launch (the classes' passes side by side)
         TimedLaunch tl("psgd_pq", s);
         psgd_pq_teams<BF16, DEF><<<team_grid, TEAM_NT, 0, s>>>(B);
         if ((rc = check_launch("psgd_pq")) != GC_OK) return rc;
-    } else {
-        for (int c = 0; c < PQ_CLASSES; ++c) {
-            if (B.cbeg[c + 1] == B.cbeg[c]) continue;
-            TimedLaunch tl("psgd_pq", s);
-            if (c == 0) psgd_pq<BF16, 256, 8, DEF><<<B.cgrid[c], 256, 0, s>>>(B, c);
-            else if (c == 1) psgd_pq<BF16, 512, 4, DEF><<<B.cgrid[c], 512, 0, s>>>(B, c);
-            else psgd_pq<BF16, 1024, 4, DEF><<<B.cgrid[c], 1024, 0, s>>>(B, c);
-            if ((rc = check_launch("psgd_pq")) != GC_OK) return rc;
+    }
+    for (int c = teams ? TEAM_CLASSES : 0; c < PQ_CLASSES; ++c) {
+        if (B.cbeg[c + 1] == B.cbeg[c]) continue;
+        TimedLaunch tl("psgd_pq", s);
+        const unsigned g = static_cast<unsigned>(B.cgrid[c]);
+        switch (c) {
+            case 0: psgd_pq<BF16, 0, DEF><<<g, PqShape<0>::NT, 0, s>>>(B); break;
+            case 1: psgd_pq<BF16, 1, DEF><<<g, PqShape<1>::NT, 0, s>>>(B); break;
+            case 2: psgd_pq<BF16, 2, DEF><<<g, PqShape<2>::NT, 0, s>>>(B); break;
+            case 3: psgd_pq<BF16, 3, DEF><<<g, PqShape<3>::NT, 0, s>>>(B); break;
+            default: psgd_pq<BF16, 4, DEF><<<g, PqShape<4>::NT, 0, s>>>(B); break;
         }
+        if ((rc = check_launch("psgd_pq")) != GC_OK) return rc;
     }
     const int s0 = B.cbeg[SPLIT_CLASS];
     if (s0 < B.count) {

@@ -96,7 +96,11 @@ def check_step(ps, grads_h, eta, label="", cond_scaled=False):
 
 SHAPES = [(64, 27, 1), (64, 27, 4), (7, 2, 2), (2, 9, 2), (1, 1, 1), (100, 512, 4), (128, 576, 2),
           (33, 1030, 3), (1000, 3, 3), (4, 4608, 4), (513, 4608, 4), (17, 64, 4), (300, 2304, 1),
-          (37, 8192, 4), (5, 8196, 2), (3, 4100, 1), (600, 6144, 3)]
+          (37, 8192, 4), (5, 8196, 2), (3, 4100, 1), (600, 6144, 3),
+          # the wide fused classes (4096 < m <= 6144 and <= 8192) at and around their edges,
+          # and the first widths past them (split path)
+          (300, 4100, 4), (200, 5000, 3), (1, 6144, 1), (70, 6148, 4), (9, 8188, 2), (64, 8192, 1),
+          (45, 4102, 2), (12, 8200, 4)]
 
 
 @pytest.mark.parametrize("n,m,r", SHAPES)
@@ -108,7 +112,8 @@ def test_shapes_fp32(n, m, r):
         check_step(ps, [g], 0.8, f"step {t}")
 
 
-@pytest.mark.parametrize("n,m,r", [(64, 27, 2), (513, 4608, 4), (1024, 1024, 4), (33, 1030, 3)])
+@pytest.mark.parametrize("n,m,r", [(64, 27, 2), (513, 4608, 4), (1024, 1024, 4), (33, 1030, 3), (129, 6148, 4),
+                                   (40, 8192, 3)])
 def test_shapes_bf16(n, m, r):
     print(f"case: psgd {n}x{m} r={r} bf16", flush=True)
     ps = PsgdSet([(n, m)], [r])
@@ -291,14 +296,14 @@ def test_max_size_one_matrix():
 @pytest.mark.parametrize("seed,dtype", [(1, "f32"), (2, "bf16"), (3, "f32")])
 def test_random_shape_sets(seed, dtype):
     """Seeded random sets of 12 matrices mixing every row-length class and the
-    split path (m from 1 to 5000, some m % 4 != 0), random ranks: the plan's
+    split path (m from 1 to 8299, some m % 4 != 0), random ranks: the plan's
     class sort, balanced shares and partial counts on shapes no workload has."""
     rs = np.random.default_rng(100 + seed)
     shapes, ranks = [], []
     for _ in range(12):
         n = int(rs.integers(1, 600))
         m = int(rs.choice([rs.integers(1, 64), rs.integers(64, 1025), rs.integers(1025, 2049),
-                           rs.integers(2049, 4097), rs.integers(4097, 5001)]))
+                           rs.integers(2049, 4097), rs.integers(4097, 6145), rs.integers(6145, 8300)]))
         if rs.uniform() < 0.7:
             m = max(4, m - m % 4)
         shapes.append((n, m))

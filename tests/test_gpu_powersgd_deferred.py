@@ -117,6 +117,60 @@ def test_resnet18_set(rank):
              label=f"ResNet-18 r{rank}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_wide_classes(dtype):
+    """Each wide fused class alone (4096 < m <= 6144 on 768 threads with two
+    float4 per thread, 6144 < m <= 8192 on 1024 threads) at its edges, three
+    steps, deferred against explicit bit for bit."""
+    for (n, m), r in [((300, 4100), 4), ((96, 4608), 2), ((33, 6144), 3), ((130, 6148), 4), ((40, 8192), 1),
+                      ((7, 8188), 4)]:
+        print(f"case: deferred vs explicit wide {n}x{m} r={r} {dtype}", flush=True)
+
+        def grads(t, n=n, m=m):
+            g = gen.gaussian_mat(n, m, 1400 + t, 1e-2)
+            return [gen.f32_to_bf16_bits(g).reshape(n, m) if dtype == "bf16" else g]
+        run_pair([(n, m)], [r], grads, 3, eta=0.9, label=f"{n}x{m} {dtype}")
+
+
+def test_wide_rank_switches():
+    """Accordion-style switches on wide rows: 4 -> 2 (the previous Q columns 2,
+    3 still rebuild the residual), 2 -> 4 with refilled columns, 4 -> 1 -> 3."""
+    shapes = [(96, 4608), (40, 8192), (130, 6148), (64, 1024)]
+    sched = [[4, 4, 4, 4], [2, 2, 2, 2], [4, 4, 2, 4], [1, 2, 4, 1], [3, 1, 3, 4]]
+    A, B = Set(shapes, sched[0], gen.CFG_C4), Set(shapes, sched[0], gen.CFG_C4)
+    for t, ranks in enumerate(sched):
+        print(f"case: deferred wide rank switch step {t} ranks={ranks}", flush=True)
+        for S in (A, B):
+            for i, r in enumerate(ranks):
+                if r > S.ranks[i]:
+                    fresh = gen.q_refill(gen.CFG_C4, i, t, shapes[i][1], 4)
+                    S.q[i][S.ranks[i]:r] = to_dev(fresh[S.ranks[i]:r])
+            S.ranks = list(ranks)
+        g = [to_dev(gen.gaussian_mat(n, m, 1500 + 10 * t + i, 1e-2)) for i, (n, m) in enumerate(shapes)]
+        A.explicit(g, 1.0)
+        B.deferred(g, 1.0)
+        compare_bitwise(A, B, f"wide rank switch step {t}")
+
+
+def test_max_size_wide_rows():
+    """One 262143 x 8192 matrix (n*m = 2^31 - 8192, the largest of the widest
+    fused class), bf16 gradients drawn on the device, rank 4: two deferred
+    steps against two explicit ones, bit for bit on the device."""
+    n, m, r = 262143, 8192, 4
+    print(f"case: deferred vs explicit, wide max size {n}x{m} r={r} bf16", flush=True)
+    rng_t = torch.Generator(device=DEV)
+    rng_t.manual_seed(94)
+    A, B = Set([(n, m)], [r], gen.CFG_C5), Set([(n, m)], [r], gen.CFG_C5)
+    for t in range(2):
+        g = (torch.randn(n, m, generator=rng_t, dtype=torch.float32, device=DEV) * 1e-3).to(torch.bfloat16)
+        A.explicit([g], 1.0)
+        B.deferred([g], 1.0)
+        del g
+        compare_bitwise(A, B, f"wide max size step {t}")
+    del A, B
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("seed,dtype", [(4, "f32"), (5, "bf16")])
 def test_random_shape_sets(seed, dtype):
     rs = np.random.default_rng(200 + seed)
@@ -124,7 +178,7 @@ def test_random_shape_sets(seed, dtype):
     for _ in range(12):
         n = int(rs.integers(1, 500))
         m = int(rs.choice([rs.integers(1, 64), rs.integers(64, 1025), rs.integers(1025, 2049),
-                           rs.integers(2049, 4097), rs.integers(4097, 5001)]))
+                           rs.integers(2049, 4097), rs.integers(4097, 6145), rs.integers(6145, 8300)]))
         if rs.uniform() < 0.7:
             m = max(4, m - m % 4)
         shapes.append((n, m))
