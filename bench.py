@@ -46,6 +46,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 PSGD_DEFERRED = True
 ORDER = "after"    # c5: where the embedding's top-k runs relative to the PowerSGD step (--order)
 FUSED_MAX_ROW = 8192   # longest row (a multiple of 4) the one-pass PowerSGD kernel takes
+SMALL_MAX = 1024       # matrices with n, m <= SMALL_MAX of any width are done in one pass too
 
 
 def parse():
@@ -201,10 +202,15 @@ def psgd_bytes(shapes, ranks, sg):
     return sum((sg + 12) * n * m + 4 * r * (n + 2 * m) for (n, m), r in zip(shapes, ranks))
 
 
+def one_pass(n, m):
+    return (m % 4 == 0 and m <= FUSED_MAX_ROW) or (n <= SMALL_MAX and m <= SMALL_MAX)
+
+
 def fused_split_elems(shapes):
-    """Entries of the matrices the one-pass kernel (psgd_pq) takes: rows of a
-    multiple of 4 and at most 8192 entries; the others take psgd_p + psgd_q."""
-    fused = sum(n * m for n, m in shapes if m % 4 == 0 and m <= FUSED_MAX_ROW)
+    """Entries of the matrices whose first pass reads M once: rows of a
+    multiple of 4 and at most 8192 entries (psgd_pq), and small matrices
+    (n, m <= 1024, any m: one workgroup each); the others take psgd_p + psgd_q."""
+    fused = sum(n * m for n, m in shapes if one_pass(n, m))
     return fused, sum(n * m for n, m in shapes) - fused
 
 
@@ -234,7 +240,7 @@ def psgd_kernel_bytes(shapes, ranks, sg, deferred=None):
     kb = {"psgd_decode": sum(4 * n * m + 4 * r * (n + m) for (n, m), r in zip(shapes, ranks))}
     qin = {True: 0, False: 0}
     for (n, m), r in zip(shapes, ranks):
-        qin[m % 4 == 0 and m <= FUSED_MAX_ROW] += 4 * r * m
+        qin[one_pass(n, m)] += 4 * r * m
     if fused:
         kb["psgd_pq"] = (sg + 8) * fused + qin[True]
     if split:

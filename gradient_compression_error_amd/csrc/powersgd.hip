@@ -112,17 +112,22 @@ static_assert(sizeof(PsMat) % 8 == 0, "table entries are copied as words");
 static_assert(sizeof(PsMat) == 144, "table entry size stated in gc.h");
 
 // Fused-pass classes by row length (m % 4 == 0): m <= 1024, 2048, 4096, 6144,
-// 8192, each with its own workgroup shape; the rest take the split path.
+// 8192, each with its own workgroup shape.  Of the other shapes, the small
+// ones (n, m <= 1024) are done whole by one workgroup each; the rest take the
+// split path.
 constexpr int PQ_CLASSES = 5;
-constexpr int SPLIT_CLASS = PQ_CLASSES;
+constexpr int SMALL_CLASS = PQ_CLASSES;
+constexpr int SPLIT_CLASS = PQ_CLASSES + 1;
+constexpr int SMALL_MAX_N = 1024, SMALL_MAX_M = 1024;
 
 // Launch parameters of one launch group; the matrices (sorted by class) are
 // in a device table (in the workspace) copied there at the start of the step.
 struct PsBatch {
     const PsMat* tbl;
+    const int* rmap;               // psgd_qreduce workgroup -> matrix (after the table)
     int count;
     float eta;
-    int cbeg[PQ_CLASSES + 2];      // matrices [cbeg[c], cbeg[c+1]) are of class c
+    int cbeg[PQ_CLASSES + 3];      // matrices [cbeg[c], cbeg[c+1]) are of class c (small, split last)
     int cgrid[PQ_CLASSES];         // psgd_pq grid of each fused class
     long long cbase[PQ_CLASSES];   // first partition unit of each fused class
     long long cent[PQ_CLASSES];    // partition units of each fused class
@@ -170,13 +175,12 @@ __device__ __forceinline__ int mat_of_entry(const PsBatch& B, int i0, int i1, lo
     return lo;
 }
 
-enum BlockMap { MAP_P, MAP_Q, MAP_R };
+enum BlockMap { MAP_P, MAP_Q };
 
 template <BlockMap K>
 __device__ __forceinline__ int first_block(MatTable T, int i) {
     if constexpr (K == MAP_P) return T[i].begin_p;
-    else if constexpr (K == MAP_Q) return T[i].begin_q;
-    else return T[i].begin_r;
+    else return T[i].begin_q;
 }
 
 // Matrix of workgroup blk among matrices [i0, i1) (last i with first block <= blk).
@@ -773,6 +777,77 @@ __global__ __launch_bounds__(PqShape<CLS>::NT, PqShape<CLS>::WAVES) void psgd_pq
     }
 }
 
+// ------------------------------------------------------------------ small matrices
+
+// A whole small matrix (n, m <= 1024; any m) by one workgroup of NT threads:
+//   1. one wave per row at a time forms M (deferred: rebuilds the residual and
+//      stores M over mem) and the row's P = M Q_in, lanes striding over the
+//      columns, summed with wave_sum; P goes to LDS and praw;
+//   2. after a barrier, threads 0..15 sum the Gram matrix over the rows in
+//      order (float64) and every thread forms M^T P for its columns from the
+//      matrix (now in the cache) and P in LDS.
+// One M^T P and one Gram partial.
+template <bool BF16, int NT, bool DEF>
+__device__ void small_pq(const PsMat& M, float eta, float* s_p) {
+    constexpr int NW = NT / 64;
+    const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int n = M.n, m = M.m;
+    const int qn = DEF ? max(M.rank, M.prank) : M.rank;   // one copy of Q, as in pq_rows
+    for (int i = w; i < n; i += NW) {
+        float ph[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (DEF) prev_phat_row(M, i, ph);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int c = lane; c < m; c += 64) {
+            float qv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qv[j] = j < qn ? M.q[static_cast<long long>(j) * m + c] : 0.0f;
+            const long long e = static_cast<long long>(i) * m + c;
+            float mv;
+            if constexpr (DEF) {
+                mv = ef_acc(residual1(M.mem[e], ph, qv), eta, load_grad1<BF16>(M.grad, e));
+                M.mem[e] = mv;
+            } else {
+                mv = load_M1<BF16>(M, eta, e);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = fmaf(mv, qv[j], acc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = wave_sum(acc[j]);
+        if (lane < 4) {
+            const float v = lane == 0 ? acc[0] : lane == 1 ? acc[1] : lane == 2 ? acc[2] : acc[3];
+            s_p[i * 4 + lane] = v;
+            M.praw[static_cast<long long>(i) * 4 + lane] = v;
+        }
+    }
+    __syncthreads();
+    if (t < 16) {
+        const int a = t >> 2, b = t & 3;
+        double g = 0.0;
+        for (int i = 0; i < n; ++i) g = fma(static_cast<double>(s_p[i * 4 + a]), static_cast<double>(s_p[i * 4 + b]), g);
+        M.gpart[t] = g;
+    }
+    for (int c = t; c < m; c += NT) {
+        float qt[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < n; ++i) {
+            const long long e = static_cast<long long>(i) * m + c;
+            const float mv = DEF ? M.mem[e] : load_M1<BF16>(M, eta, e);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qt[j] = fmaf(mv, s_p[i * 4 + j], qt[j]);
+        }
+        reinterpret_cast<float4*>(M.qpart)[c] = make_float4(qt[0], qt[1], qt[2], qt[3]);
+    }
+}
+
+constexpr int SMALL_THREADS = 256;
+
+// The small class alone (when no team launch carries it): one workgroup per matrix.
+template <bool BF16, bool DEF>
+__global__ __launch_bounds__(SMALL_THREADS) void psgd_small(const PsBatch B) {
+    __shared__ float s_p[SMALL_MAX_N * 4];
+    small_pq<BF16, SMALL_THREADS, DEF>(mat_at(B, B.cbeg[SMALL_CLASS] + blockIdx.x), B.eta, s_p);
+}
+
 // ------------------------------------------------------------------ psgd_pq_teams
 
 // Small launch groups are launch-bound, so their fused classes run in ONE
@@ -991,10 +1066,12 @@ __device__ __forceinline__ void pq_teams(const PsBatch& B, int cls, int wg_in_cl
     }
 }
 
+// The workgroups after the classes' ones take one small matrix each.
 template <bool BF16, bool DEF>
 __global__ __launch_bounds__(TEAM_NT) void psgd_pq_teams(const PsBatch B) {
     __shared__ float s_part[2][TEAM_NT / 16][4 * TEAM_RG];
     __shared__ int s_cnt[TEAM_NT / 256];
+    __shared__ float s_p[SMALL_MAX_N * 4];
     int w = blockIdx.x, cls = 0;
     for (; cls < TEAM_CLASSES; ++cls) {
         const int n = team_wgs(B.cgrid[cls], cls);
@@ -1004,6 +1081,7 @@ __global__ __launch_bounds__(TEAM_NT) void psgd_pq_teams(const PsBatch B) {
     if (cls == 0) pq_teams<BF16, 256, DEF>(B, 0, w, s_part, s_cnt);
     else if (cls == 1) pq_teams<BF16, 512, DEF>(B, 1, w, s_part, s_cnt);
     else if (cls == 2) pq_teams<BF16, 1024, DEF>(B, 2, w, s_part, s_cnt);
+    else small_pq<BF16, TEAM_NT, DEF>(mat_at(B, B.cbeg[SMALL_CLASS] + w), B.eta, s_p);
 }
 
 // ------------------------------------------------------------------ psgd_qreduce
@@ -1053,7 +1131,10 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
     __shared__ double s_g[16][16];
     __shared__ double s_T[16];
     __shared__ double4 s_q[PS_THREADS];
-    const PsMat M = mat_at(B, mat_of_block<MAP_R>(B, 0, B.count, blockIdx.x));
+    // the matrix of this workgroup from the plan's map: one scalar load, where
+    // a search of the table would chain eight dependent ones
+    typedef const __attribute__((address_space(4))) int* ConstI;
+    const PsMat M = mat_at(B, ((ConstI)(B.rmap))[blockIdx.x]);
     const int lwg = blockIdx.x - M.begin_r;
     const int m = M.m, r = M.rank, t = threadIdx.x;
     const int S = M.qs, QC = PS_THREADS / S;
@@ -1318,15 +1399,17 @@ int nstrips_host(int m) {
     return (m + w - 1) / w;
 }
 
-// Fused-pass class of a row length (SPLIT_CLASS: the split path)
+// Class of an n x m matrix: a fused class by row length, the small class,
+// or the split path.
 struct PqClass { int max_m, threads, blocks_per_cu; };
 constexpr PqClass PQ_CLASS[PQ_CLASSES] = {{1024, 256, 3}, {2048, 512, 2}, {4096, 1024, 1}, {6144, 768, 1},
                                           {8192, 1024, 1}};
 
-int shape_class(int m) {
-    if (m % 4 != 0) return SPLIT_CLASS;
-    for (int c = 0; c < PQ_CLASSES; ++c)
-        if (m <= PQ_CLASS[c].max_m) return c;
+int shape_class(int n, int m) {
+    if (m % 4 == 0)
+        for (int c = 0; c < PQ_CLASSES; ++c)
+            if (m <= PQ_CLASS[c].max_m) return c;
+    if (n <= SMALL_MAX_N && m <= SMALL_MAX_M) return SMALL_CLASS;
     return SPLIT_CLASS;
 }
 
@@ -1345,7 +1428,7 @@ struct PlanMat {
 struct PlanBatch {
     int first, count;                  // into Plan::mats
     size_t tbl_off;                    // workspace offset of the device table
-    int cbeg[PQ_CLASSES + 2];
+    int cbeg[PQ_CLASSES + 3];
     int cgrid[PQ_CLASSES];
     long long cbase[PQ_CLASSES], cent[PQ_CLASSES];
     long long eall;
@@ -1383,18 +1466,17 @@ Plan make_plan(const gc_mat* mats, int nmats) {
         const int j = std::min(nmats, i + PS_MAXB);
         std::vector<int> idx;
         for (int k = i; k < j; ++k) idx.push_back(k);
-        std::stable_sort(idx.begin(), idx.end(),
-                         [&](int a, int b) { return shape_class(mats[a].m) < shape_class(mats[b].m); });
+        std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) {
+            return shape_class(mats[a].n, mats[a].m) < shape_class(mats[b].n, mats[b].m);
+        });
         PlanBatch pb{};
         pb.first = static_cast<int>(P.mats.size());
         pb.count = j - i;
-        pb.tbl_off = o;
-        o += ws_round(static_cast<size_t>(pb.count) * sizeof(PsMat));
-        int ccount[PQ_CLASSES + 1] = {};
+        int ccount[PQ_CLASSES + 2] = {};
         int cmax[PQ_CLASSES];
         for (int c = 0; c < PQ_CLASSES; ++c) cmax[c] = 1;
         for (int a : idx) {
-            const int c = shape_class(mats[a].m);
+            const int c = shape_class(mats[a].n, mats[a].m);
             ++ccount[c];
             if (c < PQ_CLASSES) {
                 pb.cent[c] += static_cast<long long>(mats[a].n) * (mats[a].m + PQ_ROW_COST);
@@ -1402,7 +1484,7 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             }
         }
         pb.cbeg[0] = 0;
-        for (int c = 0; c <= PQ_CLASSES; ++c) pb.cbeg[c + 1] = pb.cbeg[c] + ccount[c];
+        for (int c = 0; c <= SPLIT_CLASS; ++c) pb.cbeg[c + 1] = pb.cbeg[c] + ccount[c];
         long long base = 0;
         for (int c = 0; c < PQ_CLASSES; ++c) {
             pb.cbase[c] = base;
@@ -1426,8 +1508,10 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             pm.idx = a;
             pm.off = eall;
             const int n = mats[a].n, m = mats[a].m;
-            const int c = shape_class(m);
-            if (c < PQ_CLASSES) {
+            const int c = shape_class(n, m);
+            if (c == SMALL_CLASS) {
+                pm.nq = pm.ng = 1;     // one workgroup: one partial of each
+            } else if (c < PQ_CLASSES) {
                 pm.poff = pall;
                 pall += static_cast<long long>(n) * (m + PQ_ROW_COST);
                 const long long E = pb.cent[c], rel = pm.poff - pb.cbase[c];
@@ -1457,6 +1541,9 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             P.mats.push_back(pm);
         }
         pb.eall = eall;
+        // the device table, then the psgd_qreduce workgroup -> matrix map
+        pb.tbl_off = o;
+        o += ws_round(static_cast<size_t>(pb.count) * sizeof(PsMat) + static_cast<size_t>(pb.nr) * sizeof(int));
         const long long gmax = eall <= OUT_TWO_ROUNDS_MAX ? 2LL * OUT_GRID_MAX : OUT_GRID_MAX;
         pb.gout = static_cast<int>(std::min<long long>(gmax, std::max<long long>(1, eall / 1024)));
         P.batches.push_back(pb);
@@ -1499,11 +1586,22 @@ int validate_mat(const gc_mat& a, int i, int dtype, const std::string& fn, bool 
     return GC_OK;
 }
 
-// The table goes to the device in stream order.  From pageable memory the
-// runtime stages the bytes before returning, so `tbl` may go out of scope.
-int copy_table(const PsBatch& B, const std::vector<PsMat>& tbl, hipStream_t s) {
-    const hipError_t e = hipMemcpyAsync(const_cast<PsMat*>(B.tbl), tbl.data(), tbl.size() * sizeof(PsMat),
-                                        hipMemcpyHostToDevice, s);
+// Host image of a batch's device table: the matrix entries, then the
+// psgd_qreduce map (workgroup b -> the matrix whose Q columns it reduces).
+struct TableImage {
+    std::vector<PsMat> mats;
+    std::vector<int> rmap;
+};
+
+// The table and map go to the device in stream order, as one copy.  From
+// pageable memory the runtime stages the bytes before returning, so the
+// image may go out of scope.
+int copy_table(const PsBatch& B, const TableImage& img, hipStream_t s) {
+    const size_t tb = img.mats.size() * sizeof(PsMat), mb = img.rmap.size() * sizeof(int);
+    std::vector<char> buf(tb + mb);
+    std::memcpy(buf.data(), img.mats.data(), tb);
+    if (mb) std::memcpy(buf.data() + tb, img.rmap.data(), mb);
+    const hipError_t e = hipMemcpyAsync(const_cast<PsMat*>(B.tbl), buf.data(), buf.size(), hipMemcpyHostToDevice, s);
     if (e != hipSuccess)
         return fail(GC_ERR_HIP, std::string("PowerSGD matrix table copy: ") + hipGetErrorString(e));
     return GC_OK;
@@ -1518,11 +1616,18 @@ int launch_encode(const PsBatch& B, const PlanBatch& pb, hipStream_t s) {
         fused += B.cbeg[c + 1] > B.cbeg[c] ? 1 : 0;
         team_grid += team_wgs(B.cgrid[c], c);
     }
+    const int nsmall = B.cbeg[SPLIT_CLASS] - B.cbeg[SMALL_CLASS];
+    fused += nsmall > 0 ? 1 : 0;
     const bool teams = fused >= 2 && B.eall <= TEAM_MAX_ENTRIES;
     if (teams) {
-        // small group, several classes: one launch (the classes' passes side by side)
+        // small group, several classes: one launch (the classes' passes side by
+        // side, the small matrices after them)
         TimedLaunch tl("psgd_pq", s);
-        psgd_pq_teams<BF16, DEF><<<team_grid, TEAM_NT, 0, s>>>(B);
+        psgd_pq_teams<BF16, DEF><<<team_grid + nsmall, TEAM_NT, 0, s>>>(B);
+        if ((rc = check_launch("psgd_pq")) != GC_OK) return rc;
+    } else if (nsmall > 0) {
+        TimedLaunch tl("psgd_pq", s);
+        psgd_small<BF16, DEF><<<nsmall, SMALL_THREADS, 0, s>>>(B);
         if ((rc = check_launch("psgd_pq")) != GC_OK) return rc;
     }
     for (int c = teams ? TEAM_CLASSES : 0; c < PQ_CLASSES; ++c) {
@@ -1604,7 +1709,7 @@ int launch_batch(const PsBatch& B, const PlanBatch& pb, hipStream_t s, int phase
 }
 
 template <bool BF16, bool DEF>
-int run_batch(const PsBatch& B, const PlanBatch& pb, const std::vector<PsMat>& tbl, hipStream_t s) {
+int run_batch(const PsBatch& B, const PlanBatch& pb, const TableImage& tbl, hipStream_t s) {
     const int rc = copy_table(B, tbl, s);
     return rc != GC_OK ? rc : launch_batch<BF16, DEF>(B, pb, s);
 }
@@ -1615,7 +1720,7 @@ int launch_any(bool bf16, bool def, const PsBatch& B, const PlanBatch& pb, hipSt
 }
 
 // mem = M_prev - P^_prev Q_prev^T for the matrices with prank > 0.
-int run_materialize(const PsBatch& B, const std::vector<PsMat>& tbl, hipStream_t s) {
+int run_materialize(const PsBatch& B, const TableImage& tbl, hipStream_t s) {
     int rc;
     if ((rc = copy_table(B, tbl, s)) != GC_OK) return rc;
     TimedLaunch tl("psgd_materialize", s);
@@ -1663,9 +1768,10 @@ int powersgd_call(const char* fn, StepKind kind, const gc_mat* mats, const int32
     for (const PlanBatch& pb : P.batches) {
         PsBatch B{};
         B.tbl = reinterpret_cast<const PsMat*>(wp + pb.tbl_off);
+        B.rmap = reinterpret_cast<const int*>(wp + pb.tbl_off + static_cast<size_t>(pb.count) * sizeof(PsMat));
         B.count = pb.count;
         B.eta = eta;
-        for (int c = 0; c < PQ_CLASSES + 2; ++c) B.cbeg[c] = pb.cbeg[c];
+        for (int c = 0; c < PQ_CLASSES + 3; ++c) B.cbeg[c] = pb.cbeg[c];
         for (int c = 0; c < PQ_CLASSES; ++c) {
             B.cgrid[c] = pb.cgrid[c];
             B.cbase[c] = pb.cbase[c];
@@ -1673,12 +1779,16 @@ int powersgd_call(const char* fn, StepKind kind, const gc_mat* mats, const int32
         }
         B.eall = pb.eall;
         B.gout = pb.gout;
-        std::vector<PsMat> tbl(pb.count);
+        TableImage tbl;
+        tbl.mats.resize(pb.count);
+        tbl.rmap.resize(pb.nr);
         for (int k = 0; k < pb.count; ++k) {
             const PlanMat& pm = P.mats[pb.first + k];
             const gc_mat& a = mats[pm.idx];
+            const int rend = k + 1 < pb.count ? P.mats[pb.first + k + 1].begin_r : pb.nr;
+            for (int b = pm.begin_r; b < rend; ++b) tbl.rmap[b] = k;
             char* base = wp + pm.ws_off;
-            PsMat& M = tbl[k];
+            PsMat& M = tbl.mats[k];
             M.grad = a.grad;
             M.mem = a.mem;
             M.q = a.q;

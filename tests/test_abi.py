@@ -360,7 +360,8 @@ def test_bench_kernel_bytes_accounting():
     sys.path.insert(0, ROOT)
     import bench
     assert bench.psgd_bytes([(4, 8)], [2], 2) == 14 * 32 + 4 * 2 * (4 + 16) == 608
-    for shapes, sg in [(gen.BERT_MATS, 2), ([(4, 8), (1024, 4096), (3, 2048), (512, 4608), (2, 8192)], 4)]:
+    for shapes, sg in [(gen.BERT_MATS, 2), ([(4, 8), (1024, 4096), (3, 2048), (512, 4608), (2, 8192), (64, 27)], 4),
+                       (gen.RESNET18_MATS, 4), (gen.VGG19_MATS, 4)]:
         ranks = [min(4, n, m) for n, m in shapes]
         kb = bench.psgd_kernel_bytes(shapes, ranks, sg, deferred=True)
         assert set(kb) == {"psgd_pq", "psgd_decode"}
@@ -369,10 +370,10 @@ def test_bench_kernel_bytes_accounting():
         assert kx["psgd_out"] == bench.psgd_bytes(shapes, ranks, sg)
         fused, split = bench.fused_split_elems(shapes)
         assert kx["psgd_pq"] == (sg + 4) * fused and split == 0
-    # split-path shapes (m % 4 != 0, m > 8192): the second read of M in psgd_q is charged on top
-    shapes, ranks = [(64, 27), (512, 8196)], [2, 4]
+    # split-path shapes (m % 4 != 0 and not small, m > 8192): the second read of M in psgd_q is charged on top
+    shapes, ranks = [(1100, 27), (512, 8196)], [2, 4]
     kb = bench.psgd_kernel_bytes(shapes, ranks, 4, deferred=True)
-    nm = 64 * 27 + 512 * 8196
+    nm = 1100 * 27 + 512 * 8196
     assert kb["psgd_q"] == 4 * nm
     assert kb["psgd_p"] + kb["psgd_decode"] == bench.psgd_bytes(shapes, ranks, 4)
 

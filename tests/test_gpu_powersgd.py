@@ -100,7 +100,9 @@ SHAPES = [(64, 27, 1), (64, 27, 4), (7, 2, 2), (2, 9, 2), (1, 1, 1), (100, 512, 
           # the wide fused classes (4096 < m <= 6144 and <= 8192) at and around their edges,
           # and the first widths past them (split path)
           (300, 4100, 4), (200, 5000, 3), (1, 6144, 1), (70, 6148, 4), (9, 8188, 2), (64, 8192, 1),
-          (45, 4102, 2), (12, 8200, 4)]
+          (45, 4102, 2), (12, 8200, 4),
+          # the small class (n, m <= 1024, any m) at its limits, and just past them (split path)
+          (1024, 1023, 4), (2, 999, 2), (1025, 27, 2), (7, 1030, 3)]
 
 
 @pytest.mark.parametrize("n,m,r", SHAPES)

@@ -132,6 +132,31 @@ def test_wide_classes(dtype):
         run_pair([(n, m)], [r], grads, 3, eta=0.9, label=f"{n}x{m} {dtype}")
 
 
+def test_small_class():
+    """Matrices with n, m <= 1024 whose rows are not float4-wide (any m) are
+    done whole by one workgroup: alone (their own launch) and beside fused
+    classes (inside the team launch), with a rank switch, deferred against
+    explicit bit for bit."""
+    alone = [(1024, 1023), (1000, 3), (1, 1), (64, 27), (2, 999)]
+    mixed = alone + [(300, 1024), (64, 576), (33, 2048)]
+    for shapes in (alone, mixed):
+        sched = [[min(4, n, m) for n, m in shapes], [min(2, n, m) for n, m in shapes],
+                 [min(4, n, m) for n, m in shapes], [min(3, n, m) for n, m in shapes]]
+        A, B = Set(shapes, sched[0], gen.CFG_C4), Set(shapes, sched[0], gen.CFG_C4)
+        for t, ranks in enumerate(sched):
+            print(f"case: deferred small class {len(shapes)} matrices step {t} ranks={ranks}", flush=True)
+            for S in (A, B):
+                for i, r in enumerate(ranks):
+                    if r > S.ranks[i]:
+                        fresh = gen.q_refill(gen.CFG_C4, i, t, shapes[i][1], 4)
+                        S.q[i][S.ranks[i]:r] = to_dev(fresh[S.ranks[i]:r])
+                S.ranks = list(ranks)
+            g = [to_dev(gen.gaussian_mat(n, m, 1600 + 10 * t + i, 1e-2)) for i, (n, m) in enumerate(shapes)]
+            A.explicit(g, 1.0)
+            B.deferred(g, 1.0)
+            compare_bitwise(A, B, f"small class step {t}")
+
+
 def test_wide_rank_switches():
     """Accordion-style switches on wide rows: 4 -> 2 (the previous Q columns 2,
     3 still rebuild the residual), 2 -> 4 with refilled columns, 4 -> 1 -> 3."""
