@@ -125,6 +125,7 @@ constexpr int SMALL_MAX_N = 1024, SMALL_MAX_M = 1024;
 struct PsBatch {
     const PsMat* tbl;
     const int* rmap;               // psgd_qreduce workgroup -> matrix (after the table)
+    const int* dmap;               // psgd_decode: matrix of tile 64 g, for every g (after rmap)
     int count;
     float eta;
     int cbeg[PQ_CLASSES + 3];      // matrices [cbeg[c], cbeg[c+1]) are of class c (small, split last)
@@ -1371,14 +1372,12 @@ constexpr long long DEC_GRID_MAX = 1LL << 30;
 template <bool STREAM>
 __global__ __launch_bounds__(PS_THREADS) void psgd_decode(const PsBatch B, long long ntiles) {
     const MatTable T = mat_table(B);
+    typedef const __attribute__((address_space(4))) int* ConstI;
     for (long long t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        // last matrix whose first tile is <= t
-        int lo = 0, hi = B.count;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (T[mid].dbeg <= t) lo = mid;
-            else hi = mid;
-        }
+        // last matrix whose first tile is <= t: the map gives the matrix of
+        // tile 64 (t / 64), and at most 63 tiles lie between
+        int lo = ((ConstI)(B.dmap))[t >> 6];
+        while (lo + 1 < B.count && T[lo + 1].dbeg <= t) ++lo;
         const PsMat M = mat_at(B, lo);
         const long long lt = t - M.dbeg;
         const int ns = nstrips_of(M.m);
@@ -1443,6 +1442,9 @@ struct Plan {
 };
 
 size_t ws_round(size_t x) { return round_up(x, 256); }
+
+// Entries of the decode's tile map: one per 64 tiles.
+size_t dmap_len(long long nd) { return static_cast<size_t>((nd + 63) / 64); }
 
 // Threads per column in psgd_qreduce: the smallest power of two that leaves
 // each thread at most QR_PER_THREAD partials, at most 64.
@@ -1541,9 +1543,11 @@ Plan make_plan(const gc_mat* mats, int nmats) {
             P.mats.push_back(pm);
         }
         pb.eall = eall;
-        // the device table, then the psgd_qreduce workgroup -> matrix map
+        // the device table, then the psgd_qreduce workgroup -> matrix map and
+        // the psgd_decode tile -> matrix map (one entry per 64 tiles)
         pb.tbl_off = o;
-        o += ws_round(static_cast<size_t>(pb.count) * sizeof(PsMat) + static_cast<size_t>(pb.nr) * sizeof(int));
+        o += ws_round(static_cast<size_t>(pb.count) * sizeof(PsMat) +
+                      static_cast<size_t>(pb.nr + dmap_len(pb.nd)) * sizeof(int));
         const long long gmax = eall <= OUT_TWO_ROUNDS_MAX ? 2LL * OUT_GRID_MAX : OUT_GRID_MAX;
         pb.gout = static_cast<int>(std::min<long long>(gmax, std::max<long long>(1, eall / 1024)));
         P.batches.push_back(pb);
@@ -1591,6 +1595,7 @@ int validate_mat(const gc_mat& a, int i, int dtype, const std::string& fn, bool 
 struct TableImage {
     std::vector<PsMat> mats;
     std::vector<int> rmap;
+    std::vector<int> dmap;
 };
 
 // The table and map go to the device in stream order, as one copy.  From
@@ -1598,9 +1603,11 @@ struct TableImage {
 // image may go out of scope.
 int copy_table(const PsBatch& B, const TableImage& img, hipStream_t s) {
     const size_t tb = img.mats.size() * sizeof(PsMat), mb = img.rmap.size() * sizeof(int);
-    std::vector<char> buf(tb + mb);
+    const size_t db = img.dmap.size() * sizeof(int);
+    std::vector<char> buf(tb + mb + db);
     std::memcpy(buf.data(), img.mats.data(), tb);
     if (mb) std::memcpy(buf.data() + tb, img.rmap.data(), mb);
+    if (db) std::memcpy(buf.data() + tb + mb, img.dmap.data(), db);
     const hipError_t e = hipMemcpyAsync(const_cast<PsMat*>(B.tbl), buf.data(), buf.size(), hipMemcpyHostToDevice, s);
     if (e != hipSuccess)
         return fail(GC_ERR_HIP, std::string("PowerSGD matrix table copy: ") + hipGetErrorString(e));
@@ -1769,6 +1776,7 @@ int powersgd_call(const char* fn, StepKind kind, const gc_mat* mats, const int32
         PsBatch B{};
         B.tbl = reinterpret_cast<const PsMat*>(wp + pb.tbl_off);
         B.rmap = reinterpret_cast<const int*>(wp + pb.tbl_off + static_cast<size_t>(pb.count) * sizeof(PsMat));
+        B.dmap = B.rmap + pb.nr;
         B.count = pb.count;
         B.eta = eta;
         for (int c = 0; c < PQ_CLASSES + 3; ++c) B.cbeg[c] = pb.cbeg[c];
@@ -1782,6 +1790,12 @@ int powersgd_call(const char* fn, StepKind kind, const gc_mat* mats, const int32
         TableImage tbl;
         tbl.mats.resize(pb.count);
         tbl.rmap.resize(pb.nr);
+        tbl.dmap.resize(dmap_len(pb.nd));
+        for (size_t g = 0, k = 0; g < tbl.dmap.size(); ++g) {
+            const long long t0 = static_cast<long long>(g) * 64;
+            while (k + 1 < static_cast<size_t>(pb.count) && P.mats[pb.first + k + 1].dbeg <= t0) ++k;
+            tbl.dmap[g] = static_cast<int>(k);
+        }
         for (int k = 0; k < pb.count; ++k) {
             const PlanMat& pm = P.mats[pb.first + k];
             const gc_mat& a = mats[pm.idx];
