@@ -29,9 +29,15 @@ all-reduces P and then Q' (two calls per step).  Top-k index sets differ per
 worker, so the (index, value) pairs are all-gathered.  Uncompressed tensors
 (biases, norms) stay in a dense all-reduce.
 
-Parity unpinned against the pages: they print neither the formula nor a worked
-example.  The tests pin the collective costs against a step-by-step ring
-simulation, and the break-even bandwidth against a scan of the step times.
+The pages print neither the formula nor a worked example with its inputs, so
+no number of theirs can be reproduced.  The tests pin the collective costs
+against a step-by-step ring simulation and the break-even bandwidth against a
+scan of the step times; they also check, as properties over random draws, the
+five findings of the results section: a fixed encode-decode cost loses above
+some bandwidth; an encode-decode time beyond the hiding window removes any
+speed-up; all-gathered payloads stop paying as workers grow while all-reduced
+ones do not; faster compute raises the gain (a 1.75x case at 4x compute); and
+a shorter encode-decode time beats a higher compression ratio.
 
 Host code only: it makes no GPU call.
 """
