@@ -723,6 +723,18 @@ def cpu_baseline(name):
                     oracle.powersgd_ef_step(g.reshape(n, m), np.zeros((n, m), np.float32), q[l], 1.0, 4)
                 r = oracle.topk_ef_step(np.zeros(emb.size, np.float32), emb, 1.0, ek)
                 oracle.topk_decode(r["idx"], r["val"], emb.size)
+        elif name == "c1":
+            gs = [gen.c1_grad(t) for t in range(gen.C1_STEPS)]
+            sample = (f"the whole workload: {gen.C1_STEPS} steps of top-k {gen.C1_K} EF on d = {gen.C1_D}, "
+                      "memory carried from step to step")
+            nbytes = 4 * sum(g.size for g in gs)
+
+            def run():
+                mem = np.zeros(gen.C1_D, np.float32)
+                for g in gs:
+                    r = oracle.topk_ef_step(mem, g, gen.C1_ETA, gen.C1_K)
+                    oracle.topk_decode(r["idx"], r["val"], gen.C1_D)
+                    mem = r["mem"]
         elif name == "c3randk":
             g = gen.c3_grad(0)[:2_560_000]
             idx = gen.randk_indices(gen.CFG_C3, 0, g.size, g.size // 100)
