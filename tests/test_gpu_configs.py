@@ -23,6 +23,8 @@ the uncompressed vectors must agree bit for bit.
   * BERT-large: the benchmark's C5 step (all 144 matrices in one recorded
     plan, the embedding's top-k 1%), 4 steps; encoder layers 0 and 23 (12
     matrices) and the embedding are compared every step.
+  * Determinism: two instances of the C2 and C3 steps, built from the same
+    seeds, hold the same bits in every output and state buffer after every step.
 """
 import json
 import os
@@ -205,4 +207,34 @@ def test_c5_bert_shipped_steps():
         assert np.array_equal(out, oracle.topk_decode(ref["idx"], ref["val"], d)), f"C5 step {t}: decode"
         print(f"C5 step {t}: worst PowerSGD relative error {worst:.2e}", flush=True)
     del W
+    torch.cuda.empty_cache()
+
+
+def _c2_state(W):
+    ps = W.ps
+    return ([t.clone() for t in ps.out] + [t.clone() for t in ps.mem] + [t.clone() for t in ps.q] +
+            [t.clone() for t in ps.p] + [W.vout_buf.clone()])
+
+
+def _c3_state(W):
+    return [W.idx.clone(), W.val.clone(), W.out.clone(), W.mem.clone(), W.enc.sel.clone()]
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_config_determinism(name):
+    """Two instances of a configuration's step, from the same seeds, hold the same
+    bits after every step: outputs, memories, Q, P^ and the selection record
+    (compaction order and every reduction order included)."""
+    print(f"case: determinism of the {name} step, two instances, 4 steps", flush=True)
+    gc = lib()
+    make, state = (bench.C2, _c2_state) if name == "c2" else (bench.C3, _c3_state)
+    A, B = make(torch, gc, DEV), make(torch, gc, DEV)
+    for t in range(4):
+        A.step(t)
+        B.step(t)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(state(A), state(B))):
+            assert torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32)), \
+                f"{name} step {t}: buffer {i} differs between the two instances"
+    del A, B
     torch.cuda.empty_cache()
