@@ -72,6 +72,7 @@ constexpr int PQ_ROW_COST = 1024;
 constexpr int PQ_ROWS_MIN = 8;
 constexpr int Q_ROWS = 32;           // rows per chunk in psgd_q
 constexpr int ROW_GROUP = 8;         // rows whose loads are issued together in psgd_q / psgd_out
+constexpr int QR_QUAD_BATCH = 2;     // partials whose 4-column loads psgd_qreduce issues together
 constexpr int QR_PER_THREAD = 16;    // M^T P partials per psgd_qreduce thread before slicing a column
 constexpr int CUS = 256;             // MI355X compute units
 constexpr double STREAM_MIN_BYTES = 1e9;   // psgd_out traffic above which it streams
@@ -93,7 +94,7 @@ struct PsMat {
     float* out;
     float* praw;     // [n][4]  P = M Q
     double* gpart;   // [ng][16] partial Gram matrices
-    float* qpart;    // [nq][m][4] partial M^T P
+    float* qpart;    // [nq][4][m] partial M^T P, plane j = component j (planes < rank used)
     double* tmat;    // [16] T, row-major 4x4
     long long off;   // first entry of the matrix in the batch (matrices back to back)
     long long poff;  // fused classes: first unit of the matrix in its class's psgd_pq partition
@@ -122,6 +123,13 @@ constexpr int SMALL_MAX_N = 1024, SMALL_MAX_M = 1024;
 
 // Launch parameters of one launch group; the matrices (sorted by class) are
 // in a device table (in the workspace) copied there at the start of the step.
+// M^T P partial `part`, component j: m floats (plane j of that partial).
+// Writers and psgd_qreduce touch only the planes below the rank, so a rank-r
+// step moves r/4 of the bytes of a rank-4 one.
+__device__ __forceinline__ float* qplane(const PsMat& M, long long part, int j) {
+    return M.qpart + (part * 4 + j) * static_cast<long long>(M.m);
+}
+
 struct PsBatch {
     const PsMat* tbl;
     const int* rmap;               // psgd_qreduce workgroup -> matrix (after the table)
@@ -439,9 +447,16 @@ __device__ __forceinline__ void q_chunk(const PsMat& M, float eta, int strip, in
             }
         }
     }
-    float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(chunk) * m + col0;
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) dst[v] = make_float4(acc[v][0], acc[v][1], acc[v][2], acc[v][3]);
+    for (int j = 0; j < 4; ++j) {
+        if (j < M.rank) {
+            float* dst = qplane(M, chunk, j) + col0;
+            if constexpr (VEC == 4)
+                *reinterpret_cast<float4*>(dst) = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+            else
+                dst[0] = acc[0][j];
+        }
+    }
 }
 
 template <bool BF16, bool DEF>
@@ -739,10 +754,11 @@ __device__ __forceinline__ void pq_rows(const PsMat& M, float eta, int r0, int r
 #pragma unroll
     for (int c = 0; c < VPT; ++c) {
         if (act[c]) {
-            float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(part) * m + 4 * (t + c * NT);
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc)
-                dst[cc] = make_float4(qt[c][cc][0], qt[c][cc][1], qt[c][cc][2], qt[c][cc][3]);
+            for (int j = 0; j < 4; ++j)
+                if (j < M.rank)
+                    *reinterpret_cast<float4*>(qplane(M, part, j) + 4 * (t + c * NT)) =
+                        make_float4(qt[c][0][j], qt[c][1][j], qt[c][2][j], qt[c][3][j]);
         }
     }
     if (w == 0 && lane < 16) M.gpart[static_cast<long long>(part) * 16 + lane] = g;
@@ -836,7 +852,9 @@ __device__ void small_pq(const PsMat& M, float eta, float* s_p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) qt[j] = fmaf(mv, s_p[i * 4 + j], qt[j]);
         }
-        reinterpret_cast<float4*>(M.qpart)[c] = make_float4(qt[0], qt[1], qt[2], qt[3]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (j < M.rank) qplane(M, 0, j)[c] = qt[j];
     }
 }
 
@@ -1054,9 +1072,11 @@ __device__ __forceinline__ void pq_teams(const PsBatch& B, int cls, int wg_in_cl
             k += RG;
             if (k >= nr) {
                 if (act) {
-                    float4* dst = reinterpret_cast<float4*>(M.qpart) + static_cast<long long>(part) * m + 4 * tt;
 #pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) dst[cc] = make_float4(qt[cc][0], qt[cc][1], qt[cc][2], qt[cc][3]);
+                    for (int j = 0; j < 4; ++j)
+                        if (j < M.rank)
+                            *reinterpret_cast<float4*>(qplane(M, part, j) + 4 * tt) =
+                                make_float4(qt[0][j], qt[1][j], qt[2][j], qt[3][j]);
                 }
                 if (wt == 0 && lane < 16) M.gpart[static_cast<long long>(part) * 16 + lane] = g;
                 ++mi;
@@ -1122,16 +1142,19 @@ __device__ __forceinline__ void gram_schmidt_coeffs(const double G[16], int r, d
     }
 }
 
-// Q reduction.  A matrix with nq M^T P partials uses S = qr_slices(nq)
-// threads per column (a power of two): workgroup lwg takes columns
-// [lwg 256/S, (lwg+1) 256/S), thread t sums the partials c = t / (256/S) + S i
-// of column t % (256/S) in order, and the S slice sums are added in slice
-// order through LDS.  The Gram partials are summed the same way with 16
-// slices.  Thread 0 builds T; the column threads write Q' = (M^T P) T.
+// Q reduction.  A matrix with nq M^T P partials uses S = qr_slices(nq, W)
+// threads per column group (a power of two), where a thread covers W = 4
+// adjacent columns (float4 loads from each partial plane) when m % 4 == 0, else
+// W = 1: workgroup lwg takes the column groups [lwg 256/S, (lwg+1) 256/S),
+// thread t sums the partials c = t / (256/S) + S i of column group t % (256/S)
+// in order, and the S slice sums are added in slice order through LDS.  Only
+// the planes below the rank are read.  The Gram partials are summed the same
+// way with 16 slices.  Thread 0 builds T; the column threads write
+// Q' = (M^T P) T.
 __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
     __shared__ double s_g[16][16];
     __shared__ double s_T[16];
-    __shared__ double4 s_q[PS_THREADS];
+    __shared__ double4 s_q[4][PS_THREADS];
     // the matrix of this workgroup from the plan's map: one scalar load, where
     // a search of the table would chain eight dependent ones
     typedef const __attribute__((address_space(4))) int* ConstI;
@@ -1139,6 +1162,7 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
     const int lwg = blockIdx.x - M.begin_r;
     const int m = M.m, r = M.rank, t = threadIdx.x;
     const int S = M.qs, QC = PS_THREADS / S;
+    const bool quad = m % 4 == 0;
     {
         const int e = t & 15, sl = t >> 4;
         double g = 0.0;
@@ -1156,24 +1180,49 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
         s_g[sl][e] = g;
     }
     const int cl = t % QC, sl = t / QC;
-    const int col = lwg * QC + cl;
-    double4 sv = make_double4(0.0, 0.0, 0.0, 0.0);
+    const int col = (lwg * QC + cl) * (quad ? 4 : 1);
+    // sv[c]: the rank components of column col + c
+    double4 sv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sv[c] = make_double4(0.0, 0.0, 0.0, 0.0);
     if (col < m) {
-        const float4* qp = reinterpret_cast<const float4*>(M.qpart) + col;
-        for (int c = sl; c < M.nq; c += 4 * S) {
-            float4 x[4];
+        if (quad) {
+            for (int c = sl; c < M.nq; c += QR_QUAD_BATCH * S) {
+                float4 x[QR_QUAD_BATCH][4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int cu = c + S * u;
-                x[u] = cu < M.nq ? qp[static_cast<long long>(cu) * m] : make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int u = 0; u < QR_QUAD_BATCH; ++u) {
+                    const int cu = c + S * u;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        x[u][j] = (cu < M.nq && j < r) ? *reinterpret_cast<const float4*>(qplane(M, cu, j) + col)
+                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int u = 0; u < QR_QUAD_BATCH; ++u) {
+                    sv[0].x += x[u][0].x; sv[1].x += x[u][0].y; sv[2].x += x[u][0].z; sv[3].x += x[u][0].w;
+                    sv[0].y += x[u][1].x; sv[1].y += x[u][1].y; sv[2].y += x[u][1].z; sv[3].y += x[u][1].w;
+                    sv[0].z += x[u][2].x; sv[1].z += x[u][2].y; sv[2].z += x[u][2].z; sv[3].z += x[u][2].w;
+                    sv[0].w += x[u][3].x; sv[1].w += x[u][3].y; sv[2].w += x[u][3].z; sv[3].w += x[u][3].w;
+                }
             }
+        } else {
+            for (int c = sl; c < M.nq; c += 4 * S) {
+                float x[4][4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                sv.x += x[u].x; sv.y += x[u].y; sv.z += x[u].z; sv.w += x[u].w;
+                for (int u = 0; u < 4; ++u) {
+                    const int cu = c + S * u;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x[u][j] = (cu < M.nq && j < r) ? qplane(M, cu, j)[col] : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    sv[0].x += x[u][0]; sv[0].y += x[u][1]; sv[0].z += x[u][2]; sv[0].w += x[u][3];
+                }
             }
         }
     }
-    s_q[t] = sv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s_q[c][t] = sv[c];
     __syncthreads();
     if (t == 0) {
         double G[16], T[16];
@@ -1191,21 +1240,25 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
         }
     }
     __syncthreads();
-    if (t < QC && col < m) {
-        double4 a = s_q[t];
+    // one thread per column: column c of group g adds its S slices in order
+    const int ncol = quad ? 4 : 1;
+    for (int idx = t; idx < QC * ncol; idx += PS_THREADS) {
+        const int g = idx % QC, c = idx / QC;
+        const int cc = (lwg * QC + g) * ncol + c;
+        if (cc >= m) continue;
+        double4 a = s_q[c][g];
         for (int k = 1; k < S; ++k) {
-            const double4 x = s_q[k * QC + t];
+            const double4 x = s_q[c][k * QC + g];
             a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
         }
         const double sa[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll 1
+        for (int j = 0; j < r; ++j) {
+            double v = 0.0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (j < r) {
-                double v = 0.0;
-#pragma unroll
-                for (int i = 0; i <= j; ++i) v += sa[i] * s_T[i * 4 + j];
-                M.q[static_cast<long long>(j) * m + col] = static_cast<float>(v);
-            }
+            for (int i = 0; i < 4; ++i)
+                if (i <= j) v += sa[i] * s_T[i * 4 + j];
+            M.q[static_cast<long long>(j) * m + cc] = static_cast<float>(v);
         }
     }
 }
@@ -1446,11 +1499,13 @@ size_t ws_round(size_t x) { return round_up(x, 256); }
 // Entries of the decode's tile map: one per 64 tiles.
 size_t dmap_len(long long nd) { return static_cast<size_t>((nd + 63) / 64); }
 
-// Threads per column in psgd_qreduce: the smallest power of two that leaves
-// each thread at most QR_PER_THREAD partials, at most 64.
-int qr_slices(int nq) {
+// Threads per column group in psgd_qreduce: the smallest power of two that
+// leaves each thread at most QR_PER_THREAD partial loads (a thread covering
+// 4 columns loads 4 values per partial: QR_PER_THREAD / 4 partials), at most 64.
+int qr_slices(int nq, int cols_per_thread) {
+    const int per = cols_per_thread == 4 ? QR_PER_THREAD / 4 : QR_PER_THREAD;
     int sl = 1;
-    while (sl < 64 && sl * QR_PER_THREAD < nq) sl *= 2;
+    while (sl < 64 && sl * per < nq) sl *= 2;
     return sl;
 }
 
@@ -1528,9 +1583,10 @@ Plan make_plan(const gc_mat* mats, int nmats) {
                 pm.begin_q = pb.nq;
                 pb.nq += nstrips_host(m) * pm.nq;
             }
-            pm.qs = qr_slices(pm.nq);
+            const int cpt = m % 4 == 0 ? 4 : 1;     // psgd_qreduce columns per thread
+            pm.qs = qr_slices(pm.nq, cpt);
             pm.begin_r = pb.nr;
-            const int qc = PS_THREADS / pm.qs;
+            const int qc = PS_THREADS / pm.qs * cpt;
             pb.nr += (m + qc - 1) / qc;
             pm.dbeg = pb.nd;
             pb.nd += static_cast<long long>((n + DEC_ROWS - 1) / DEC_ROWS) * nstrips_host(m);
