@@ -382,8 +382,7 @@ def gc_powersgd_materialize(mats: Sequence[Mat], prev_rank, ws, stream=None) -> 
 
 # ------------------------------------------------------------------ uncompressed tensors
 
-def gc_passthrough(grads, outs, eta: float, stream=None) -> None:
-    """Vectors sent uncompressed: outs[i] = eta * grads[i] (float32, one rounding)."""
+def _vec_array(grads, outs):
     import torch
     _need(len(grads) >= 1 and len(grads) == len(outs), "need one out per gradient, at least one")
     arr = (gc_vec * len(grads))()
@@ -392,8 +391,35 @@ def gc_passthrough(grads, outs, eta: float, stream=None) -> None:
         _need(g.dtype == grads[0].dtype, "every gradient must have the first one's dtype")
         _need(g.numel() == o.numel(), f"grads[{i}] and outs[{i}] must have the same number of entries")
         arr[i] = gc_vec(_ptr(g), _ptr(o), g.numel())
+    return arr
+
+
+def gc_passthrough(grads, outs, eta: float, stream=None) -> None:
+    """Vectors sent uncompressed: outs[i] = eta * grads[i] (float32, one rounding)."""
+    arr = _vec_array(grads, outs)
     _check(lib.gc_passthrough(arr, len(grads), _dtype_code(grads[0]), float(eta), _stream(stream)),
            "gc_passthrough")
+
+
+class PreparedVecs:
+    """gc_passthrough's argument array built once, for a set of vectors that is
+    sent every step: calling it costs one library call and no per-vector
+    marshalling.  It keeps the tensors alive; they must stay in place (their
+    device addresses are in the array)."""
+
+    def __init__(self, grads, outs):
+        self.arr = _vec_array(grads, outs)
+        self.n = len(grads)
+        self.dtype = _dtype_code(grads[0])
+        self._keep = (list(grads), list(outs))
+
+    def __call__(self, eta: float, stream=None) -> None:
+        _check(lib.gc_passthrough(self.arr, self.n, self.dtype, float(eta), _stream(stream)), "gc_passthrough")
+
+
+def gc_passthrough_prepare(grads, outs) -> PreparedVecs:
+    """The argument array of gc_passthrough(grads, outs, ...) for repeated calls."""
+    return PreparedVecs(grads, outs)
 
 
 # ------------------------------------------------------------------ norms / Accordion

@@ -303,6 +303,13 @@ def test_passthrough_binding_checks(gcl):
         gcl.gc_passthrough([f32(4), f32(4)], [f32(4)], 1.0)
     with pytest.raises(TypeError, match="outs"):
         gcl.gc_passthrough([f32(4)], [torch.zeros(4, dtype=torch.float64)], 1.0)
+    # the prepared form validates the same way, once
+    with pytest.raises(ValueError, match="same number of entries"):
+        gcl.gc_passthrough_prepare([f32(4)], [f32(5)])
+    with pytest.raises(TypeError, match="outs"):
+        gcl.gc_passthrough_prepare([f32(4)], [torch.zeros(4, dtype=torch.float64)])
+    with pytest.raises(ValueError, match="device tensor"):
+        gcl.gc_passthrough_prepare([f32(4)], [f32(4)])
 
 
 def test_accordion_host_matches_oracle(gcl):

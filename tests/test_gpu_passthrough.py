@@ -55,3 +55,21 @@ def test_resnet18_vectors():
         outs = run(host, 1.0)
         for h, o in zip(host, outs):
             assert np.array_equal(f32_bits(o), f32_bits(oracle.passthrough_step(h, 1.0)))
+
+
+def test_prepared_call_equals_direct_call():
+    print("case: passthrough prepared call, ResNet-18 set, 3 calls", flush=True)
+    gc = lib()
+    for t in range(2):
+        host = gen.c2_vectors(t)
+        grads = [to_dev(h) for h in host]
+        direct = [torch.full((h.size,), float("nan"), device=DEV) for h in host]
+        outs = [torch.full((h.size,), float("nan"), device=DEV) for h in host]
+        call = gc.gc_passthrough_prepare(grads, outs)
+        for eta in (1.0, 0.3, 1.0):
+            gc.gc_passthrough(grads, direct, eta)
+            call(eta)
+            torch.cuda.synchronize()
+            for h, a, b in zip(host, direct, outs):
+                assert np.array_equal(f32_bits(a), f32_bits(b))
+                assert np.array_equal(f32_bits(b), f32_bits(oracle.passthrough_step(h, eta)))
