@@ -16,14 +16,21 @@
 //                4(t+NT)..) takes rows in groups, finishes each row's
 //                P = M Q_in with a DPP reduce-scatter plus one LDS exchange,
 //                and adds M[i,:]^T P[i,:] into per-thread M^T P accumulators;
-//                one M^T P and one Gram (float64) partial per workgroup and
-//                matrix.  Five classes by row length (<= 1024, 2048, 4096,
-//                6144, 8192, m a multiple of 4)
+//                one M^T P partial (the rank's planes of m floats) and one
+//                Gram (float64) partial per workgroup and matrix.  Five
+//                classes by row length (<= 1024, 2048, 4096, 6144, 8192, m a
+//                multiple of 4)
+//   psgd_pq_teams the same pass for classes 0-2 of a small launch group in
+//                one launch (teams of a class's row width in 1024-thread
+//                workgroups), small matrices included
+//   psgd_small   the same pass, one workgroup per matrix, for n, m <= 1024
+//                with m not a multiple of 4
 //   psgd_p/psgd_q the same two products as separate passes, for the other
-//                shapes (m not a multiple of 4, or m > 8192)
+//                shapes (m not a multiple of 4 and n or m > 1024, or m > 8192)
 //   psgd_qreduce sums the partials in a fixed order, builds T from the summed
 //                Gram matrix, writes Q' = (M^T P) T into q (warm start)
 //   psgd_out     P^ = P T per row, out = P^ Q'^T, mem = M - out, P^ into p
+//   psgd_decode  the deferred form's output pass: out = P^ Q'^T, P^ into p
 //
 // Two forms of the memory:
 //   explicit     (gc_powersgd_ef_step) M is never stored: psgd_pq and psgd_out

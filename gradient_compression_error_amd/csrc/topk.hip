@@ -59,7 +59,7 @@ constexpr int H2_BINS = 4096;
 constexpr int H2_SHIFT = 7;    // key bits 18..7
 constexpr int H3_BINS = 128;   // key bits 6..0
 constexpr int NCOPY = 8;       // copies of the level-1/2 histograms (spreads the device atomics)
-constexpr int TK_SMALL_GRID = 2048;
+constexpr int TK_SMALL_GRID = 2048;      // workgroups of the candidate passes: one per tile, at most this many
 constexpr int DEC_TILE = 4096;
 constexpr int PREP_ZERO_BLOCKS = 32;     // topk_prep blocks that zero the histograms
 constexpr int FAST_GRID = 256;           // workgroups of topk_capture's slot pass
