@@ -25,6 +25,10 @@ the uncompressed vectors must agree bit for bit.
     matrices) and the embedding are compared every step.
   * Determinism: two instances of the C2 and C3 steps, built from the same
     seeds, hold the same bits in every output and state buffer after every step.
+  * The ResNet-50-sized flat gradient over the 50 steps of its protocol
+    (fresh gradient each step, deferred top-k 1%): every step against the
+    properties that fix an exact top-k EF step, on the device at full size;
+    four steps against the oracle from the GPU's state.
 """
 import json
 import os
@@ -37,6 +41,7 @@ import torch
 import gen
 import oracle
 from gpu_util import DEV, f32_bits, lib, rel_err, require_gpu, to_dev
+from topk_props import check_topk_step_properties
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
@@ -237,4 +242,46 @@ def test_config_determinism(name):
             assert torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32)), \
                 f"{name} step {t}: buffer {i} differs between the two instances"
     del A, B
+    torch.cuda.empty_cache()
+
+
+def test_c3_fifty_steps_deferred():
+    """The ResNet-50-sized flat gradient for the 50 steps of its protocol, a
+    fresh heavy-tailed gradient each step, k = 1%, through the benchmark's
+    deferred top-k encoder and decode: every step against the properties that
+    fix an exact top-k EF step (checked on the device, at full size), and
+    steps 0, 1, 25 and 49 against the float64 oracle from the memory the GPU
+    held before them."""
+    print("case: C3 50 steps, deferred top-k, d=25.6M k=1%", flush=True)
+    gc = lib()
+    d, k = gen.C3_D, gen.C3_KS[1]
+    enc = bench.TopkEncoder(torch, gc, DEV)
+    assert enc.deferred
+    mem = torch.zeros(d, device=DEV)
+    idx = torch.empty(k, dtype=torch.int32, device=DEV)
+    val = torch.empty(k, device=DEV)
+    out = torch.empty(d, device=DEV)
+    ws = torch.empty(gc.gc_topk_workspace_bytes(d, k), dtype=torch.uint8, device=DEV)
+    oracle_steps = {0, 1, 25, 49}
+    for t in range(50):
+        g_h = gen.c3_grad(t)
+        g = to_dev(g_h)
+        before = mem.clone()
+        if enc.has_prev:
+            gc.gc_topk_materialize(before, enc.sel)
+        acc = before + g                       # fl32(m + fl32(1 * g)): eta = 1
+        enc.encode(g, mem, 1.0, k, idx, val, ws)
+        gc.gc_topk_decode(idx, val, out)
+        after = mem.clone()
+        gc.gc_topk_materialize(after, enc.sel)
+        torch.cuda.synchronize()
+        check_topk_step_properties(acc, idx, val, out, after, k, f"C3 step {t}")
+        if t in oracle_steps:
+            ref = oracle.topk_ef_step(before.cpu().numpy(), g_h, 1.0, k)
+            assert np.array_equal(idx.cpu().numpy(), ref["idx"]), f"C3 step {t}: indices vs oracle"
+            assert np.array_equal(f32_bits(val), f32_bits(ref["val"])), f"C3 step {t}: values vs oracle"
+            assert np.array_equal(f32_bits(after), f32_bits(ref["mem"])), f"C3 step {t}: memory vs oracle"
+        if t % 10 == 9:
+            print(f"C3 step {t}: ok", flush=True)
+    del mem, out, ws
     torch.cuda.empty_cache()
