@@ -25,8 +25,9 @@ the uncompressed vectors must agree bit for bit.
   * BERT-large: the benchmark's C5 step (all 144 matrices in one recorded
     plan, the embedding's top-k 1%), the 5 steps of the protocol; encoder layers 0 and 23 (12
     matrices) and the embedding are compared every step.
-  * Determinism: two instances of the C2 and C3 steps, built from the same
-    seeds, hold the same bits in every output and state buffer after every step.
+  * Determinism: two instances of each configuration's step (C1-C5), built
+    from the same seeds, hold the same bits in every output and state buffer
+    after every step (C4 across a rank switch).
   * The ResNet-50-sized flat gradient over the 50 steps of its protocol
     (fresh gradient each step, deferred top-k 1%): every step against the
     properties that fix an exact top-k EF step, on the device at full size;
@@ -236,16 +237,45 @@ def _c3_state(W):
     return [W.idx.clone(), W.val.clone(), W.out.clone(), W.mem.clone(), W.enc.sel.clone()]
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
+def _c4_state(W):
+    ps = W.ps
+    return ([t.clone() for t in ps.out] + [t.clone() for t in ps.mem] + [t.clone() for t in ps.q] +
+            [t.clone() for t in ps.p] + [W.norms.clone()])
+
+
+def _c5_state(W):
+    ps = W.ps
+    return ([ps.out_buf.clone()] + [t.clone() for t in ps.mem] + [t.clone() for t in ps.q] +
+            [t.clone() for t in ps.p] + [W.idx.clone(), W.val.clone(), W.emb_out.clone(), W.emb_mem.clone(),
+                                         W.enc.sel.clone()])
+
+
+def _make_c4(torch_, gc, dev):
+    W = bench.C4(torch_, gc, dev)
+    # trajectory steps 100..111: the checks at 100 (l_high) and 110 (l_low, ranks 2 -> 4)
+    W.prepare(0, 12)
+    return W
+
+
+CONFIGS = {
+    "c1": (bench.C1, _c3_state, 10),
+    "c2": (bench.C2, _c2_state, 4),
+    "c3": (bench.C3, _c3_state, 4),
+    "c4": (_make_c4, _c4_state, 12),
+    "c5": (bench.C5, _c5_state, 3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
 def test_config_determinism(name):
     """Two instances of a configuration's step, from the same seeds, hold the same
-    bits after every step: outputs, memories, Q, P^ and the selection record
-    (compaction order and every reduction order included)."""
-    print(f"case: determinism of the {name} step, two instances, 4 steps", flush=True)
+    bits after every step: outputs, memories, Q, P^, the norms and the
+    selection record (compaction order and every reduction order included)."""
+    make, state, steps = CONFIGS[name]
+    print(f"case: determinism of the {name} step, two instances, {steps} steps", flush=True)
     gc = lib()
-    make, state = (bench.C2, _c2_state) if name == "c2" else (bench.C3, _c3_state)
     A, B = make(torch, gc, DEV), make(torch, gc, DEV)
-    for t in range(4):
+    for t in range(steps):
         A.step(t)
         B.step(t)
         torch.cuda.synchronize()
