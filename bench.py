@@ -87,6 +87,13 @@ class Workload:
     config = {}
     dtype = "f32"             # arithmetic type of the path (gradients widen exactly to float32)
     graphable = False         # steps may be captured as HIP graphs (--graph)
+    entries = 0               # gradient entries per step
+    decisions = None          # Accordion checks of the timed steps, when the workload has them
+
+    def message_words(self):
+        """32-bit words one worker sends per step (values and indices, P and Q
+        entries, uncompressed entries), averaged over the timed steps."""
+        return None
 
     def graph_key(self, t):
         """Which captured graph replays step t (None: run it eagerly)."""
@@ -286,6 +293,8 @@ class C5(Workload):
         self.pending = None
         total = sum(sizes)
         self.grad_bytes = 2 * total
+        self.entries = total
+        self.decisions = []
         mat_elems = sum(n * m for n, m in shapes)
         self.kernel_bytes = {
             **psgd_kernel_bytes(shapes, self.ps.ranks, 2),
@@ -312,6 +321,13 @@ class C5(Workload):
     def graph_key(self, t):
         return None if t % 10 == 0 else t % 2
 
+    def message_words(self):
+        # P and Q entries of the 144 matrices, and the embedding's (index, value) pairs
+        return sum(r * (n + m) for (n, m), r in zip(self.ps.shapes, self.ps.ranks)) + 2 * self.k
+
+    def timed_begin(self):
+        self.decisions = []
+
     def step(self, t):
         self.host_part(t)
         self.device_step(t)
@@ -325,6 +341,9 @@ class C5(Workload):
             self.levels, self.prev = gc.gc_accordion_select(self.norms_host.numpy(), self.prev, gen.C4_THRESHOLD,
                                                             self.checks > 0)
             self.checks += 1
+            self.decisions.append({"check": self.checks,
+                                   "tensors_at_l_low": int(np.sum(self.levels == gc.GC_LEVEL_LOW)),
+                                   "tensors": int(len(self.levels))})
             self.pending = None
 
     def device_step(self, t):
@@ -379,6 +398,7 @@ class C1(Workload):
         self.val = torch.empty(self.k, dtype=torch.float32, device=dev)
         self.ws = torch.empty(gc.gc_topk_workspace_bytes(d, self.k), dtype=torch.uint8, device=dev)
         self.enc = TopkEncoder(torch, gc, dev)
+        self.entries = d
         self.grad_bytes = 4 * d
         self.alg_bytes = 16 * d + 16 * self.k
         self.kernel_bytes = {"topk_accum_hist": 12 * d, "topk_decode_set": 4 * d + 8 * self.k}
@@ -392,6 +412,9 @@ class C1(Workload):
 
     def graph_key(self, t):
         return t % len(self.g)
+
+    def message_words(self):
+        return 2 * self.k
 
     def step(self, t):
         self.enc.encode(self.g[t % len(self.g)], self.mem, gen.C1_ETA, self.k, self.idx, self.val, self.ws)
@@ -426,6 +449,7 @@ class C2(Workload):
         self.vcalls = [gc.gc_passthrough_prepare(vs, self.vout) for vs in self.vsets]
         ve = sum(vsizes)
         me = sum(sizes)
+        self.entries, self.vector_entries = me + ve, ve
         self.grad_bytes = 4 * (me + ve)
         self.alg_bytes = psgd_bytes(shapes, self.ps.ranks, 4) + 8 * ve
         self.kernel_bytes = {**psgd_kernel_bytes(shapes, self.ps.ranks, 4), "passthrough": 8 * ve}
@@ -440,6 +464,10 @@ class C2(Workload):
 
     def graph_key(self, t):
         return t % 2
+
+    def message_words(self):
+        # P and Q entries of the 21 matrices, and the BN/bias vectors as they are
+        return sum(r * (n + m) for (n, m), r in zip(self.ps.shapes, self.ps.ranks)) + self.vector_entries
 
     def step(self, t):
         self.ps.step(t % 2)
@@ -460,6 +488,7 @@ class C3(Workload):
         self.val = torch.empty(k, dtype=torch.float32, device=dev)
         self.ws = torch.empty(gc.gc_topk_workspace_bytes(d, k), dtype=torch.uint8, device=dev)
         self.enc = TopkEncoder(torch, gc, dev)
+        self.entries = d
         self.grad_bytes = 4 * d
         self.alg_bytes = 16 * d + 16 * k
         self.kernel_bytes = {"topk_accum_hist": 12 * d, "topk_decode_set": 4 * d + 8 * k}
@@ -473,6 +502,9 @@ class C3(Workload):
 
     def graph_key(self, t):
         return t % 2
+
+    def message_words(self):
+        return 2 * self.k
 
     def step(self, t):
         self.enc.encode(self.g[t % 2], self.mem, 1.0, self.k, self.idx, self.val, self.ws)
@@ -493,6 +525,7 @@ class C3Randk(Workload):
         self.mem = torch.zeros(d, device=dev)
         self.out = torch.zeros(d, device=dev)
         self.val = torch.empty(k, dtype=torch.float32, device=dev)
+        self.entries = d
         self.grad_bytes = 4 * d
         self.alg_bytes = 16 * d + 16 * k
         self.kernel_bytes = {"randk_encode": 12 * d + 8 * k, "topk_decode_set": 4 * d + 8 * k}
@@ -504,6 +537,10 @@ class C3Randk(Workload):
 
     def graph_key(self, t):
         return t % 2
+
+    def message_words(self):
+        # the values only: every worker draws the same index subset from the shared seed
+        return self.k
 
     def step(self, t):
         s = t % 2
@@ -534,6 +571,8 @@ class C3Acc(Workload):
         self.prev = np.zeros(1, np.float32)
         self.k = self.k_low
         self.ks = []
+        self.entries = d
+        self.decisions = []
         self.grad_bytes = 4 * d
         self.kernel_bytes = {"topk_accum_hist": 12 * d, "topk_decode_set": 4 * d + 8 * self.k_low,
                              "norm_partial": 4 * d / 10.0}
@@ -549,8 +588,13 @@ class C3Acc(Workload):
         for t in range(tmax):
             self.g[t] = self.base[t % 2] * float(gen.acc_topk_scale(t))
 
+    def message_words(self):
+        ks = self.ks or [self.k_low]
+        return 2 * sum(ks) / len(ks)
+
     def timed_begin(self):
         self.ks = []
+        self.decisions = []
 
     @property
     def alg_bytes(self):
@@ -564,6 +608,7 @@ class C3Acc(Workload):
             gc.gc_grad_norm([g], self.norms, self.nws)
             lv, self.prev = gc.gc_accordion_select(self.norms.cpu().numpy(), self.prev, gen.C4_THRESHOLD, t > 0)
             self.k = self.k_low if lv[0] == gc.GC_LEVEL_LOW else self.k_high
+            self.decisions.append({"step": t, "level": "l_low" if lv[0] == gc.GC_LEVEL_LOW else "l_high", "k": self.k})
         self.ks.append(self.k)
         self.enc.encode(g, self.mem, 1.0, self.k, self.idx[:self.k], self.val[:self.k], self.ws)
         gc.gc_topk_decode(self.idx[:self.k], self.val[:self.k], self.out)
@@ -609,6 +654,8 @@ class C4(Workload):
         self.norms_host = torch.empty(len(shapes), dtype=torch.float32, pin_memory=True)
         self.ev_norm = torch.cuda.Event()
         me = sum(self.sizes)
+        self.entries = me
+        self.decisions = []
         self.grad_bytes = 4 * me
         self.ranks_log = []
         self.kernel_bytes = {**psgd_kernel_bytes(shapes, [4] * len(shapes), 4), "norm_partial": 4 * me / 10.0}
@@ -668,6 +715,11 @@ class C4(Workload):
 
     def timed_begin(self):
         self.ranks_log = []
+        self.decisions = []
+
+    def message_words(self):
+        log = self.ranks_log or [[4] * len(self.shapes)]
+        return sum(sum(r * (n + m) for (n, m), r in zip(self.shapes, ranks)) for ranks in log) / len(log)
 
     @property
     def alg_bytes(self):
@@ -687,6 +739,8 @@ class C4(Workload):
             lv, self.prev_norms = gc.gc_accordion_select(self.norms_host.numpy(), self.prev_norms,
                                                          gen.C4_THRESHOLD, True)
             new = [gen.C4_RANK_LOW_COMPRESSION if v == gc.GC_LEVEL_LOW else gen.C4_RANK_HIGH_COMPRESSION for v in lv]
+            self.decisions.append({"step": tau, "layers_at_l_low": int(np.sum(lv == gc.GC_LEVEL_LOW)),
+                                   "ranks": sorted(set(new))})
             for l, (old_r, new_r) in enumerate(zip(self.ps.ranks, new)):
                 refill_q(self.ps, l, tau, old_r, new_r, gen.CFG_C4, self.refills[(tau, l)])
             self.ps.set_ranks(new)
@@ -969,6 +1023,11 @@ def main():
             run_step(args.warmup + 1 + t)
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3
+    # the accounting of the timed steps, before any later pass moves a
+    # trajectory workload on (the ranks or k in force, the checks taken)
+    alg_bytes = W.alg_bytes
+    words = W.message_words()
+    decisions = list(W.decisions) if W.decisions is not None else None
     if graphs:
         gc.gc_timing_enable(dominant)
         for t in range(args.steps):
@@ -993,7 +1052,7 @@ def main():
 
     ms_step = wall_ms / args.steps
     gbs = W.grad_bytes / (ms_step * 1e-3) / 1e9
-    step_frac = W.alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    step_frac = alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
     launches_per_step = k_launches / args.steps
     bytes_per_launch = W.kernel_bytes[dominant] / launches_per_step
     mean_launch_ms = k_ms / k_launches
@@ -1008,11 +1067,12 @@ def main():
 
     line = {"metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "us_per_step": round(ms_step * 1e3, 1),
-            "hbm_frac_step": round(step_frac, 4), "algorithmic_bytes_per_step": int(W.alg_bytes),
+            "hbm_frac_step": round(step_frac, 4), "algorithmic_bytes_per_step": int(alg_bytes),
+            "algorithmic_gbs": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
             "us_per_step_median": round(float(np.median(step_ms)) * 1e3, 1),
             "us_per_step_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 1),
             "device_copy_gbs": round(copy_gbs, 1),
-            "frac_of_device_copy_step": round(W.alg_bytes / (ms_step * 1e-3) / 1e9 / copy_gbs, 4),
+            "frac_of_device_copy_step": round(alg_bytes / (ms_step * 1e-3) / 1e9 / copy_gbs, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": W.dtype,
             "grad_dtype": W.config.get("grad_dtype", "f32"), "memory_dtype": W.config.get("memory_dtype", "f32"),
             "data": "synthetic", "cache": "cold: 1 GiB written then 1 GiB read between steps" if args.flush else "warm (back-to-back steps)",
@@ -1020,6 +1080,11 @@ def main():
             "config": W.config, "description": W.description, "device": torch.cuda.get_device_name(0),
             "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
             "roofline": roof}
+    if words:
+        line["message"] = {"words_per_step": round(float(words), 1), "bytes_per_step": int(4 * words),
+                           "compression_ratio": round(W.entries / float(words), 2)}
+    if decisions is not None:
+        line["level_decisions"] = decisions
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cb = cpu_baseline(W.name)
