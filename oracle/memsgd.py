@@ -8,7 +8,9 @@ at the rate of vanilla SGD (results section).
 The shift ``a`` is not defined on the pages; it is an argument here.  Noise is
 passed in (one row per step) so that the compressed and the uncompressed runs
 see the same stochastic gradients.  Everything is float64 -- this is the
-algorithm, not the float32 kernel.  Parity unpinned beyond the qualitative
+algorithm, not the float32 kernel.  Pinned exactly by two identities of the
+update (k = d is vanilla SGD bit for bit; x_t - m_t moves by exactly -eta_t
+times the stochastic gradient, to float64 rounding) and qualitatively by the
 convergence claim.
 """
 from __future__ import annotations
@@ -46,10 +48,12 @@ def _subset64(v: np.ndarray, idx: np.ndarray) -> np.ndarray:
 
 
 def run_memsgd(prob: QuadraticProblem, x0: np.ndarray, noise: np.ndarray, sigma: float,
-               k: int | None, mu: float, a: float, subsets: np.ndarray | None = None):
+               k: int | None, mu: float, a: float, subsets: np.ndarray | None = None,
+               trace: list | None = None):
     """Run len(noise) steps.  k=None means no compression (vanilla SGD).
     With ``subsets`` (one row of k coordinates per step) the compressor is
-    rand-k on those coordinates instead of top-k.
+    rand-k on those coordinates instead of top-k.  With ``trace`` (a list),
+    every step appends (eta_t, stochastic gradient, x_{t+1}, m_{t+1}).
 
     Returns (x_T, x_bar_T) where x_bar_T is the uniform average of x_1..x_T.
     """
@@ -69,4 +73,6 @@ def run_memsgd(prob: QuadraticProblem, x0: np.ndarray, noise: np.ndarray, sigma:
         mem = acc - g
         x = x - g
         xsum += x
+        if trace is not None:
+            trace.append((eta, grad, x.copy(), mem.copy()))
     return x, xsum / noise.shape[0]

@@ -55,3 +55,51 @@ def test_memory_is_what_makes_it_converge():
         sel = oracle.magnitude_order(v)[:k]
         x[sel] -= v[sel]
     assert prob.f(x_mem) < 0.5 * prob.f(x)
+
+
+def _problem(seed, d=60, mu=1.0, L=10.0):
+    r = gen.rng(0, gen.KIND_MISC, seed)
+    lam = np.exp(r.uniform(np.log(mu), np.log(L), d))
+    return oracle.QuadraticProblem(lam, r.standard_normal(d)), r
+
+
+def test_k_equal_d_is_vanilla_sgd():
+    """With k = d the compressor keeps everything: g_t = m_t + eta_t grad_t,
+    the memory stays zero and the iterate is SGD's, bit for bit."""
+    prob, r = _problem(92)
+    d = prob.lam.size
+    noise = r.standard_normal((400, d))
+    tr = []
+    x_k, xb_k = oracle.run_memsgd(prob, np.zeros(d), noise, 0.1, d, 1.0, 16 * 10.0, trace=tr)
+    x_s, xb_s = oracle.run_memsgd(prob, np.zeros(d), noise, 0.1, None, 1.0, 16 * 10.0)
+    assert np.array_equal(x_k, x_s) and np.array_equal(xb_k, xb_s)
+    assert all(not m.any() for _, _, _, m in tr)
+
+
+@pytest.mark.parametrize("k,subsets", [(1, False), (7, False), (7, True)])
+def test_virtual_iterate_moves_like_sgd(k, subsets):
+    """Method section of "Sparsified SGD with Memory": the memory holds what
+    was not yet applied, so x_{t+1} - m_{t+1} = x_t - m_t - eta_t grad_t exactly
+    (here to float64 rounding) for any comp_k, top-k or rand-k; and the memory
+    holds at most d - k nonzero entries after each top-k step."""
+    prob, r = _problem(93)
+    d, T = prob.lam.size, 600
+    noise = r.standard_normal((T, d))
+    sub = np.stack([np.sort(r.choice(d, k, replace=False)) for _ in range(T)]) if subsets else None
+    tr = []
+    x0 = r.standard_normal(d)
+    oracle.run_memsgd(prob, x0, noise, 0.1, k, 1.0, max(d / k, 160.0), subsets=sub, trace=tr)
+    v_prev = x0.copy()                       # x_0 - m_0, m_0 = 0
+    for t, (eta, grad, x, m) in enumerate(tr):
+        v = x - m
+        want = v_prev - eta * grad
+        scale = max(1.0, float(np.max(np.abs(v_prev))))
+        assert np.max(np.abs(v - want)) <= 1e-13 * scale, f"step {t}"
+        if not subsets:
+            assert np.count_nonzero(m) <= d - k
+        v_prev = v
+    # a planted mistake (the memory keeps acc instead of acc - g) breaks the identity
+    eta, grad, x, m = tr[10]
+    _, _, x_prev, m_prev = tr[9]
+    acc = m_prev + eta * grad
+    assert np.max(np.abs((x - acc) - (x_prev - m_prev - eta * grad))) > 1e-6
