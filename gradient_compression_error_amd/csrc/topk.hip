@@ -749,6 +749,152 @@ __global__ __launch_bounds__(256) void topk_decode_add(
     }
 }
 
+// ---------------------------------------------------------------- small vectors
+
+// The whole encode of a vector of d <= SMALL_D entries in one workgroup, where
+// the multi-kernel path would be nine dependent launches of almost no work.
+// Thread t holds the SMALL_PER consecutive entries [t SMALL_PER, (t+1)
+// SMALL_PER), so index order is thread order and then register order, and
+// one block scan places every selected entry.  Same arithmetic and selection
+// as the general path: acc = fl32(m + fl32(eta * g)); the 12 + 12 + 7-bit
+// radix select on the magnitude key, in LDS; the entries above the threshold
+// key T, then ties in index order.  Memory, pairs and the selection record get
+// the same bits.
+constexpr int SMALL_THREADS = 1024;
+constexpr int SMALL_PER = 16;
+constexpr long long SMALL_D = static_cast<long long>(SMALL_THREADS) * SMALL_PER;   // 16384
+
+template <bool BF16, bool DEFR>
+__global__ __launch_bounds__(SMALL_THREADS) void topk_small(
+        const void* __restrict__ grad, float* __restrict__ mem, long long d, float eta, unsigned k,
+        int* __restrict__ out_idx, float* __restrict__ out_val, unsigned* __restrict__ sel) {
+    __shared__ unsigned h[H1_BINS];
+    __shared__ unsigned s_tmp[SMALL_THREADS / 64];
+    __shared__ unsigned s_bin, s_above;
+    const int t = threadIdx.x;
+    const long long i0 = static_cast<long long>(t) * SMALL_PER;
+    const int n = static_cast<int>(i0 < d ? (d - i0 < SMALL_PER ? d - i0 : SMALL_PER) : 0);   // entries held
+    PrevSel ps{};
+    if constexpr (DEFR) ps = read_sel(sel);
+    float a[SMALL_PER];
+    unsigned key[SMALL_PER];
+    if (n == SMALL_PER) {
+#pragma unroll
+        for (int u = 0; u < SMALL_PER / 4; ++u) {
+            const float4 m4 = reinterpret_cast<const float4*>(mem)[i0 / 4 + u];
+            const float4 g4 = load_grad4<BF16>(grad, i0 / 4 + u);
+            const float mv[4] = {m4.x, m4.y, m4.z, m4.w}, gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float m = mv[j];
+                if constexpr (DEFR) m = mem_of(m, i0 + 4 * u + j, ps);
+                a[4 * u + j] = ef_acc(m, eta, gv[j]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < SMALL_PER; ++c) {
+            a[c] = 0.0f;
+            if (c < n) {
+                float m = mem[i0 + c];
+                if constexpr (DEFR) m = mem_of(m, i0 + c, ps);
+                a[c] = ef_acc(m, eta, load_grad1<BF16>(grad, i0 + c));
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < SMALL_PER; ++c) key[c] = key_of(a[c]);
+    // level 1: key >> 19
+    for (int b = t; b < H1_BINS; b += SMALL_THREADS) h[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < SMALL_PER; ++c)
+        if (c < n) atomicAdd(&h[key[c] >> H1_SHIFT], 1u);
+    __syncthreads();
+    select_bin<H1_BINS, 1, SMALL_THREADS>(h, H1_BINS, k, h, s_tmp, &s_bin, &s_above);
+    const unsigned b1 = s_bin, above1 = s_above;
+    // level 2: (key >> 7) & 4095 within b1
+    for (int b = t; b < H2_BINS; b += SMALL_THREADS) h[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < SMALL_PER; ++c)
+        if (c < n && (key[c] >> H1_SHIFT) == b1) atomicAdd(&h[(key[c] >> H2_SHIFT) & (H2_BINS - 1)], 1u);
+    __syncthreads();
+    select_bin<H2_BINS, 1, SMALL_THREADS>(h, H2_BINS, k - above1, h, s_tmp, &s_bin, &s_above);
+    const unsigned prefix2 = (b1 << 12) | s_bin, above2 = above1 + s_above;
+    // level 3: key & 127 within prefix2
+    for (int b = t; b < H3_BINS; b += SMALL_THREADS) h[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < SMALL_PER; ++c)
+        if (c < n && (key[c] >> H2_SHIFT) == prefix2) atomicAdd(&h[key[c] & (H3_BINS - 1)], 1u);
+    __syncthreads();
+    select_bin<H3_BINS, 1, SMALL_THREADS>(h, H3_BINS, k - above2, h, s_tmp, &s_bin, &s_above);
+    const unsigned thr = (prefix2 << H2_SHIFT) | s_bin;
+    const unsigned need = k - (above2 + s_above);   // ties of key thr taken, lowest indices first
+    // one block scan of the packed per-thread counts (above thr in the low 16
+    // bits, equal to thr in the high 16) places every entry
+    unsigned cgt = 0, ceq = 0;
+#pragma unroll
+    for (int c = 0; c < SMALL_PER; ++c) {
+        cgt += (c < n && key[c] > thr) ? 1u : 0u;
+        ceq += (c < n && key[c] == thr) ? 1u : 0u;
+    }
+    const unsigned v = cgt | (ceq << 16);
+    unsigned total;
+    const unsigned excl = block_inclusive_scan<SMALL_THREADS / 64>(v, s_tmp, &total) - v;
+    unsigned gt_before = excl & 0xFFFFu, eq_before = excl >> 16;
+    int cut = -1;
+    unsigned taken = 0;          // bit c: entry c selected
+#pragma unroll
+    for (int c = 0; c < SMALL_PER; ++c) {
+        if (c < n) {
+            const bool gt = key[c] > thr, eq = key[c] == thr;
+            const bool take = gt || (eq && eq_before < need);
+            if (take) {
+                const unsigned pos = gt_before + (eq_before < need ? eq_before : need);
+                out_idx[pos] = static_cast<int>(i0 + c);
+                out_val[pos] = a[c];
+                if (eq && eq_before + 1 == need) cut = static_cast<int>(i0 + c);
+                taken |= 1u << c;
+            }
+            gt_before += gt ? 1u : 0u;
+            eq_before += eq ? 1u : 0u;
+        }
+    }
+    // explicit memory: the selected entries become +0.0; deferred: acc stays
+    // and the record marks them
+    const unsigned zero = sel ? 0u : taken;
+    float* const mrow = mem + i0;
+    if (n == SMALL_PER) {
+#pragma unroll
+        for (int u = 0; u < SMALL_PER / 4; ++u) {
+            float4 x;
+            x.x = (zero >> (4 * u)) & 1u ? 0.0f : a[4 * u];
+            x.y = (zero >> (4 * u + 1)) & 1u ? 0.0f : a[4 * u + 1];
+            x.z = (zero >> (4 * u + 2)) & 1u ? 0.0f : a[4 * u + 2];
+            x.w = (zero >> (4 * u + 3)) & 1u ? 0.0f : a[4 * u + 3];
+            reinterpret_cast<float4*>(mrow)[u] = x;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < SMALL_PER; ++c)
+            if (c < n) mrow[c] = (zero >> c) & 1u ? 0.0f : a[c];
+    }
+    if (sel) {
+        // the selection record of a deferred call: at most one thread holds
+        // the cut (none when no tie is taken); thread 0 writes the record
+        if (t == 0) s_bin = 0xFFFFFFFFu;
+        __syncthreads();
+        if (cut >= 0) s_bin = static_cast<unsigned>(cut);
+        __syncthreads();
+        if (t == 0) {
+            sel[0] = thr;
+            sel[1] = s_bin;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- rand-k
 
 // Rand-k with memory ("Sparsified SGD with Memory", method section): comp_k
@@ -853,6 +999,20 @@ int topk_encode(const char* fname, const void* grad, int grad_dtype, float* mem,
         return fail(GC_ERR_WORKSPACE, fn + ": workspace smaller than gc_topk_workspace_bytes");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (d <= SMALL_D) {
+        // one workgroup does the whole encode (the workspace is not touched)
+        TimedLaunch tl("topk_small", s);
+        const unsigned ku = static_cast<unsigned>(k);
+        if (grad_dtype == GC_BF16 && defr)
+            topk_small<true, true><<<1, SMALL_THREADS, 0, s>>>(grad, mem, d, eta, ku, out_idx, out_val, sel_out);
+        else if (grad_dtype == GC_BF16)
+            topk_small<true, false><<<1, SMALL_THREADS, 0, s>>>(grad, mem, d, eta, ku, out_idx, out_val, sel_out);
+        else if (defr)
+            topk_small<false, true><<<1, SMALL_THREADS, 0, s>>>(grad, mem, d, eta, ku, out_idx, out_val, sel_out);
+        else
+            topk_small<false, false><<<1, SMALL_THREADS, 0, s>>>(grad, mem, d, eta, ku, out_idx, out_val, sel_out);
+        return check_launch("topk_small");
+    }
     char* w = static_cast<char*>(ws);
     auto* st = reinterpret_cast<TopkState*>(w + L.state);
     auto* hist1 = reinterpret_cast<unsigned*>(w + L.hist1);

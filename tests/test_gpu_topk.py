@@ -55,12 +55,25 @@ def test_c1_ten_steps():
 
 
 @pytest.mark.parametrize("d,k", [(1, 1), (3, 2), (4, 4), (4095, 1), (4095, 4095), (4096, 100), (4097, 4097),
-                                 (12289, 1000), (12289, 1), (100_003, 777), (300_001, 30_000)])
+                                 (12289, 1000), (12289, 1), (16383, 500), (16384, 16384), (16384, 1), (16385, 163),
+                                 (100_003, 777), (300_001, 30_000)])
 def test_edge_sizes(d, k):
     print(f"case: edge d={d} k={k}", flush=True)
     g = gen.gaussian_vector(d, d % 1000)
     m = gen.gaussian_vector(d, d % 1000 + 1, 0.5)
     one_step(TopkRunner(d, k), g, m, 0.37)
+
+
+@pytest.mark.parametrize("d,k", [(16384, 1), (16384, 1234), (16384, 16383), (16385, 1234)])
+def test_tie_heavy_single_workgroup_sizes(d, k):
+    """Vectors of at most 16384 entries take the single-workgroup encode; the
+    first size past it takes the multi-kernel path.  Both on a coarse grid
+    (many ties at the threshold), with and without memory, bf16 too."""
+    print(f"case: tie-heavy d={d} k={k}", flush=True)
+    one_step(TopkRunner(d, k), gen.tie_heavy(d, k), np.zeros(d, np.float32), 1.0)
+    one_step(TopkRunner(d, k), gen.tie_heavy(d, k + 1), gen.tie_heavy(d, k + 2), 1.0)
+    g = gen.f32_to_bf16_bits(gen.gaussian_vector(d, 40 + k % 7, 1e-3))
+    one_step(TopkRunner(d, k), g, gen.gaussian_vector(d, 41, 1e-3), 0.3)
 
 
 @pytest.mark.parametrize("k", [1, 1000, 12_345, 49_999, 50_000])

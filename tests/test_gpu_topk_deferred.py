@@ -90,18 +90,20 @@ def test_tiny_ten_steps_against_oracle():
         mem_h = ref["mem"]
 
 
-@pytest.mark.parametrize("d,k", [(1, 1), (7, 3), (1000, 1000), (4097, 1), (65537, 600), (300_001, 3000)])
+@pytest.mark.parametrize("d,k", [(1, 1), (7, 3), (1000, 1000), (4097, 1), (16384, 16384), (16384, 700),
+                                 (16385, 700), (65537, 600), (300_001, 3000)])
 def test_edge_sizes(d, k):
     print(f"case: deferred top-k edge d={d} k={k}", flush=True)
     grads = [gen.gaussian_vector(d, 2000 + t + d % 97) for t in range(4)]
     chain(d, k, grads, gen.gaussian_vector(d, 3000 + d % 89, 0.5), 0.37, label="edge")
 
 
-def test_tie_heavy():
+@pytest.mark.parametrize("d", [50_000, 16_384])
+def test_tie_heavy(d):
     """Values on a coarse grid: many ties at the threshold, so the cut index
-    (the last tie taken) decides which equal keys were selected."""
-    d = 50_000
-    print("case: deferred top-k tie-heavy", flush=True)
+    (the last tie taken) decides which equal keys were selected (16384: the
+    single-workgroup encode)."""
+    print(f"case: deferred top-k tie-heavy d={d}", flush=True)
     grads = [gen.tie_heavy(d, 1000 + t) for t in range(5)]
     chain(d, 1234, grads, gen.tie_heavy(d, 7), 1.0, label="ties")
     chain(d, 1, grads, np.zeros(d, np.float32), 1.0, label="ties k=1")
