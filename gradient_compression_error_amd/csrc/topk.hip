@@ -28,6 +28,10 @@
 //                    counts, then the k (index, value) pairs in ascending
 //                    index order; zeroes the selected memory entries.
 //
+// Vectors of at most 16384 entries skip that chain: topk_small does the
+// accumulate, the three levels, the compaction and the memory in one
+// workgroup, with the same arithmetic and the same bits.
+//
 // Deferred memory (gc_topk_ef_encode_deferred): topk_emit leaves the selected
 // entries as they are (no scattered writes) and topk_count / topk_emit write
 // a selection record {T, index of the last tie taken}; the next call's
