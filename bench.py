@@ -401,7 +401,7 @@ class C1(Workload):
         self.entries = d
         self.grad_bytes = 4 * d
         self.alg_bytes = 16 * d + 16 * self.k
-        self.kernel_bytes = {"topk_accum_hist": 12 * d, "topk_decode_set": 4 * d + 8 * self.k}
+        self.kernel_bytes = {"topk_small": 12 * d + 8 * self.k, "topk_decode_set": 4 * d + 8 * self.k}
         self.description = gen.WORKLOADS["c1"].description + " (latency only)"
         self.config = {"workload": "mem-sgd tiny vector", "params": d, "topk_k": self.k, "eta": gen.C1_ETA,
                        "grad_dtype": "f32", "memory_dtype": "f32", "claim": "latency only"}
