@@ -118,7 +118,7 @@ int gc_timing_read(double* total_ms, int64_t* launches) {
 }
 
 const char* gc_kernel_names(void) {
-    return "topk_prep,topk_accum_hist,topk_select1,topk_capture,topk_select2,topk_refine,"
+    return "topk_prep,topk_accum_hist,topk_capture,topk_select2,topk_refine,"
            "topk_count,topk_emit,topk_materialize,topk_decode_set,topk_decode_add,topk_small,randk_encode,"
            "psgd_pq,psgd_p,psgd_q,psgd_qreduce,psgd_out,psgd_decode,psgd_materialize,"
            "norm_partial,norm_final,passthrough";

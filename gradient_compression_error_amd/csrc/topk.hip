@@ -14,11 +14,16 @@
 //                    histogram of key>>19 per workgroup, merged with device
 //                    atomics into one of 8 copies; every entry with key >= G
 //                    is appended, in index order, to its tile's slot region
-//                    (wave ballots + a cross-wave prefix).  topk_select1 -> bin b1
-//   topk_capture     when G <= b1's lower edge every candidate is already in
-//                    the slots: only the level-2 histogram of bin b1 is built
-//                    from them.  Otherwise re-reads acc and appends every
-//                    entry with key>>19 >= b1 instead.  topk_select2 -> bin b2
+//                    (wave ballots + a cross-wave prefix); the captured
+//                    entries are counted.
+//   topk_capture     every workgroup finds bin b1 of the k-th largest key
+//                    with one wave, scanning the level-1 bins from G's bin
+//                    with the captured count as the count above it.  When
+//                    at least k entries were captured (G <= b1's lower edge)
+//                    every candidate is already in the slots: only the
+//                    level-2 histogram of bin b1 is built from them.
+//                    Otherwise re-reads acc and appends every entry with
+//                    key>>19 >= b1 instead.  topk_select2 -> bin b2
 //   topk_refine      level-3 histogram over the captured entries only (8
 //                    copies, like levels 1 and 2).
 //   topk_count       threshold T and ties to take from the level-3 histogram
@@ -42,9 +47,11 @@
 // for fp32 gradients); the rest work on the captured entries, which are a
 // superset of the candidates at or above the threshold in index order, so
 // the later kernels filter by key.  The guess only decides how much work is
-// done, never the result.  The select steps
-// are single-workgroup kernels: the kernel boundary is the only cross-
-// workgroup synchronisation (a per-workgroup device-scope release fence
+// done, never the result.  The level-1 bin is found at the start of the
+// kernel that needs it, by every workgroup; the level-2 bin by a
+// single-workgroup kernel (a 4096-bin search that every workgroup repeating
+// would cost more than the launch).  The kernel boundary is the only
+// cross-workgroup synchronisation (a per-workgroup device-scope release fence
 // would write back the L2 once per workgroup).
 #include <cmath>
 
@@ -63,6 +70,14 @@ constexpr int H2_BINS = 4096;
 constexpr int H2_SHIFT = 7;    // key bits 18..7
 constexpr int H3_BINS = 128;   // key bits 6..0
 constexpr int NCOPY = 8;       // copies of the level-1/2 histograms (spreads the device atomics)
+// The counters zeroed by topk_prep, one block: word offsets from its start.
+constexpr int HIST1_W = 0;                                // NCOPY x 4096 level-1 bins
+constexpr int HIST2_W = HIST1_W + NCOPY * H1_BINS;        // NCOPY x 4096 level-2 bins
+constexpr int HIST3_W = HIST2_W + NCOPY * H2_BINS;        // NCOPY x 128 level-3 bins
+constexpr int CAP_W = HIST3_W + NCOPY * H3_BINS;          // NCOPY counts of captured entries,
+constexpr int CAP_STRIDE = 32;                            // one 128-byte line each
+constexpr int COUNTERS_W = CAP_W + NCOPY * CAP_STRIDE;
+static_assert(COUNTERS_W % 64 == 0, "256-byte multiple");
 constexpr int TK_SMALL_GRID = 2048;      // workgroups of the candidate passes: one per tile, at most this many
 constexpr int DEC_TILE = 4096;
 constexpr int PREP_ZERO_BLOCKS = 32;     // topk_prep blocks that zero the histograms
@@ -80,7 +95,7 @@ struct TopkState {
 static_assert(sizeof(TopkState) == 64, "TopkState layout");
 
 struct TopkLayout {
-    size_t state, hist1, hist2, hist3, tile_cnt, wg_gt, wg_eq;
+    size_t state, counters, tile_cnt, wg_gt, wg_eq;
     size_t slot_idx, slot_val, total, zero_from, zero_end;
     long long ntiles;
 };
@@ -92,9 +107,7 @@ TopkLayout topk_layout(long long d) {
     size_t o = 0;
     L.state = o;     o += round_up(sizeof(TopkState), 256);
     L.zero_from = o;
-    L.hist1 = o;     o += NCOPY * H1_BINS * 4;
-    L.hist2 = o;     o += NCOPY * H2_BINS * 4;
-    L.hist3 = o;     o += round_up(NCOPY * H3_BINS * 4, 256);
+    L.counters = o;  o += COUNTERS_W * 4;
     L.zero_end = o;
     L.tile_cnt = o;  o += round_up(nt * 4, 256);
     L.wg_gt = o;     o += TK_SMALL_GRID * 4;
@@ -194,6 +207,74 @@ __device__ void select_bin(const unsigned* hist, int stride, unsigned need, unsi
         }
     }
     __syncthreads();
+}
+
+// Inclusive prefix sum over the 64 lanes of one wave (all lanes active).
+__device__ __forceinline__ unsigned wave_inclusive_scan(unsigned v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned t = __shfl_up(v, o, WAVE);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Level-1 bin b1 of the k-th largest key, found by one wave from the
+// captured count instead of the whole histogram.  With S(b) = #keys whose
+// level-1 bin is >= b, b1 is the highest bin with S(b1) >= k and
+// S(g0) = ncap is known for the guess bin g0 (every key with bin >= g0 was
+// captured).  ncap >= k: b1 >= g0; windows of 64 bins are scanned upwards
+// from g0, S falling by each window's count.  ncap < k: b1 < g0; windows are
+// scanned downwards from g0 - 1, S rising by each window's count.  S(4096) = 0
+// < k and S(0) = d >= k, so at most 64 windows.  Lane j holds one bin of the
+// window (NCOPY copies summed).  Every lane gets b1 and S(b1 + 1).
+struct BinPick {
+    unsigned bin, above;
+};
+
+__device__ __forceinline__ BinPick find_b1_wave(const unsigned* __restrict__ hist1, unsigned ncap, int g0,
+                                                unsigned k) {
+    const int lane = threadIdx.x & 63;
+    if (ncap >= k) {
+        unsigned s_lo = ncap;   // S(lo)
+        for (int lo = g0; lo < H1_BINS; lo += 64) {
+            const int b = lo + lane;
+            unsigned c = 0;
+            if (b < H1_BINS) {
+#pragma unroll
+                for (int cp = 0; cp < NCOPY; ++cp) c += hist1[cp * H1_BINS + b];
+            }
+            const unsigned incl = wave_inclusive_scan(c);
+            const unsigned excl = incl - c;
+            // S(lo + j) = s_lo - excl(j) >= k  <=>  excl(j) <= s_lo - k  (s_lo >= k here)
+            const unsigned long long keep = __ballot(excl <= s_lo - k);
+            const int j = 63 - __builtin_clzll(keep);   // highest such lane (lane 0 always qualifies)
+            const unsigned total = readlane_any(incl, 63);
+            if (j < 63 || s_lo - total < k)
+                return BinPick{static_cast<unsigned>(lo + j), s_lo - readlane_any(incl, j)};
+            s_lo -= total;
+        }
+        return BinPick{H1_BINS - 1, 0u};   // not reached for a consistent histogram
+    }
+    unsigned s_hi = ncap;   // S(hi)
+    for (int hi = g0; hi > 0; hi -= 64) {
+        const int b = hi - 1 - lane;
+        unsigned c = 0;
+        if (b >= 0) {
+#pragma unroll
+            for (int cp = 0; cp < NCOPY; ++cp) c += hist1[cp * H1_BINS + b];
+        }
+        const unsigned incl = wave_inclusive_scan(c);
+        // S(hi - 1 - j) = s_hi + incl(j): the first lane where it reaches k
+        const unsigned long long hit = __ballot(s_hi + incl >= k);
+        if (hit) {
+            const int j = __builtin_ctzll(hit);
+            return BinPick{static_cast<unsigned>(hi - 1 - j), s_hi + readlane_any(incl - c, j)};
+        }
+        s_hi += readlane_any(incl, 63);
+    }
+    return BinPick{0u, 0u};   // not reached for a consistent histogram
 }
 
 // ---------------------------------------------------------------- kernels
@@ -328,7 +409,7 @@ __device__ __forceinline__ unsigned append_chunks(const bool (&flag)[U][J], cons
 template <bool BF16, bool DEFR>
 __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
         const void* __restrict__ grad, float* __restrict__ mem, long long d, float eta,
-        const TopkState* __restrict__ st, unsigned* __restrict__ hist1, int* __restrict__ slot_idx,
+        const TopkState* __restrict__ st, unsigned* __restrict__ ctr, int* __restrict__ slot_idx,
         float* __restrict__ slot_val, unsigned* __restrict__ tile_cnt, const unsigned* __restrict__ sel) {
     __shared__ unsigned h[H1_BINS];
     __shared__ unsigned s_cnt[2][TK_SUBS][4];
@@ -403,50 +484,62 @@ __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
         }
         running += append_chunks<1, 1>(cap, a, e0, running, sidx, sval, s_cnt, parity);
     }
-    if (threadIdx.x == 0) tile_cnt[blockIdx.x] = running;
+    if (threadIdx.x == 0) {
+        tile_cnt[blockIdx.x] = running;
+        if (running) atomicAdd(ctr + CAP_W + (blockIdx.x % NCOPY) * CAP_STRIDE, running);
+    }
     __syncthreads();
-    unsigned* dst = hist1 + (blockIdx.x % NCOPY) * H1_BINS;
+    unsigned* dst = ctr + HIST1_W + (blockIdx.x % NCOPY) * H1_BINS;
     for (int i = threadIdx.x; i < H1_BINS; i += TK_THREADS) {
         const unsigned c = h[i];
         if (c) atomicAdd(dst + i, c);
     }
 }
 
-constexpr int SEL_THREADS = 1024;   // single-workgroup selection kernels
-
-__global__ __launch_bounds__(SEL_THREADS) void topk_select1(const unsigned* __restrict__ hist1, unsigned k,
-                                                            TopkState* __restrict__ st) {
-    __shared__ unsigned s_h[H1_BINS];
-    __shared__ unsigned s_tmp[SEL_THREADS / 64];
-    __shared__ unsigned s_bin, s_above;
-    select_bin<H1_BINS, NCOPY, SEL_THREADS>(hist1, H1_BINS, k, s_h, s_tmp, &s_bin, &s_above);
-    if (threadIdx.x == 0) {
-        st->b1 = s_bin;
-        st->above1 = s_above;
-        st->fast = st->guess <= (s_bin << H1_SHIFT) ? 1u : 0u;
-    }
-}
-
-// Level-2 histogram of bin b1.  Fast case (every key >= b1 << 19 is already in
-// the slots): from the tile's slots.  Otherwise re-reads acc and replaces the
-// tile's slots with the entries of key>>19 >= b1, in index order.
+// Level-1 bin b1 (the bin of the k-th largest key; every workgroup finds it
+// with find_b1_wave, workgroup 0 records it), then the level-2 histogram of
+// bin b1.  Fast case (every key >= b1 << 19 is already
+// in the slots): from the tile's slots.  Otherwise re-reads acc and replaces
+// the tile's slots with the entries of key>>19 >= b1, in index order.
+// The fast case holds exactly when at least k entries were captured: the
+// slots hold the keys of level-1 bin >= bin(guess), and b1 is the highest
+// bin whose count from the top reaches k.
 __global__ __launch_bounds__(TK_THREADS) void topk_capture(
-        const float* __restrict__ acc, long long d, const TopkState* __restrict__ st,
-        unsigned* __restrict__ hist2, int* __restrict__ slot_idx, float* __restrict__ slot_val,
+        const float* __restrict__ acc, long long d, unsigned k, TopkState* __restrict__ st,
+        unsigned* __restrict__ ctr, int* __restrict__ slot_idx, float* __restrict__ slot_val,
         unsigned* __restrict__ tile_cnt) {
     __shared__ unsigned h[H2_BINS];
     __shared__ unsigned s_cnt[2][TK_SUBS][4];
+    __shared__ unsigned s_b1;
+    // both loads in flight together: the guess bin addresses the first window
+    const int g0 = static_cast<int>(st->guess >> H1_SHIFT);
+    unsigned ncap = 0;
+#pragma unroll
+    for (int c = 0; c < NCOPY; ++c) ncap += ctr[CAP_W + c * CAP_STRIDE];
+    asm volatile("" ::"s"(g0));   // keeps the guess load here instead of after the exit test
+    const bool fast = ncap >= k;
+    // fast case: the first FAST_GRID workgroups stride over the tiles' slots; the rest exit
+    if (fast && static_cast<int>(blockIdx.x) >= FAST_GRID) return;
+    if (threadIdx.x < 64) {
+        const BinPick p1 = find_b1_wave(ctr + HIST1_W, ncap, g0, k);
+        if (threadIdx.x == 0) {
+            s_b1 = p1.bin;
+            if (blockIdx.x == 0) {
+                st->b1 = p1.bin;
+                st->above1 = p1.above;
+                st->fast = fast ? 1u : 0u;
+            }
+        }
+    }
     for (int i = threadIdx.x; i < H2_BINS; i += TK_THREADS) h[i] = 0u;
     __syncthreads();
 
-    const unsigned b1 = st->b1;
+    const unsigned b1 = s_b1;
     const long long base = static_cast<long long>(blockIdx.x) * TK_TILE;
     int* const sidx = slot_idx + base;
     float* const sval = slot_val + base;
-    if (st->fast) {
-        // the first FAST_GRID workgroups stride over the tiles' slots; the rest exit
+    if (fast) {
         const int ntiles = static_cast<int>(gridDim.x);
-        if (static_cast<int>(blockIdx.x) >= FAST_GRID) return;
         for (int t = blockIdx.x; t < ntiles; t += FAST_GRID) {
             const unsigned cnt = tile_cnt[t];
             const float* tv = slot_val + static_cast<long long>(t) * TK_TILE;
@@ -496,12 +589,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_capture(
         if (threadIdx.x == 0) tile_cnt[blockIdx.x] = running;
     }
     __syncthreads();
-    unsigned* dst = hist2 + (blockIdx.x % NCOPY) * H2_BINS;
+    unsigned* dst = ctr + HIST2_W + (blockIdx.x % NCOPY) * H2_BINS;
     for (int i = threadIdx.x; i < H2_BINS; i += TK_THREADS) {
         const unsigned c = h[i];
         if (c) atomicAdd(dst + i, c);
     }
 }
+
+constexpr int SEL_THREADS = 1024;   // single-workgroup selection kernel
 
 __global__ __launch_bounds__(SEL_THREADS) void topk_select2(const unsigned* __restrict__ hist2, unsigned k,
                                                             TopkState* __restrict__ st) {
@@ -1019,9 +1114,8 @@ int topk_encode(const char* fname, const void* grad, int grad_dtype, float* mem,
     }
     char* w = static_cast<char*>(ws);
     auto* st = reinterpret_cast<TopkState*>(w + L.state);
-    auto* hist1 = reinterpret_cast<unsigned*>(w + L.hist1);
-    auto* hist2 = reinterpret_cast<unsigned*>(w + L.hist2);
-    auto* hist3 = reinterpret_cast<unsigned*>(w + L.hist3);
+    auto* ctr = reinterpret_cast<unsigned*>(w + L.counters);
+    auto* hist3 = ctr + HIST3_W;
     auto* tile_cnt = reinterpret_cast<unsigned*>(w + L.tile_cnt);
     auto* wg_gt = reinterpret_cast<unsigned*>(w + L.wg_gt);
     auto* wg_eq = reinterpret_cast<unsigned*>(w + L.wg_eq);
@@ -1051,32 +1145,27 @@ int topk_encode(const char* fname, const void* grad, int grad_dtype, float* mem,
     {
         TimedLaunch tl("topk_accum_hist", s);
         if (grad_dtype == GC_BF16 && defr)
-            topk_accum_hist<true, true><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx,
-                                                                      slot_val, tile_cnt, sel);
+            topk_accum_hist<true, true><<<ntiles, TK_THREADS, 0, s>>>(
+                grad, mem, d, eta, st, ctr, slot_idx, slot_val, tile_cnt, sel);
         else if (grad_dtype == GC_BF16)
-            topk_accum_hist<true, false><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx,
-                                                                       slot_val, tile_cnt, sel);
+            topk_accum_hist<true, false><<<ntiles, TK_THREADS, 0, s>>>(
+                grad, mem, d, eta, st, ctr, slot_idx, slot_val, tile_cnt, sel);
         else if (defr)
-            topk_accum_hist<false, true><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx,
-                                                                       slot_val, tile_cnt, sel);
+            topk_accum_hist<false, true><<<ntiles, TK_THREADS, 0, s>>>(
+                grad, mem, d, eta, st, ctr, slot_idx, slot_val, tile_cnt, sel);
         else
-            topk_accum_hist<false, false><<<ntiles, TK_THREADS, 0, s>>>(grad, mem, d, eta, st, hist1, slot_idx,
-                                                                        slot_val, tile_cnt, sel);
+            topk_accum_hist<false, false><<<ntiles, TK_THREADS, 0, s>>>(
+                grad, mem, d, eta, st, ctr, slot_idx, slot_val, tile_cnt, sel);
         if ((rc = check_launch("topk_accum_hist")) != GC_OK) return rc;
     }
     {
-        TimedLaunch tl("topk_select1", s);
-        topk_select1<<<1, SEL_THREADS, 0, s>>>(hist1, ku, st);
-        if ((rc = check_launch("topk_select1")) != GC_OK) return rc;
-    }
-    {
         TimedLaunch tl("topk_capture", s);
-        topk_capture<<<ntiles, TK_THREADS, 0, s>>>(mem, d, st, hist2, slot_idx, slot_val, tile_cnt);
+        topk_capture<<<ntiles, TK_THREADS, 0, s>>>(mem, d, ku, st, ctr, slot_idx, slot_val, tile_cnt);
         if ((rc = check_launch("topk_capture")) != GC_OK) return rc;
     }
     {
         TimedLaunch tl("topk_select2", s);
-        topk_select2<<<1, SEL_THREADS, 0, s>>>(hist2, ku, st);
+        topk_select2<<<1, SEL_THREADS, 0, s>>>(ctr + HIST2_W, ku, st);
         if ((rc = check_launch("topk_select2")) != GC_OK) return rc;
     }
     {

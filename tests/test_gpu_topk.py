@@ -199,6 +199,60 @@ def test_guess_too_high_takes_full_capture():
     assert np.count_nonzero(ref["g"]) == k
 
 
+def _outside_sampled_runs(d, n, rng):
+    """n positions none of which lies in the 256 sampled runs of 64 entries
+    (run r starts at floor(r d / 256)), so the sample cannot see them."""
+    starts = (np.arange(256, dtype=np.int64) * d) // 256
+    pos = []
+    while len(pos) < n:
+        p = int(rng.integers(0, d))
+        r = min(255, (p * 256) // d + 1)
+        if not any(s <= p < s + 64 for s in starts[max(0, r - 2):r + 1]):
+            pos.append(p)
+    return np.unique(np.array(pos, np.int64))
+
+
+def test_guess_far_below_threshold_scans_up():
+    """The k largest magnitudes (around 1e20) all lie outside the sampled runs,
+    so the guess comes from the N(0, 1e-3^2) bulk and lies ~1500 level-1 bins
+    below the threshold's bin: the slots hold every candidate and the level-1
+    bin is found by scanning some 24 windows of 64 bins upwards from the
+    guess.  Bit-exact with the oracle."""
+    d = 1 << 20
+    rng = np.random.default_rng(91)
+    g = gen.gaussian_vector(d, 91, 1e-3)
+    big = _outside_sampled_runs(d, 3000, rng)
+    g[big] = (1e20 * (1.0 + rng.random(big.size))).astype(np.float32) * np.where(rng.random(big.size) < 0.5, -1, 1)
+    k = 2000
+    print(f"case: top-k guess far below threshold d={d} k={k}", flush=True)
+    r = TopkRunner(d, k)
+    ref = one_step(r, g, np.zeros(d, np.float32), 1.0)
+    state = r.ws[:64].view(torch.int32).cpu().numpy()
+    assert state[8] == 1, "expected the slot path (every candidate captured)"
+    assert (state[0] - (state[7] >> 19)) > 64 * 10, "guess expected many windows below the level-1 bin"
+    assert np.count_nonzero(ref["g"]) == k
+
+
+def test_guess_far_above_threshold_scans_down():
+    """64 entries of 1e30 inside one sampled run lift the guess ~1700 level-1
+    bins above the threshold's bin (k = 1000 keeps the sampled rank below 64
+    and reaches into the N(0, 1e-3^2) bulk): the capture re-reads the
+    accumulator, after finding the level-1 bin by scanning some 27 windows
+    downwards from the guess.  Bit-exact."""
+    d = 1 << 20
+    g = gen.gaussian_vector(d, 92, 1e-3)
+    run0 = 7 * (d // 256)
+    g[run0:run0 + 64] = 1e30
+    k = 1000
+    print(f"case: top-k guess far above threshold d={d} k={k}", flush=True)
+    r = TopkRunner(d, k)
+    ref = one_step(r, g, np.zeros(d, np.float32), 1.0)
+    state = r.ws[:64].view(torch.int32).cpu().numpy()
+    assert state[8] == 0, "expected the re-reading capture path"
+    assert ((state[7] >> 19) - state[0]) > 64 * 10, "guess expected many windows above the level-1 bin"
+    assert np.count_nonzero(ref["g"]) == k
+
+
 def test_max_size():
     """d = INT32_MAX, the longest vector the ABI takes, k = 1%.  The oracle cannot
     run at this size, so the checks are ones that fix the answer:
