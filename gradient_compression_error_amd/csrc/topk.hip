@@ -82,6 +82,8 @@ constexpr int TK_SMALL_GRID = 2048;      // workgroups of the candidate passes: 
 constexpr int DEC_TILE = 4096;
 constexpr int PREP_ZERO_BLOCKS = 32;     // topk_prep blocks that zero the histograms
 constexpr int FAST_GRID = 256;           // workgroups of topk_capture's slot pass
+constexpr int CAP_GROUP = 4;             // tiles per round trip in topk_capture's slot pass
+constexpr int CAP_SPEC = 2;              // slots per thread and tile read before the tile's count
 
 struct TopkState {
     unsigned b1, above1;       // level-1 bin, #keys in higher level-1 bins
@@ -539,13 +541,44 @@ __global__ __launch_bounds__(TK_THREADS) void topk_capture(
     int* const sidx = slot_idx + base;
     float* const sval = slot_val + base;
     if (fast) {
+        // Tiles b, b + FAST_GRID, ... of this workgroup, CAP_GROUP at a time: their
+        // counts and the first CAP_SPEC slots per thread of each are loaded
+        // together, before the counts are known (the slot region of every tile
+        // is allocated; what lies past a count is read and ignored), so a group
+        // costs one memory round trip instead of one per tile and slot row.
         const int ntiles = static_cast<int>(gridDim.x);
-        for (int t = blockIdx.x; t < ntiles; t += FAST_GRID) {
-            const unsigned cnt = tile_cnt[t];
-            const float* tv = slot_val + static_cast<long long>(t) * TK_TILE;
-            for (unsigned e = threadIdx.x; e < cnt; e += TK_THREADS) {
-                const unsigned key = key_of(tv[e]);
-                if ((key >> H1_SHIFT) == b1) atomicAdd(&h[(key >> H2_SHIFT) & (H2_BINS - 1)], 1u);
+        auto count_l2 = [&](float v) {
+            const unsigned key = key_of(v);
+            if ((key >> H1_SHIFT) == b1) atomicAdd(&h[(key >> H2_SHIFT) & (H2_BINS - 1)], 1u);
+        };
+        for (int t0 = blockIdx.x; t0 < ntiles; t0 += CAP_GROUP * FAST_GRID) {
+            unsigned cnt[CAP_GROUP];
+            float v[CAP_GROUP][CAP_SPEC];
+#pragma unroll
+            for (int g = 0; g < CAP_GROUP; ++g) {
+                const int t = t0 + g * FAST_GRID;
+                const bool real = t < ntiles;
+                const float* tv = slot_val + static_cast<long long>(real ? t : t0) * TK_TILE;
+                cnt[g] = real ? tile_cnt[t] : 0u;
+#pragma unroll
+                for (int sp = 0; sp < CAP_SPEC; ++sp) v[g][sp] = tv[threadIdx.x + sp * TK_THREADS];
+            }
+#pragma unroll
+            for (int g = 0; g < CAP_GROUP; ++g) {
+#pragma unroll
+                for (int sp = 0; sp < CAP_SPEC; ++sp)
+                    if (threadIdx.x + sp * TK_THREADS < cnt[g]) count_l2(v[g][sp]);
+                // the rest of a longer tile, 4 slot rows per round trip (indices
+                // clamped into the tile, the values past the count ignored)
+                const float* tv = slot_val + static_cast<long long>(t0 + g * FAST_GRID) * TK_TILE;
+                for (unsigned e = threadIdx.x + CAP_SPEC * TK_THREADS; e < cnt[g]; e += 4 * TK_THREADS) {
+                    float w[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w[q] = tv[min(e + q * TK_THREADS, static_cast<unsigned>(TK_TILE - 1))];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (e + q * TK_THREADS < cnt[g]) count_l2(w[q]);
+                }
             }
         }
     } else {
@@ -615,16 +648,36 @@ __global__ __launch_bounds__(TK_THREADS) void topk_refine(
         const TopkState* __restrict__ st, unsigned* __restrict__ hist3,
         const float* __restrict__ slot_val, const unsigned* __restrict__ tile_cnt, int ntiles) {
     __shared__ unsigned h[H3_BINS];
+    const unsigned prefix2 = st->prefix2;
+    auto count_l3 = [&](float v) {
+        const unsigned key = key_of(v);
+        if ((key >> H2_SHIFT) == prefix2) atomicAdd(&h[key & (H3_BINS - 1)], 1u);
+    };
+    // the tile's count and its first two slot rows are read together with
+    // prefix2 (grid <= ntiles, so every workgroup has a tile)
+    int t = blockIdx.x;
+    unsigned cnt = tile_cnt[t];
+    const float* sv = slot_val + static_cast<long long>(t) * TK_TILE;
+    float v0 = sv[threadIdx.x], v1 = sv[threadIdx.x + TK_THREADS];
     for (int i = threadIdx.x; i < H3_BINS; i += TK_THREADS) h[i] = 0u;
     __syncthreads();
-    const unsigned prefix2 = st->prefix2;
-    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const unsigned cnt = tile_cnt[t];
-        const float* sv = slot_val + static_cast<long long>(t) * TK_TILE;
-        for (unsigned e = threadIdx.x; e < cnt; e += TK_THREADS) {
-            const unsigned key = key_of(sv[e]);
-            if ((key >> H2_SHIFT) == prefix2) atomicAdd(&h[key & (H3_BINS - 1)], 1u);
+    while (true) {
+        if (threadIdx.x < cnt) count_l3(v0);
+        if (threadIdx.x + TK_THREADS < cnt) count_l3(v1);
+        for (unsigned e = threadIdx.x + 2 * TK_THREADS; e < cnt; e += 4 * TK_THREADS) {
+            float w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = sv[min(e + q * TK_THREADS, static_cast<unsigned>(TK_TILE - 1))];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (e + q * TK_THREADS < cnt) count_l3(w[q]);
         }
+        t += gridDim.x;
+        if (t >= ntiles) break;
+        cnt = tile_cnt[t];
+        sv = slot_val + static_cast<long long>(t) * TK_TILE;
+        v0 = sv[threadIdx.x];
+        v1 = sv[threadIdx.x + TK_THREADS];
     }
     __syncthreads();
     // merged into one of NCOPY copies: every workgroup adds to the same 128
@@ -654,6 +707,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_count(
     __shared__ unsigned s_tmp[4];
     __shared__ unsigned s_bin, s_above;
     const unsigned above2 = st->above2, prefix2 = st->prefix2;
+    // the first tile's count and two slot rows are read with the level-3
+    // histogram (grid <= ntiles: every workgroup has a tile)
+    const int t0 = tile_lo(blockIdx.x, gridDim.x, ntiles), t1 = tile_lo(blockIdx.x + 1, gridDim.x, ntiles);
+    unsigned cnt = tile_cnt[t0];
+    const float* sv = slot_val + static_cast<long long>(t0) * TK_TILE;
+    float v0 = sv[threadIdx.x], v1 = sv[threadIdx.x + TK_THREADS];
     select_bin<H3_BINS, NCOPY>(hist3, H3_BINS, k - above2, s_h, s_tmp, &s_bin, &s_above);
     const unsigned thr = (prefix2 << H2_SHIFT) | s_bin;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -669,16 +728,29 @@ __global__ __launch_bounds__(TK_THREADS) void topk_count(
         }
     }
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int t0 = tile_lo(blockIdx.x, gridDim.x, ntiles), t1 = tile_lo(blockIdx.x + 1, gridDim.x, ntiles);
     unsigned rgt = 0, req = 0;
     for (int t = t0; t < t1; ++t) {
-        const unsigned cnt = tile_cnt[t];
-        const float* sv = slot_val + static_cast<long long>(t) * TK_TILE;
+        if (t > t0) {
+            cnt = tile_cnt[t];
+            sv = slot_val + static_cast<long long>(t) * TK_TILE;
+            v0 = sv[threadIdx.x];
+            v1 = sv[threadIdx.x + TK_THREADS];
+        }
         unsigned gt = 0, eq = 0;
-        for (unsigned e = threadIdx.x; e < cnt; e += TK_THREADS) {
-            const unsigned key = key_of(sv[e]);
+        auto tally = [&](float v) {
+            const unsigned key = key_of(v);
             gt += key > thr;
             eq += key == thr;
+        };
+        if (threadIdx.x < cnt) tally(v0);
+        if (threadIdx.x + TK_THREADS < cnt) tally(v1);
+        for (unsigned e = threadIdx.x + 2 * TK_THREADS; e < cnt; e += 4 * TK_THREADS) {
+            float w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = sv[min(e + q * TK_THREADS, static_cast<unsigned>(TK_TILE - 1))];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (e + q * TK_THREADS < cnt) tally(w[q]);
         }
         gt = wave_sum(gt);
         eq = wave_sum(eq);
@@ -708,12 +780,34 @@ __global__ __launch_bounds__(TK_THREADS) void topk_emit(
     const unsigned need = st->need;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const unsigned long long lt = lanemask_lt();
+    // the first slot row of the first tile is read with the counts below
+    // (grid <= ntiles: every workgroup has a tile)
+    const int t0 = tile_lo(blockIdx.x, gridDim.x, ntiles), t1 = tile_lo(blockIdx.x + 1, gridDim.x, ntiles);
+    unsigned cnt = tile_cnt[t0];
+    long long sbase = static_cast<long long>(t0) * TK_TILE;
+    float v = slot_val[sbase + threadIdx.x];
+    int ix = slot_idx[sbase + threadIdx.x];
     // ties and selected entries before this workgroup's tile range: the ties
-    // are taken in index order, so min(need, ties before) of them precede it
+    // are taken in index order, so min(need, ties before) of them precede it.
+    // Eight loads per thread and round trip (indices clamped, extra values
+    // ignored).
     unsigned pgt = 0, peq = 0;
-    for (int b = threadIdx.x; b < static_cast<int>(blockIdx.x); b += TK_THREADS) {
-        pgt += wg_gt[b];
-        peq += wg_eq[b];
+    const int nb = static_cast<int>(blockIdx.x);
+    for (int b0 = threadIdx.x; b0 < nb; b0 += 8 * TK_THREADS) {
+        unsigned a[8], c[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int b = min(b0 + j * TK_THREADS, nb - 1);
+            a[j] = wg_gt[b];
+            c[j] = wg_eq[b];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (b0 + j * TK_THREADS < nb) {
+                pgt += a[j];
+                peq += c[j];
+            }
+        }
     }
     pgt = wave_sum(pgt);
     peq = wave_sum(peq);
@@ -725,18 +819,23 @@ __global__ __launch_bounds__(TK_THREADS) void topk_emit(
     unsigned eqr = ((s_sel[0] + s_sel[1]) + s_sel[2]) + s_sel[3];
     unsigned off = (((s_eq[0] + s_eq[1]) + s_eq[2]) + s_eq[3]) + min(need, eqr);
     __syncthreads();
-    const int t0 = tile_lo(blockIdx.x, gridDim.x, ntiles), t1 = tile_lo(blockIdx.x + 1, gridDim.x, ntiles);
     for (int t = t0; t < t1; ++t) {
-        const unsigned cnt = tile_cnt[t];
-        const long long sbase = static_cast<long long>(t) * TK_TILE;
+        if (t > t0) {
+            cnt = tile_cnt[t];
+            sbase = static_cast<long long>(t) * TK_TILE;
+            v = slot_val[sbase + threadIdx.x];
+            ix = slot_idx[sbase + threadIdx.x];
+        }
         for (unsigned c0 = 0; c0 < cnt; c0 += TK_THREADS) {
             const unsigned e = c0 + threadIdx.x;
-            const bool valid = e < cnt;
-            float v = 0.0f;
-            int ix = 0;
-            if (valid) {
-                v = slot_val[sbase + e];
-                ix = slot_idx[sbase + e];
+            const bool valid = e < cnt;   // v and ix past the count are read but not used
+            // the next slot row of the tile, read while this one is placed
+            float vn = 0.0f;
+            int ixn = 0;
+            if (c0 + TK_THREADS < cnt) {
+                const unsigned en = min(e + TK_THREADS, static_cast<unsigned>(TK_TILE - 1));
+                vn = slot_val[sbase + en];
+                ixn = slot_idx[sbase + en];
             }
             const unsigned key = key_of(v);
             const bool is_eq = valid && key == thr;
@@ -771,6 +870,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_emit(
             }
             eqr += teq;
             off += tsel;
+            v = vn;
+            ix = ixn;
             __syncthreads();
         }
     }
