@@ -279,6 +279,19 @@ __device__ __forceinline__ BinPick find_b1_wave(const unsigned* __restrict__ his
     return BinPick{0u, 0u};   // not reached for a consistent histogram
 }
 
+// Adds a workgroup's 4096-bin LDS histogram into one device copy: the 16 LDS
+// reads of a thread are issued together, then the nonzero bins are added.
+__device__ __forceinline__ void merge_hist4096(const unsigned* h, unsigned* __restrict__ dst) {
+    static_assert(H1_BINS == 4096 && H2_BINS == 4096, "level-1 and level-2 histograms of 4096 bins");
+    constexpr int PER = 4096 / TK_THREADS;
+    unsigned c[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) c[j] = h[threadIdx.x + j * TK_THREADS];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (c[j]) atomicAdd(dst + threadIdx.x + j * TK_THREADS, c[j]);
+}
+
 // ---------------------------------------------------------------- kernels
 
 constexpr int PREP_THREADS = 1024;
@@ -491,11 +504,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_accum_hist(
         if (running) atomicAdd(ctr + CAP_W + (blockIdx.x % NCOPY) * CAP_STRIDE, running);
     }
     __syncthreads();
-    unsigned* dst = ctr + HIST1_W + (blockIdx.x % NCOPY) * H1_BINS;
-    for (int i = threadIdx.x; i < H1_BINS; i += TK_THREADS) {
-        const unsigned c = h[i];
-        if (c) atomicAdd(dst + i, c);
-    }
+    merge_hist4096(h, ctr + HIST1_W + (blockIdx.x % NCOPY) * H1_BINS);
 }
 
 // Level-1 bin b1 (the bin of the k-th largest key; every workgroup finds it
@@ -622,11 +631,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_capture(
         if (threadIdx.x == 0) tile_cnt[blockIdx.x] = running;
     }
     __syncthreads();
-    unsigned* dst = ctr + HIST2_W + (blockIdx.x % NCOPY) * H2_BINS;
-    for (int i = threadIdx.x; i < H2_BINS; i += TK_THREADS) {
-        const unsigned c = h[i];
-        if (c) atomicAdd(dst + i, c);
-    }
+    merge_hist4096(h, ctr + HIST2_W + (blockIdx.x % NCOPY) * H2_BINS);
 }
 
 constexpr int SEL_THREADS = 1024;   // single-workgroup selection kernel
