@@ -1156,8 +1156,8 @@ __device__ __forceinline__ void gram_schmidt_coeffs(const double G[16], int r, d
 // thread t sums the partials c = t / (256/S) + S i of column group t % (256/S)
 // in order, and the S slice sums are added in slice order through LDS.  Only
 // the planes below the rank are read.  The Gram partials are summed the same
-// way with 16 slices.  Thread 0 builds T; the column threads write
-// Q' = (M^T P) T.
+// way with 16 slices (16 lanes add one entry's slices each).  Thread 0 builds
+// T; the column threads write Q' = (M^T P) T.
 __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
     __shared__ double s_g[16][16];
     __shared__ double s_T[16];
@@ -1231,19 +1231,26 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) s_q[c][t] = sv[c];
     __syncthreads();
-    if (t == 0) {
-        double G[16], T[16];
-        for (int i = 0; i < 16; ++i) {
-            double g = 0.0;
-            for (int k = 0; k < 16; ++k) g += s_g[k][i];
-            G[i] = g;
+    if (t < 64) {
+        // lanes 0..15 of wave 0 each add one Gram entry's 16 slices (in slice
+        // order, as one thread would), lane 0 builds T from them
+        double g = 0.0;
+        if (t < 16) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) g += s_g[k][t];
         }
-        gram_schmidt_coeffs(G, r, T);
+        double G[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s_T[i] = T[i];
-        if (lwg == 0) {
+        for (int i = 0; i < 16; ++i) G[i] = readlane_any(g, i);
+        if (t == 0) {
+            double T[16];
+            gram_schmidt_coeffs(G, r, T);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) M.tmat[i] = T[i];
+            for (int i = 0; i < 16; ++i) s_T[i] = T[i];
+            if (lwg == 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) M.tmat[i] = T[i];
+            }
         }
     }
     __syncthreads();
