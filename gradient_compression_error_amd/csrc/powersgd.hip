@@ -1170,6 +1170,13 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
     const int m = M.m, r = M.rank, t = threadIdx.x;
     const int S = M.qs, QC = PS_THREADS / S;
     const bool quad = m % 4 == 0;
+    // The partials live in the workspace (global memory): loads through global
+    // pointers, unconditional (indices clamped, values past the count replaced
+    // by zero), so the loads of a round are in flight together instead of
+    // each waiting at the join of its own branch.
+    typedef const __attribute__((address_space(1))) double* GD;
+    typedef const __attribute__((address_space(1))) f32x4* GF4;
+    typedef const __attribute__((address_space(1))) float* GF;
     {
         const int e = t & 15, sl = t >> 4;
         double g = 0.0;
@@ -1179,7 +1186,8 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int bu = b + 16 * u;
-                x[u] = bu < M.ng ? M.gpart[static_cast<long long>(bu) * 16 + e] : 0.0;
+                const double v = ((GD)(M.gpart))[static_cast<long long>(bu < M.ng ? bu : M.ng - 1) * 16 + e];
+                x[u] = bu < M.ng ? v : 0.0;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) g += x[u];
@@ -1199,10 +1207,14 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
 #pragma unroll
                 for (int u = 0; u < QR_QUAD_BATCH; ++u) {
                     const int cu = c + S * u;
+                    const bool in = cu < M.nq;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        x[u][j] = (cu < M.nq && j < r) ? *reinterpret_cast<const float4*>(qplane(M, cu, j) + col)
-                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+                    for (int j = 0; j < 4; ++j) {
+                        // every partial has all four planes allocated
+                        const f32x4 v = ((GF4)(qplane(M, in ? cu : M.nq - 1, j) + col))[0];
+                        const bool use = in && j < r;
+                        x[u][j] = make_float4(use ? v.x : 0.f, use ? v.y : 0.f, use ? v.z : 0.f, use ? v.w : 0.f);
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < QR_QUAD_BATCH; ++u) {
@@ -1219,8 +1231,18 @@ __global__ __launch_bounds__(PS_THREADS, 4) void psgd_qreduce(const PsBatch B) {
                 for (int u = 0; u < 4; ++u) {
                     const int cu = c + S * u;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) x[u][j] = (cu < M.nq && j < r) ? qplane(M, cu, j)[col] : 0.0f;
+                    for (int j = 0; j < 4; ++j) x[u][j] = ((GF)(qplane(M, cu < M.nq ? cu : M.nq - 1, j) + col))[0];
                 }
+                // all 16 loads issued before any is used (the compiler would
+                // otherwise move each into the branch of its own condition)
+                asm volatile("" : "+v"(x[0][0]), "+v"(x[0][1]), "+v"(x[0][2]), "+v"(x[0][3]), "+v"(x[1][0]),
+                                  "+v"(x[1][1]), "+v"(x[1][2]), "+v"(x[1][3]), "+v"(x[2][0]), "+v"(x[2][1]),
+                                  "+v"(x[2][2]), "+v"(x[2][3]), "+v"(x[3][0]), "+v"(x[3][1]), "+v"(x[3][2]),
+                                  "+v"(x[3][3]));
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x[u][j] = (c + S * u < M.nq && j < r) ? x[u][j] : 0.0f;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     sv[0].x += x[u][0]; sv[0].y += x[u][1]; sv[0].z += x[u][2]; sv[0].w += x[u][3];
