@@ -957,7 +957,7 @@ __global__ __launch_bounds__(256) void topk_decode_add(
 // ---------------------------------------------------------------- small vectors
 
 // The whole encode of a vector of d <= SMALL_D entries in one workgroup, where
-// the multi-kernel path would be nine dependent launches of almost no work.
+// the multi-kernel path would be seven dependent launches of almost no work.
 // Thread t holds the SMALL_PER consecutive entries [t SMALL_PER, (t+1)
 // SMALL_PER), so index order is thread order and then register order, and
 // one block scan places every selected entry.  Same arithmetic and selection
